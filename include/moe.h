@@ -1,0 +1,196 @@
+/*
+ * moe.h -- C ABI of a routed-expert Mixture-of-Experts layer whose experts are
+ * stored as 4-bit group-64 affine records, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one call of moe_forward, T tokens of width H):
+ *   1. router:   l[t,e] = sum_h x[t,h] * Wr[e,h] + beta[e]       (8-bit Wr)
+ *   2. select:   ids[t,:] = the top_k experts by logit, ordered by
+ *                (logit descending, expert index ascending); ties go to the
+ *                lowest index.
+ *   3. weights:  p[t,j] = softmax over the top_k selected logits.
+ *   4. experts:  FFN_e(x) = Wd_e (SiLU(Wg_e x) * (Wu_e x)),  SiLU(z) = z/(1+e^-z)
+ *   5. combine:  y[t] = sum_j p[t,j] FFN_{ids[t,j]}(x[t])  [+ FFN_shared(x[t])]
+ * Sources: TurboFieldfare page ("Gemma 4 26B'yi 2GB RAM ile ...") sections
+ * "Belleği azaltan çalışma yapısı" (MLX affine 4-bit, group 64; 8-bit router;
+ * 4-bit shared and routed experts) and "Token üretim süreci" (router on the GPU
+ * from resident weights, top-8 ids, shared-expert branch computed alongside,
+ * shared and routed outputs combined, prefill in chunks of at most 128 tokens);
+ * WASTE page ("Kimi K3'ü 29 GB RAM'de ...") section "Disk streaming mimarisi"
+ * (one expert = one 4 KiB-aligned record with gate, up and down contiguous;
+ * magic, expert id and offsets are checked before a record is used) and section
+ * "Önceden okuma ve router tahmini" (16 expert ids per layer; running the next
+ * layer's router one residual ahead changes neither the selected experts nor
+ * the output).
+ *
+ * ---------------------------------------------------------------------------
+ * Record format (normative)
+ * ---------------------------------------------------------------------------
+ * Affine quantization, group 64 along each matrix's input (reduction) axis:
+ *     W[r, c] = s[r, c/64] * q[r, c] + b[r, c/64]
+ * q unsigned (4-bit: 0..15, 8-bit: 0..255); s and b are IEEE fp16 (subnormals
+ * are values, never flushed).  All multi-byte fields are little-endian.
+ *
+ * Tiled matrix.  A matrix of R rows (outputs) by C columns (inputs), R and C
+ * multiples of 64, is stored as (R/64) * (C/64) tiles in row-block-major order:
+ * tile (rb, g) covers rows rb*64 .. rb*64+63 and columns g*64 .. g*64+63 and
+ * starts at byte ((rb * (C/64)) + g) * TILE_BYTES.
+ *   4-bit tile (TILE_BYTES = 2304):
+ *     bytes [h*1024 + r*16 + j], h in {0,1}, r in 0..63, j in 0..15:
+ *         low nibble  = q[rb*64 + r, g*64 + h*32 + 2j]
+ *         high nibble = q[rb*64 + r, g*64 + h*32 + 2j + 1]
+ *     bytes [2048 + 4r .. 2048 + 4r + 3]: s[rb*64 + r, g] (fp16), then
+ *         b[rb*64 + r, g] (fp16)
+ *   8-bit tile (TILE_BYTES = 4352):
+ *     byte  [c4*1024 + r*16 + j], c4 in 0..3: q[rb*64 + r, g*64 + c4*16 + j]
+ *     bytes [4096 + 4r ..]: s then b, as above.
+ * (Each 16-byte piece is one row's run of consecutive columns, and 64 rows'
+ * pieces are adjacent, so one wave64 load of 16 bytes per lane reads 1 KiB
+ * of contiguous memory.)
+ *
+ * Expert record (4-bit).  hidden H, intermediate I (both multiples of 64):
+ *   [0, 256)   header:
+ *       u32 magic = 0x58455251 ("QREX"), u32 version = 1,
+ *       i32 expert_id (index in the bank; -1 for the shared expert),
+ *       u32 hidden, u32 inter, u32 group = 64, u32 bits = 4, u32 tile_rows = 64,
+ *       u64 gate_off, u64 up_off, u64 down_off, u64 end_off, rest zero.
+ *   gate: tiled 4-bit matrix I x H at gate_off = 256
+ *   up:   tiled 4-bit matrix I x H at up_off   = gate_off + (I/64)(H/64)*2304
+ *   down: tiled 4-bit matrix H x I at down_off = up_off   + (I/64)(H/64)*2304
+ *   end_off = down_off + (H/64)(I/64)*2304; the record is padded with zeros to
+ *   a multiple of 4096 bytes.  A bank is E records at a fixed stride
+ *   (a multiple of 4096, >= end_off).
+ * Router: one tiled 8-bit matrix of ceil(E/64)*64 rows by H columns; rows
+ * >= E are padding and never read as experts.
+ *
+ * ---------------------------------------------------------------------------
+ * Ownership, streams, errors
+ * ---------------------------------------------------------------------------
+ * Every buffer is caller-owned device memory unless stated otherwise.  The
+ * library owns only the context.  Weight pointers passed to moe_set_weights
+ * are borrowed until the next moe_set_weights or moe_close and are never
+ * written or freed.  All device work of a call is enqueued on the caller's
+ * hipStream_t (passed as void*, NULL = the null stream); moe_forward performs
+ * no host synchronisation and no allocation.  A context is not thread-safe and
+ * two calls on one context must not overlap on different streams (they share
+ * the workspace).  Functions return MOE_OK (0) or a negative status; the
+ * context keeps a message for the last failure (moe_last_error).  Asynchronous
+ * kernel faults surface on a later call or synchronisation, as HIP reports them.
+ */
+#ifndef QREB_MOE_H
+#define QREB_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK            0
+#define MOE_EINVAL       (-1)   /* bad argument: null pointer, size out of range */
+#define MOE_EUNSUPPORTED (-2)   /* shape or option this build does not handle    */
+#define MOE_ENOMEM       (-3)   /* workspace too small                           */
+#define MOE_EBADRECORD   (-4)   /* a record header failed validation             */
+#define MOE_ESTATE       (-5)   /* call out of order (forward before weights)    */
+#define MOE_EHIP         (-6)   /* a HIP runtime call failed                     */
+
+#define MOE_BF16 1              /* x dtype: bf16 [T, H]                           */
+#define MOE_F32  2              /* x dtype: fp32 [T, H] (e.g. a residual stream)  */
+
+#define MOE_F_SHARED 1u         /* config flag: an always-on shared expert exists */
+
+#define MOE_ABI_VERSION 1
+
+typedef struct moe_ctx moe_ctx;
+
+/* Layer shape, fixed for the life of a context. */
+typedef struct moe_config {
+    uint32_t struct_size;   /* sizeof(moe_config) */
+    int32_t  hidden;        /* H, multiple of 64, 64..16384 */
+    int32_t  n_experts;     /* E, 1..1024 */
+    int32_t  top_k;         /* k, 1..min(E, 32) */
+    int32_t  inter;         /* I, multiple of 64, 64..16384 */
+    int32_t  shared_inter;  /* Is, multiple of 64; read only with MOE_F_SHARED */
+    int32_t  group;         /* must be 64 */
+    int32_t  max_tokens;    /* largest T a forward may pass, 1..65536 */
+    int32_t  device;        /* HIP device ordinal the context runs on */
+    uint32_t flags;         /* MOE_F_SHARED */
+} moe_config;
+
+/* Weights and workspace, all device pointers (borrowed). */
+typedef struct moe_weights {
+    uint32_t    struct_size;     /* sizeof(moe_weights) */
+    const void *router;          /* tiled 8-bit router matrix (see format) */
+    const float *router_bias;    /* fp32 [E] added to the logits, or NULL */
+    const void *bank;            /* E expert records */
+    uint64_t    record_stride;   /* bytes between records, multiple of 4096 */
+    const void *shared_record;   /* shared-expert record, NULL iff no MOE_F_SHARED */
+    void       *workspace;       /* >= moe_workspace_bytes(cfg) bytes, 256-aligned */
+    uint64_t    workspace_bytes;
+} moe_weights;
+
+/* Bytes of device workspace a context with this config needs (0 if the config
+ * is invalid).  Pure host computation. */
+uint64_t moe_workspace_bytes(const moe_config *cfg);
+
+/* Validate cfg and create a context on cfg->device.  *out is set only on
+ * success.  Errors: MOE_EINVAL (null or struct_size mismatch), MOE_EUNSUPPORTED
+ * (shape outside the ranges above, group != 64), MOE_EHIP. */
+int moe_open(const moe_config *cfg, moe_ctx **out);
+
+/* Bind weights.  Copies every record header (and the shared one) to the host
+ * with one synchronous copy on `stream`, validates each with
+ * moe_check_record_header, and initialises the workspace's counters.  On any
+ * failure the context keeps no weights (a later forward gives MOE_ESTATE).
+ * Errors: MOE_EINVAL, MOE_EBADRECORD, MOE_ENOMEM (workspace too small),
+ * MOE_EHIP. */
+int moe_set_weights(moe_ctx *ctx, const moe_weights *w, void *stream);
+
+/* Run the layer on T = n_tokens rows of x (x_dtype MOE_BF16 or MOE_F32,
+ * row-major [T, H]).  Writes y (fp32 [T, H]); ids_out (int32 [T, k]) and p_out
+ * (fp32 [T, k]) receive the selection when non-NULL.  If lookahead_next is a
+ * context of the same shape with weights bound, its router also runs on this
+ * x and its next forward orders expert work by that prediction; the selected
+ * experts and every output are unchanged by it.  T = 0 is a no-op.  Errors:
+ * MOE_EINVAL (null x/y, T < 0 or > max_tokens, bad dtype, mismatched
+ * lookahead context), MOE_ESTATE (no weights), MOE_EHIP (launch failure). */
+int moe_forward(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
+                float *y, int32_t *ids_out, float *p_out,
+                moe_ctx *lookahead_next, void *stream);
+
+/* Router step only: logits fp32 [T, E] (including router_bias).  Same
+ * argument rules as moe_forward. */
+int moe_router_logits(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
+                      float *logits, void *stream);
+
+/* Tuning knob: experts whose row count (tokens routed to them in one forward)
+ * is >= min_rows use the matrix-core path, the others the streaming path.
+ * The shared expert follows the same rule with row count T.  Default 16;
+ * 1 sends everything to the matrix-core path, a value above max_tokens
+ * sends nothing.  Does not change the selected experts. */
+int moe_set_mfma_min_rows(moe_ctx *ctx, int32_t min_rows);
+
+/* Free the context (NULL is a no-op).  Does not touch borrowed memory. */
+void moe_close(moe_ctx *ctx);
+
+const char *moe_strerror(int code);
+const char *moe_last_error(const moe_ctx *ctx);
+
+/* Host-only validation of one record header (header_bytes >= 256 host bytes):
+ * magic, version, expert_id == expected_id (-1 for the shared expert), hidden
+ * and inter equal to the config's (inter = shared_inter when expected_id is -1),
+ * group 64, bits 4, tile_rows 64, and section offsets exactly as the format
+ * fixes them with end_off <= record_stride.  Returns MOE_OK or
+ * MOE_EBADRECORD / MOE_EINVAL.  Touches no GPU. */
+int moe_check_record_header(const void *header, uint64_t header_bytes,
+                            const moe_config *cfg, int32_t expected_id,
+                            uint64_t record_stride);
+
+/* Test hook: dequantize a tiled matrix (bits 4 or 8) to fp32 [rows, cols] on
+ * the GPU with the same decoding the kernels use. */
+int moe_debug_dequant(const void *tiles, int32_t bits, int32_t rows, int32_t cols,
+                      float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QREB_MOE_H */
