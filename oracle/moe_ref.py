@@ -166,12 +166,18 @@ class OracleLayer:
     def logits(self, x: np.ndarray) -> np.ndarray:
         return router_logits(x, self.wr, self.beta)
 
-    def forward(self, x: np.ndarray, logits=None) -> dict:
-        """x fp64 [T, H] -> dict(y, ids, p, gap, logits)."""
+    def forward(self, x: np.ndarray, logits=None, force_ids=None) -> dict:
+        """x fp64 [T, H] -> dict(y, ids, p, gap, logits).
+
+        ``force_ids`` [T, k] replaces the top-k selection (the layer evaluated
+        on a given selection; p is still the softmax of the oracle's logits of
+        those experts).  Used where the top-k is not unique within a tolerance."""
         x = np.asarray(x, dtype=np.float64)
         t = x.shape[0]
         lg = self.logits(x) if logits is None else logits
         ids, gap = select_topk(lg, self.top_k)
+        if force_ids is not None:
+            ids = np.asarray(force_ids, dtype=np.int64).reshape(t, self.top_k)
         p = softmax_selected(lg, ids)
         # out[t, j] = FFN_{ids[t,j]}(x[t]); tokens sharing an expert are one matmul
         out = np.zeros((t, self.top_k, self.hidden))

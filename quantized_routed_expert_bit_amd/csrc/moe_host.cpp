@@ -1,0 +1,284 @@
+// C ABI of the MoE layer library (declarations and contract: include/moe.h).
+// Validation, workspace layout and stream-ordered launches; no allocation and
+// no host synchronisation on the forward path.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "moe_internal.h"
+
+using namespace qreb;
+
+struct moe_ctx {
+  moe_config cfg;
+  LayerDev d;
+  bool has_weights = false;
+  std::string err;
+};
+
+namespace qreb {
+
+int router_ksplit(int hidden) { return (hidden / kGroup + kRouterWaves - 1) / kRouterWaves; }
+
+int router_tok_block(int n_tokens) {
+  if (n_tokens <= 4) return 1;
+  if (n_tokens <= 64) return 4;
+  return kRouterTokMax;
+}
+
+static size_t al(size_t v) { return (v + 255) & ~size_t(255); }
+
+WsLayout ws_layout(const moe_config& c) {
+  WsLayout L{};
+  const size_t T = (size_t)c.max_tokens, H = (size_t)c.hidden, E = (size_t)c.n_experts;
+  const size_t k = (size_t)c.top_k, I = (size_t)c.inter;
+  const size_t Is = (c.flags & MOE_F_SHARED) ? (size_t)c.shared_inter : 0;
+  const size_t Epad = (E + 63) / 64 * 64, G = H / 64;
+  const size_t KS = (size_t)router_ksplit(c.hidden);
+  const size_t Tk = T * k, Ts = (c.flags & MOE_F_SHARED) ? T : 0;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o += al(bytes);
+    return r;
+  };
+  L.part = take(KS * T * Epad * 4);
+  L.logits = take(0);
+  L.x16 = take(T * H * 2);
+  L.x16lo = take(T * H * 2);
+  L.xs = take(T * G * 4);
+  L.ids = take(Tk * 4);
+  L.p = take(Tk * 4);
+  L.rank = take(Tk * 4);
+  // counts, cnt_tb and misc are contiguous ints (zeroed together at bind time)
+  L.counts = o;
+  o += E * 4;
+  L.cnt_tb = o;
+  o += T * 4;
+  L.misc = o;
+  o += kMiscInts * 4;
+  o = al(o);
+  L.offs = take((E + 1) * 4);
+  L.slots = take((Tk + T) * 4);
+  L.items = take((E + 1) * 16);
+  L.mitems = take((E + 1) * 16);
+  L.mtiles = take(((Tk + kMfmaBM - 1) / kMfmaBM + E + (T + kMfmaBM - 1) / kMfmaBM + 1) * 8);
+  L.pred = take(Tk * 4);
+  L.hbuf = take((Tk * I + Ts * Is) * 2);
+  L.hs = take((Tk * (I / 64) + Ts * (Is / 64)) * 4);
+  L.yslot = take((Tk + Ts) * H * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace qreb
+
+static int check_config(const moe_config* c) {
+  if (!c || c->struct_size != sizeof(moe_config)) return MOE_EINVAL;
+  if (c->group != 64) return MOE_EUNSUPPORTED;
+  if (c->hidden < 64 || c->hidden > 16384 || c->hidden % 64) return MOE_EUNSUPPORTED;
+  if (c->inter < 64 || c->inter > 16384 || c->inter % 64) return MOE_EUNSUPPORTED;
+  if (c->n_experts < 1 || c->n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > kMaxTopK) return MOE_EUNSUPPORTED;
+  if (c->max_tokens < 1 || c->max_tokens > 65536) return MOE_EUNSUPPORTED;
+  if (c->flags & ~MOE_F_SHARED) return MOE_EUNSUPPORTED;
+  if (c->flags & MOE_F_SHARED) {
+    if (c->shared_inter < 64 || c->shared_inter > 16384 || c->shared_inter % 64)
+      return MOE_EUNSUPPORTED;
+  }
+  if (c->device < 0) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+static int fail(moe_ctx* ctx, int code, const char* fmt, ...) {
+  if (ctx) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    ctx->err = buf;
+  }
+  return code;
+}
+
+static int hip_fail(moe_ctx* ctx, hipError_t e, const char* what) {
+  return fail(ctx, MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+extern "C" {
+
+uint64_t moe_workspace_bytes(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return ws_layout(*cfg).total;
+}
+
+int moe_open(const moe_config* cfg, moe_ctx** out) {
+  if (!out) return MOE_EINVAL;
+  const int rc = check_config(cfg);
+  if (rc != MOE_OK) return rc;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev) return MOE_EHIP;
+  moe_ctx* c = new moe_ctx();
+  c->cfg = *cfg;
+  LayerDev& d = c->d;
+  memset(&d, 0, sizeof d);
+  d.H = cfg->hidden;
+  d.E = cfg->n_experts;
+  d.Epad = (cfg->n_experts + 63) / 64 * 64;
+  d.k = cfg->top_k;
+  d.I = cfg->inter;
+  d.has_shared = (cfg->flags & MOE_F_SHARED) ? 1 : 0;
+  d.Is = d.has_shared ? cfg->shared_inter : 0;
+  d.max_tokens = cfg->max_tokens;
+  d.mfma_min_rows = 1 << 30;
+  d.L = ws_layout(*cfg);
+  *out = c;
+  return MOE_OK;
+}
+
+int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
+  if (!ctx) return MOE_EINVAL;
+  ctx->has_weights = false;
+  const moe_config& c = ctx->cfg;
+  if (!w || w->struct_size != sizeof(moe_weights))
+    return fail(ctx, MOE_EINVAL, "moe_weights is NULL or has the wrong struct_size");
+  if (!w->router || !w->bank || !w->workspace)
+    return fail(ctx, MOE_EINVAL, "router, bank and workspace must be non-NULL");
+  if (((uintptr_t)w->workspace & 255) || ((uintptr_t)w->router & 15) || ((uintptr_t)w->bank & 255))
+    return fail(ctx, MOE_EINVAL, "workspace and bank must be 256-byte aligned, router 16-byte");
+  if (ctx->d.has_shared != (w->shared_record != nullptr))
+    return fail(ctx, MOE_EINVAL, "shared_record must be given iff the config has MOE_F_SHARED");
+  if (w->shared_record && ((uintptr_t)w->shared_record & 255))
+    return fail(ctx, MOE_EINVAL, "shared_record must be 256-byte aligned");
+  if (w->record_stride == 0 || w->record_stride % 4096)
+    return fail(ctx, MOE_EINVAL, "record_stride must be a positive multiple of 4096");
+  if (w->workspace_bytes < ctx->d.L.total)
+    return fail(ctx, MOE_ENOMEM, "workspace has %llu bytes, needs %llu",
+                (unsigned long long)w->workspace_bytes, (unsigned long long)ctx->d.L.total);
+  hipError_t e = hipSetDevice(c.device);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipSetDevice");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<uint8_t> hdr((size_t)c.n_experts * 256);
+  e = hipMemcpy2DAsync(hdr.data(), 256, w->bank, w->record_stride, 256, c.n_experts,
+                       hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "copying record headers");
+  std::vector<uint8_t> shdr(256);
+  if (w->shared_record) {
+    e = hipMemcpyAsync(shdr.data(), w->shared_record, 256, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "copying the shared record header");
+  }
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
+  for (int i = 0; i < c.n_experts; ++i) {
+    const int rc = moe_check_record_header(hdr.data() + (size_t)i * 256, 256, &c, i,
+                                           w->record_stride);
+    if (rc != MOE_OK) return fail(ctx, rc, "record %d failed header validation", i);
+  }
+  if (w->shared_record) {
+    const int rc = moe_check_record_header(shdr.data(), 256, &c, -1, UINT64_MAX);
+    if (rc != MOE_OK) return fail(ctx, rc, "shared record failed header validation");
+  }
+  LayerDev& d = ctx->d;
+  d.router = static_cast<const uint8_t*>(w->router);
+  d.router_bias = w->router_bias;
+  d.bank = static_cast<const uint8_t*>(w->bank);
+  d.stride = w->record_stride;
+  d.shared = static_cast<const uint8_t*>(w->shared_record);
+  d.ws = static_cast<uint8_t*>(w->workspace);
+  e = launch_ws_init(d, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "workspace init");
+  ctx->has_weights = true;
+  ctx->err.clear();
+  return MOE_OK;
+}
+
+static int check_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens,
+                         const void* out) {
+  if (!ctx) return MOE_EINVAL;
+  if (!ctx->has_weights) return fail(ctx, MOE_ESTATE, "no weights bound");
+  if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return fail(ctx, MOE_EINVAL, "bad x dtype");
+  if (n_tokens < 0 || n_tokens > ctx->cfg.max_tokens)
+    return fail(ctx, MOE_EINVAL, "n_tokens %d outside [0, %d]", n_tokens, ctx->cfg.max_tokens);
+  if (n_tokens > 0 && (!x || !out)) return fail(ctx, MOE_EINVAL, "x and output must be non-NULL");
+  return MOE_OK;
+}
+
+int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
+                int32_t* ids_out, float* p_out, moe_ctx* next, void* stream) {
+  int rc = check_forward(ctx, x, x_dtype, n_tokens, y);
+  if (rc != MOE_OK) return rc;
+  if (next) {
+    if (next == ctx) return fail(ctx, MOE_EINVAL, "lookahead context is this context");
+    if (!next->has_weights) return fail(ctx, MOE_ESTATE, "lookahead context has no weights");
+    if (next->cfg.hidden != ctx->cfg.hidden || next->cfg.max_tokens < n_tokens)
+      return fail(ctx, MOE_EINVAL, "lookahead context does not match this layer");
+  }
+  if (n_tokens == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int f32 = x_dtype == MOE_F32;
+  const LayerDev& d = ctx->d;
+  hipError_t e = launch_router(d, x, f32, n_tokens, 0, nullptr, ids_out, p_out, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "router launch");
+  e = launch_experts(d, f32, n_tokens, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "expert launch");
+  e = launch_combine(d, n_tokens, reinterpret_cast<const float*>(d.ws + d.L.p), y, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "combine launch");
+  if (next) {
+    e = launch_router(next->d, x, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
+  }
+  return MOE_OK;
+}
+
+int moe_router_logits(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens,
+                      float* logits, void* stream) {
+  int rc = check_forward(ctx, x, x_dtype, n_tokens, logits);
+  if (rc != MOE_OK) return rc;
+  if (n_tokens == 0) return MOE_OK;
+  hipError_t e = launch_router(ctx->d, x, x_dtype == MOE_F32, n_tokens, 1, logits, nullptr,
+                               nullptr, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(ctx, e, "router launch");
+  return MOE_OK;
+}
+
+int moe_set_mfma_min_rows(moe_ctx* ctx, int32_t min_rows) {
+  if (!ctx) return MOE_EINVAL;
+  if (min_rows < 1) return fail(ctx, MOE_EINVAL, "min_rows must be >= 1");
+  ctx->d.mfma_min_rows = min_rows;
+  return MOE_OK;
+}
+
+void moe_close(moe_ctx* ctx) { delete ctx; }
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or option";
+    case MOE_ENOMEM: return "workspace too small";
+    case MOE_EBADRECORD: return "record header failed validation";
+    case MOE_ESTATE: return "call out of order (no weights bound)";
+    case MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(const moe_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+int moe_debug_dequant(const void* tiles, int32_t bits, int32_t rows, int32_t cols, float* out,
+                      void* stream) {
+  if (!tiles || !out || (bits != 4 && bits != 8) || rows <= 0 || cols <= 0 || rows % 64 ||
+      cols % 64)
+    return MOE_EINVAL;
+  hipError_t e = launch_debug_dequant(tiles, bits, rows, cols, out,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+}  // extern "C"

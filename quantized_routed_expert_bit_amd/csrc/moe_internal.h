@@ -1,0 +1,84 @@
+// Private interface between the C ABI (moe_host.cpp) and the kernels
+// (moe_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace qreb {
+
+// Storage format constants (record format in include/moe.h).
+constexpr int kGroup = 64;
+constexpr int kTileRows = 64;
+constexpr int kQ4TileBytes = 2304;     // 2048 code bytes + 64 (scale, bias) fp16 pairs
+constexpr int kQ4CodeBytes = 2048;
+constexpr int kQ8TileBytes = 4352;     // 4096 code bytes + 256
+constexpr int kQ8CodeBytes = 4096;
+constexpr int kHeaderBytes = 256;
+constexpr uint32_t kMagic = 0x58455251u;
+constexpr uint32_t kVersion = 1;
+
+// Router launch geometry: one wave per 64-column group, four groups per
+// workgroup, up to kRouterTokMax tokens per workgroup.
+constexpr int kRouterWaves = 4;
+constexpr int kRouterTokMax = 16;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 1024;
+
+// Streaming (GEMV) expert path: up to kGemvTok tokens per pass over the weights.
+constexpr int kGemvTok = 16;
+constexpr int kGemvWaves = 4;
+
+// Matrix-core (MFMA) expert path: rows (tokens) per tile.
+constexpr int kMfmaBM = 64;
+
+// misc[] slots (int32) in the workspace
+enum MiscSlot {
+  kCntAll = 0,      // token blocks whose top-k is done (self-resetting)
+  kNGemv = 1,       // items on the streaming path
+  kNMfma = 2,       // items on the matrix-core path
+  kNTiles = 3,      // matrix-core row tiles
+  kPredValid = 4,   // predicted slots a lookahead left for the next forward (0: none)
+  kMiscInts = 64,
+};
+
+struct WsLayout {
+  size_t part, logits, x16, x16lo, xs, ids, p, rank, counts, offs, cnt_tb, misc,
+      slots, items, mitems, mtiles, pred, hbuf, hs, yslot, total;
+};
+
+// All sizes derived from the config; identical on every call.
+WsLayout ws_layout(const moe_config& c);
+int router_ksplit(int hidden);            // k-splits of the router reduction
+int router_tok_block(int n_tokens);       // tokens per router workgroup
+
+struct LayerDev {
+  // weights
+  const uint8_t* router;
+  const float* router_bias;
+  const uint8_t* bank;
+  uint64_t stride;
+  const uint8_t* shared;
+  // shape
+  int H, E, Epad, k, I, Is, has_shared, max_tokens;
+  int mfma_min_rows;
+  // workspace
+  uint8_t* ws;
+  WsLayout L;
+};
+
+// Router (+ top-k + bucketing).  mode: 0 forward, 1 logits only, 2 lookahead
+// prediction into the context's own pred[] buffer.
+hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int mode,
+                         float* logits_out, int32_t* ids_out, float* p_out,
+                         hipStream_t s);
+hipError_t launch_experts(const LayerDev& d, int x_f32, int T, hipStream_t s);
+hipError_t launch_combine(const LayerDev& d, int T, const float* p, float* y, hipStream_t s);
+hipError_t launch_ws_init(const LayerDev& d, hipStream_t s);
+hipError_t launch_debug_dequant(const void* tiles, int bits, int rows, int cols, float* out,
+                                hipStream_t s);
+
+}  // namespace qreb

@@ -1,0 +1,114 @@
+"""MoE layer object over the C ABI.  PyTorch supplies device memory and the
+current stream; every step of the layer runs in the HIP library."""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (status {code})")
+        self.code = code
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class MoELayer:
+    """One routed-expert layer: router (8-bit), top-k, 4-bit experts, combine."""
+
+    def __init__(self, hidden, n_experts, top_k, inter, shared_inter=0, max_tokens=1,
+                 device=0):
+        self.lib = L.load()
+        self.cfg = L.make_config(hidden, n_experts, top_k, inter, shared_inter, max_tokens,
+                                 device)
+        self.hidden, self.n_experts, self.top_k = hidden, n_experts, top_k
+        self.max_tokens = max_tokens
+        self.device = torch.device("cuda", device)
+        self.ctx = ctypes.c_void_p()
+        rc = self.lib.moe_open(ctypes.byref(self.cfg), ctypes.byref(self.ctx))
+        if rc != 0:
+            raise MoEError(rc, f"moe_open: {self.lib.moe_strerror(rc).decode()}")
+        self.workspace_bytes = int(self.lib.moe_workspace_bytes(ctypes.byref(self.cfg)))
+        self._keep = ()
+
+    def _check(self, rc, what):
+        if rc != 0:
+            msg = self.lib.moe_last_error(self.ctx).decode() or self.lib.moe_strerror(rc).decode()
+            raise MoEError(rc, f"{what}: {msg}")
+
+    def set_weights(self, router, bank, record_stride, shared=None, router_bias=None,
+                    workspace=None):
+        if workspace is None:
+            workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
+        w = L.MoeWeights(ctypes.sizeof(L.MoeWeights), _ptr(router), _ptr(router_bias),
+                         _ptr(bank), record_stride, _ptr(shared), _ptr(workspace),
+                         workspace.numel())
+        self._keep = (router, bank, shared, router_bias, workspace)
+        self._check(self.lib.moe_set_weights(self.ctx, ctypes.byref(w), _stream()),
+                    "moe_set_weights")
+        return self
+
+    @staticmethod
+    def _dtype(x):
+        if x.dtype == torch.bfloat16:
+            return L.MOE_BF16
+        if x.dtype == torch.float32:
+            return L.MOE_F32
+        raise TypeError("x must be bfloat16 or float32")
+
+    def forward(self, x, return_selection=False, lookahead=None, y=None):
+        T = x.shape[0]
+        x = x.contiguous()
+        if y is None:
+            y = torch.empty((T, self.hidden), dtype=torch.float32, device=self.device)
+        ids = p = None
+        if return_selection:
+            ids = torch.empty((T, self.top_k), dtype=torch.int32, device=self.device)
+            p = torch.empty((T, self.top_k), dtype=torch.float32, device=self.device)
+        nxt = lookahead.ctx if lookahead is not None else None
+        self._check(self.lib.moe_forward(self.ctx, _ptr(x), self._dtype(x), T, _ptr(y),
+                                         _ptr(ids), _ptr(p), nxt, _stream()), "moe_forward")
+        return (y, ids, p) if return_selection else y
+
+    __call__ = forward
+
+    def router_logits(self, x):
+        T = x.shape[0]
+        x = x.contiguous()
+        out = torch.empty((T, self.n_experts), dtype=torch.float32, device=self.device)
+        self._check(self.lib.moe_router_logits(self.ctx, _ptr(x), self._dtype(x), T, _ptr(out),
+                                               _stream()), "moe_router_logits")
+        return out
+
+    def set_mfma_min_rows(self, n):
+        self._check(self.lib.moe_set_mfma_min_rows(self.ctx, n), "moe_set_mfma_min_rows")
+
+    def close(self):
+        if self.ctx:
+            self.lib.moe_close(self.ctx)
+            self.ctx = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def debug_dequant(tiles, bits, rows, cols):
+    lib = L.load()
+    out = torch.empty((rows, cols), dtype=torch.float32, device=tiles.device)
+    rc = lib.moe_debug_dequant(_ptr(tiles), bits, rows, cols, _ptr(out), _stream())
+    if rc != 0:
+        raise MoEError(rc, "moe_debug_dequant")
+    return out

@@ -1,0 +1,160 @@
+"""Parity of the HIP path with the CPU oracle on the GPU (all through the C ABI)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _layer(li, dev, max_tokens, mfma_min_rows=None):
+    from quantized_routed_expert_bit_amd import MoELayer
+    sh = li.shape
+    w = P.upload_layer(li, dev)
+    m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, max_tokens)
+    m.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
+    if mfma_min_rows is not None:
+        m.set_mfma_min_rows(mfma_min_rows)
+    m._w = w
+    return m
+
+
+def test_dequant_bit_exact(torch_dev):
+    """GPU decoding of 4-bit and 8-bit tiles equals the oracle's exactly (s*q+b
+    is exact in fp32 for these data)."""
+    import torch
+    from quantized_routed_expert_bit_amd import debug_dequant
+    P.log("dequant: record gate section + router, config-1 shapes")
+    rec = synth.make_record(0, 1, 0, 3, 2816, 704)
+    lay = synth.record_layout(2816, 704)
+    t = torch.from_numpy(rec[lay["down"]:lay["end"]].copy()).to(torch_dev)
+    got = debug_dequant(t, 4, 2816, 704).cpu().numpy()
+    ref = oracle.dequant_tiled(rec, lay["down"], 2816, 704, 4)
+    assert np.array_equal(got.astype(np.float64), ref)
+    r = synth.make_router(0, 1, 0, 2816, 128)
+    got = debug_dequant(torch.from_numpy(r).to(torch_dev), 8, 128, 2816).cpu().numpy()
+    assert np.array_equal(got.astype(np.float64), oracle.dequant_tiled(r, 0, 128, 2816, 8))
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_router_logits(torch_dev, cfg):
+    import torch
+    wl = synth.WORKLOADS[cfg]
+    li = synth.layer_inputs(wl)
+    T = max(wl.batches)
+    m = _layer(li, torch_dev, T)
+    ol = P.oracle_layer(li)
+    xb = synth.make_hidden(0, cfg, T, wl.shape.hidden)
+    lg = m.router_logits(P.bf16_tensor(xb, torch_dev)).cpu().numpy()
+    ref = ol.logits(oracle.bf16_bits_to_f64(xb))
+    err = np.abs(lg - ref).max()
+    P.log(f"router cfg{cfg}: max |logit err| = {err:.3e}")
+    assert err < 2e-5
+    # fp32 input takes the hi/lo split path
+    x32 = (np.random.default_rng(1).standard_normal((T, wl.shape.hidden))).astype(np.float32)
+    lg = m.router_logits(torch.from_numpy(x32).to(torch_dev)).cpu().numpy()
+    err = np.abs(lg - ol.logits(x32.astype(np.float64))).max()
+    P.log(f"router cfg{cfg} fp32 input: max |logit err| = {err:.3e}")
+    assert err < 2e-5
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_layer_parity_decode(torch_dev, cfg):
+    wl = synth.WORKLOADS[cfg]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, max(wl.batches))
+    ol = P.oracle_layer(li)
+    for T in wl.batches:
+        P.log(f"cfg{cfg} T={T}")
+        xb = synth.make_hidden(0, cfg, T, wl.shape.hidden)
+        y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+        P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                        p.cpu().numpy(), f"cfg{cfg} T={T}")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(H=320, E=65, k=3, I=128, Is=0, T=7),        # ragged router split, padded experts
+    dict(H=128, E=16, k=16, I=64, Is=192, T=5),      # k = E: dense softmax
+    dict(H=192, E=8, k=1, I=192, Is=64, T=33),       # k = 1, many tokens per expert
+    dict(H=64, E=1, k=1, I=64, Is=0, T=3),           # single expert
+])
+def test_layer_parity_edge_shapes(torch_dev, shape):
+    H, E, k, I, Is, T = (shape[n] for n in ("H", "E", "k", "I", "Is", "T"))
+    P.log(f"edge shape {shape}")
+    li = synth.LayerInputs(11, 90, 0, synth.LayerShape(H, E, k, I, Is), "normal0.5")
+    m = _layer(li, torch_dev, T)
+    ol = P.oracle_layer(li)
+    for t in (T, 1):
+        xb = synth.make_hidden(11, 90, t, H)
+        y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+        P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                        p.cpu().numpy(), f"edge T={t}")
+
+
+def test_fp32_input_parity(torch_dev):
+    import torch
+    wl = synth.WORKLOADS[0]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, 8)
+    ol = P.oracle_layer(li)
+    x32 = (np.random.default_rng(5).standard_normal((8, 512)) * 1.7).astype(np.float32)
+    y, ids, p = m.forward(torch.from_numpy(x32).to(torch_dev), return_selection=True)
+    P.check_forward(ol, x32.astype(np.float64), y.cpu().numpy(), ids.cpu().numpy(),
+                    p.cpu().numpy(), "fp32 input")
+
+
+def test_repeatable_bitwise(torch_dev):
+    import torch
+    wl = synth.WORKLOADS[1]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, 16)
+    x = P.bf16_tensor(synth.make_hidden(0, 1, 16, 2816, tag=3), torch_dev)
+    y0, i0, p0 = m.forward(x, return_selection=True)
+    for _ in range(10):
+        y, i, p = m.forward(x, return_selection=True)
+        assert torch.equal(y, y0) and torch.equal(i, i0) and torch.equal(p, p0)
+
+
+def test_error_paths(torch_dev):
+    import torch
+    from quantized_routed_expert_bit_amd import MoELayer, MoEError
+    wl = synth.WORKLOADS[0]
+    li = synth.layer_inputs(wl)
+    sh = wl.shape
+    w = P.upload_layer(li, torch_dev)
+    m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, 0, 4)
+    x = P.bf16_tensor(synth.make_hidden(0, 0, 4, 512), torch_dev)
+    with pytest.raises(MoEError) as ei:
+        m.forward(x)
+    assert ei.value.code == -5                                     # no weights yet
+    bad = w["bank"].clone()
+    bad[3 * w["stride"]] ^= 1                                      # record 3 magic
+    with pytest.raises(MoEError) as ei:
+        m.set_weights(w["router"], bad, w["stride"])
+    assert ei.value.code == -4
+    with pytest.raises(MoEError) as ei:
+        m.forward(x)
+    assert ei.value.code == -5                                     # failed bind keeps no weights
+    small = torch.empty(1024, dtype=torch.uint8, device=torch_dev)
+    with pytest.raises(MoEError) as ei:
+        m.set_weights(w["router"], w["bank"], w["stride"], workspace=small)
+    assert ei.value.code == -3
+    m.set_weights(w["router"], w["bank"], w["stride"])
+    with pytest.raises(MoEError) as ei:
+        m.forward(P.bf16_tensor(synth.make_hidden(0, 0, 5, 512), torch_dev))
+    assert ei.value.code == -1                                     # T > max_tokens
+    y = torch.full((0, 512), 7.0, device=torch_dev)
+    m.forward(x[:0], y=y)                                          # T = 0: no-op
+    with pytest.raises(MoEError) as ei:
+        m.set_weights(w["router"], w["bank"], w["stride"], shared=w["bank"][:4096])
+    assert ei.value.code == -1                                     # shared without the flag
