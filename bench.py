@@ -1,0 +1,228 @@
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+Default workload: the decode layer (hidden 2816, 128 experts, top-8,
+intermediate 704, shared expert 2112) at 16 tokens per forward.  A step is one
+moe_forward: router + top-k + bucketing, gate/up, down, combine.  Steps rotate
+over several copies of the layer (distinct weights, like consecutive layers of
+a model) so the active weights come from HBM, not from the 256 MB last-level
+cache.  The timed region is one HIP graph holding K forwards; HIP events that
+the library records around each kernel inside that graph give per-kernel
+durations for the roofline line.
+
+Prints ONE JSON line (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
+METRIC = "MoE layer tokens/s; decode HBM GB/s and prefill TFLOP/s as % of MI355X peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def record_bytes(h, i):
+    """Algorithmic bytes of one expert record: 3*H*I weights at 4.5 bits."""
+    return 3 * h * i * 9 // 16
+
+
+def build_layers(wl_index, n_copies, max_tokens, dev):
+    import synth
+    from quantized_routed_expert_bit_amd import MoELayer
+    from tests.parity import upload_layer
+    wl = synth.WORKLOADS[wl_index]
+    sh = wl.shape
+    layers = []
+    for l in range(n_copies):
+        li = synth.LayerInputs(0, wl.index, l, sh, wl.bias)
+        w = upload_layer(li, dev)
+        m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, max_tokens)
+        m.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
+        m._w, m._li = w, li
+        layers.append(m)
+        log(f"  layer copy {l} uploaded")
+    return wl, layers
+
+
+def run_case(layers, sh, T, steps, warmup, tag=0):
+    """Warm up eagerly, capture `steps` forwards in one graph, replay it once
+    (the timed region).  Returns timings and routing stats."""
+    import torch
+    import synth
+    from tests.parity import bf16_tensor
+    dev = torch.device("cuda", 0)
+    n = len(layers)
+    xs = [bf16_tensor(synth.make_hidden(0, layers[l]._li.cfg, T, sh.hidden, tag=100 + l + tag), dev)
+          for l in range(n)]
+    ys = [torch.empty((T, sh.hidden), dtype=torch.float32, device=dev) for _ in range(n)]
+    # routing per copy (deterministic): distinct experts and rows
+    distinct = []
+    for l in range(n):
+        _, ids, _ = layers[l].forward(xs[l], return_selection=True)
+        distinct.append(len(np.unique(ids.cpu().numpy())))
+    for i in range(warmup):
+        layers[i % n].forward(xs[i % n], y=ys[i % n])
+    torch.cuda.synchronize()
+    # timed region: one graph replay of `steps` forwards
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(steps):
+            layers[i % n].forward(xs[i % n], y=ys[i % n])
+    g.replay()                       # untimed replay (graph upload)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    del g
+    # kernel timing pass: the same forwards eagerly, with the library's event
+    # pairs around each kernel; a spin kernel holds the GPU while the host
+    # queues them, so no kernel waits on the host.
+    kp = min(steps, 120)
+    per_copy = [(kp + n - 1 - l) // n for l in range(n)]
+    for l in range(n):
+        layers[l].profile_start(per_copy[l])
+    t_first = torch.cuda.Event(enable_timing=True)
+    t_last = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2.4e9 * 0.05))          # ~50 ms of GPU spin
+    t_first.record()
+    for i in range(kp):
+        layers[i % n].forward(xs[i % n], y=ys[i % n])
+    t_last.record()
+    torch.cuda.synchronize()
+    eager_ms = t_first.elapsed_time(t_last) / kp
+    prof = [layers[l].profile_read() for l in range(n)]
+    kern = {}
+    for name in prof[0][0]:
+        tot = sum(p[0][name] * p[1] for p in prof)
+        cnt = sum(p[1] for p in prof if p[0][name] > 0)
+        kern[name] = tot / cnt if cnt else 0.0
+    d_avg = float(np.average(distinct, weights=per_copy))
+    return dict(elapsed=el, ms_per_step=el * 1e3 / steps, tok_s=T * steps / el, kern_ms=kern,
+                distinct=d_avg, per_copy=per_copy, distinct_per_copy=distinct,
+                eager_ms_per_step=eager_ms)
+
+
+def cpu_baseline(layer0, sh, T):
+    """The oracle (fp64 NumPy) on one forward of the same workload."""
+    import oracle
+    import synth
+    from tests.parity import oracle_layer
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    ol = oracle_layer(layer0._li, cache=True)
+    xb = synth.make_hidden(0, layer0._li.cfg, T, sh.hidden, tag=100)
+    x64 = oracle.bf16_bits_to_f64(xb)
+    ids = ol.forward(x64[:1])["ids"]          # warm: regenerate the records the batch uses
+    for e in np.unique(oracle.select_topk(ol.logits(x64), sh.top_k)[0]):
+        ol.get_record(int(e))
+    t0 = time.perf_counter()
+    ol.forward(x64)
+    el = time.perf_counter() - t0
+    return dict(value=round(T / el, 3), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"one oracle forward of the {T}-token batch on layer copy 0 (fp64 dequant "
+                       f"of every active record + router, top-k, FFNs, combine; record "
+                       f"generation excluded): {el:.2f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--copies", type=int, default=6, help="layer copies the steps rotate over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the T=1 and T=4 lines")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    T = args.batch
+    wl, layers = build_layers(1, args.copies, max(T, 16), dev)
+    sh = wl.shape
+    res = run_case(layers, sh, T, args.steps, args.warmup)
+    log(f"T={T}: {res['ms_per_step']*1e3:.1f} us/step, kernels {res['kern_ms']}")
+
+    # dominant kernel: streaming gate/up.  Algorithmic bytes per launch =
+    # (distinct routed experts + shared when it streams) * 2*H*I*4.5/8.
+    rmin = layers[0].mfma_min_rows
+    shared_streams = sh.has_shared and T < rmin
+    up_bytes = res["distinct"] * 2 * sh.hidden * sh.inter * 9 / 16 + \
+        (2 * sh.hidden * sh.shared_inter * 9 / 16 if shared_streams else 0)
+    up_ms = res["kern_ms"]["gemv_up"]
+    achieved = up_bytes / (up_ms * 1e-3) / 1e9
+    layer_bytes = res["distinct"] * record_bytes(sh.hidden, sh.inter) + \
+        (record_bytes(sh.hidden, sh.shared_inter) if sh.has_shared else 0) + \
+        sh.n_experts * sh.hidden * 17 / 16 + T * sh.hidden * 6 + T * sh.top_k * 8
+    out = {
+        "metric": METRIC,
+        "value": round(res["tok_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"decode MoE layer: hidden {sh.hidden}, {sh.n_experts} experts, "
+                               f"top-{sh.top_k}, intermediate {sh.inter}, shared expert "
+                               f"{sh.shared_inter}, {T} tokens per forward, 4-bit g64 experts, "
+                               f"8-bit router, {args.copies} rotating layer copies",
+                   "tokens_per_step": T, "layer_copies": args.copies, "launch": "hip_graph"},
+        "roofline": {"bound": "hbm", "kernel": "gemv_up", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": int(up_bytes),
+                     "avg_launch_us": round(up_ms * 1e3, 3)},
+        "layer_hbm": {"alg_bytes_per_step": int(layer_bytes),
+                      "GB_s": round(layer_bytes / (res["ms_per_step"] * 1e-3) / 1e9, 1),
+                      "frac": round(layer_bytes / (res["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "kernel_us": {k: round(v * 1e3, 3) for k, v in res["kern_ms"].items()},
+        "eager_us_per_step": round(res["eager_ms_per_step"] * 1e3, 2),
+        "distinct_experts": res["distinct"],
+    }
+    if not args.no_extra:
+        extra = {}
+        for Tx in (1, 4):
+            r = run_case(layers, sh, Tx, args.steps, args.warmup, tag=Tx)
+            ub = r["distinct"] * 2 * sh.hidden * sh.inter * 9 / 16 + \
+                (2 * sh.hidden * sh.shared_inter * 9 / 16 if sh.has_shared and Tx < rmin else 0)
+            extra[f"T{Tx}"] = {"tokens_s": round(r["tok_s"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2),
+                               "gemv_up_GB_s": round(ub / (r["kern_ms"]["gemv_up"] * 1e-3) / 1e9, 1),
+                               "kernel_us": {k: round(v * 1e3, 3) for k, v in r["kern_ms"].items()},
+                               "distinct_experts": r["distinct"]}
+            log(f"T={Tx}: {extra[f'T{Tx}']}")
+        out["extra"] = extra
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers[0], sh, T)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -162,12 +162,31 @@ int moe_forward(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
 int moe_router_logits(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
                       float *logits, void *stream);
 
-/* Tuning knob: experts whose row count (tokens routed to them in one forward)
- * is >= min_rows use the matrix-core path, the others the streaming path.
- * The shared expert follows the same rule with row count T.  Default 16;
- * 1 sends everything to the matrix-core path, a value above max_tokens
- * sends nothing.  Does not change the selected experts. */
-int moe_set_mfma_min_rows(moe_ctx *ctx, int32_t min_rows);
+/* Tuning knob for the expert paths.  An expert's row count is the number of
+ * tokens routed to it in one forward (T for the shared expert).  Rows below
+ * mfma_min_rows take the streaming dot-product path; rows in
+ * [mfma_min_rows, wide_min_rows) take the matrix-core path in 32-row tiles;
+ * rows >= wide_min_rows take it in 128-row tiles.  Defaults 4 and 64.
+ * mfma_min_rows = 1 sends every expert to the matrix cores; values above
+ * max_tokens keep them all on the streaming path.  Never changes the selected
+ * experts.  Errors: MOE_EINVAL unless 1 <= mfma_min_rows <= wide_min_rows. */
+int moe_set_path_rows(moe_ctx *ctx, int32_t mfma_min_rows, int32_t wide_min_rows);
+
+/* Kernel timing (measurement aid).  moe_profile_start creates event pairs for
+ * up to max_calls forwards; each later moe_forward on a stream that is not
+ * being captured into a graph records one pair around each kernel it launches,
+ * on the forward's stream.  moe_profile_read waits for the
+ * recorded events, writes the average milliseconds per launch of each kernel
+ * slot into avg_ms[0 .. n_slots-1] (0 for a slot never launched) and the number
+ * of profiled forwards into *n_calls, then stops profiling.  Slots:
+ * 0 router+top-k+bucketing, 1 streaming gate/up, 2 streaming down,
+ * 3 matrix-core gate/up (128-row tiles), 4 matrix-core down (128-row tiles),
+ * 5 combine, 6 matrix-core gate/up (32-row tiles), 7 matrix-core down
+ * (32-row tiles).
+ * Errors: MOE_EINVAL, MOE_EHIP. */
+#define MOE_PROFILE_SLOTS 8
+int moe_profile_start(moe_ctx *ctx, int32_t max_calls);
+int moe_profile_read(moe_ctx *ctx, float *avg_ms, int32_t *n_calls, int32_t n_slots);
 
 /* Free the context (NULL is a no-op).  Does not touch borrowed memory. */
 void moe_close(moe_ctx *ctx);

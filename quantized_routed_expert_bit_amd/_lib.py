@@ -15,8 +15,11 @@ MOE_F_SHARED = 1
 
 # every function include/moe.h declares
 EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
-            "moe_router_logits", "moe_set_mfma_min_rows", "moe_close", "moe_strerror",
-            "moe_last_error", "moe_check_record_header", "moe_debug_dequant")
+            "moe_router_logits", "moe_set_path_rows", "moe_close", "moe_strerror",
+            "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
+            "moe_profile_start", "moe_profile_read")
+PROFILE_SLOTS = ("router", "gemv_up", "gemv_down", "mfma_up", "mfma_down", "combine",
+                 "narrow_up", "narrow_down")
 
 
 class MoeConfig(ctypes.Structure):
@@ -56,8 +59,8 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.restype = c_int
     lib.moe_router_logits.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]
     lib.moe_router_logits.restype = c_int
-    lib.moe_set_mfma_min_rows.argtypes = [c_void_p, c_int32]
-    lib.moe_set_mfma_min_rows.restype = c_int
+    lib.moe_set_path_rows.argtypes = [c_void_p, c_int32, c_int32]
+    lib.moe_set_path_rows.restype = c_int
     lib.moe_close.argtypes = [c_void_p]
     lib.moe_close.restype = None
     lib.moe_strerror.argtypes = [c_int]
@@ -68,6 +71,10 @@ def load() -> ctypes.CDLL:
     lib.moe_check_record_header.restype = c_int
     lib.moe_debug_dequant.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]
     lib.moe_debug_dequant.restype = c_int
+    lib.moe_profile_start.argtypes = [c_void_p, c_int32]
+    lib.moe_profile_start.restype = c_int
+    lib.moe_profile_read.argtypes = [c_void_p, P(c_float), P(c_int32), c_int32]
+    lib.moe_profile_read.restype = c_int
     _lib = lib
     return lib
 

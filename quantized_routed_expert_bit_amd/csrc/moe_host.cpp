@@ -19,16 +19,31 @@ struct moe_ctx {
   LayerDev d;
   bool has_weights = false;
   std::string err;
+  // kernel timing: events [call][slot][begin/end]
+  std::vector<hipEvent_t> ev;
+  std::vector<uint8_t> launched;  // [call][slot]
+  int prof_max = 0, prof_calls = 0;
 };
+
+static void prof_clear(moe_ctx* c) {
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  c->ev.clear();
+  c->launched.clear();
+  c->prof_max = c->prof_calls = 0;
+}
 
 namespace qreb {
 
-int router_ksplit(int hidden) { return (hidden / kGroup + kRouterWaves - 1) / kRouterWaves; }
+int router_ksplit(int hidden) { return (hidden / kGroup + kRouterGPW - 1) / kRouterGPW; }
 
-int router_tok_block(int n_tokens) {
-  if (n_tokens <= 4) return 1;
-  if (n_tokens <= 64) return 4;
-  return kRouterTokMax;
+// Tokens per router workgroup: all of a decode batch when it fits (then one
+// workgroup finishes top-k and bucketing without a second hand-off), bounded
+// so the token block's logits fit the workgroup's LDS (tokens * Epad <= 4096).
+int router_tok_block(int n_tokens, int e_pad) {
+  int tb = 4096 / e_pad;
+  if (tb > kRouterTokMax) tb = kRouterTokMax;
+  if (tb < 1) tb = 1;
+  return n_tokens < tb ? n_tokens : tb;
 }
 
 static size_t al(size_t v) { return (v + 255) & ~size_t(255); }
@@ -68,6 +83,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.items = take((E + 1) * 16);
   L.mitems = take((E + 1) * 16);
   L.mtiles = take(((Tk + kMfmaBM - 1) / kMfmaBM + E + (T + kMfmaBM - 1) / kMfmaBM + 1) * 8);
+  L.ntiles = take(((Tk + kNarrowBM - 1) / kNarrowBM + E + (T + kNarrowBM - 1) / kNarrowBM + 1) * 8);
   L.pred = take(Tk * 4);
   L.hbuf = take((Tk * I + Ts * Is) * 2);
   L.hs = take((Tk * (I / 64) + Ts * (Is / 64)) * 4);
@@ -136,7 +152,8 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
   d.has_shared = (cfg->flags & MOE_F_SHARED) ? 1 : 0;
   d.Is = d.has_shared ? cfg->shared_inter : 0;
   d.max_tokens = cfg->max_tokens;
-  d.mfma_min_rows = 1 << 30;
+  d.mfma_min_rows = 4;
+  d.wide_min_rows = 64;
   d.L = ws_layout(*cfg);
   *out = c;
   return MOE_OK;
@@ -223,16 +240,108 @@ int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int f32 = x_dtype == MOE_F32;
   const LayerDev& d = ctx->d;
+  // Timing events are recorded only on a stream that is not being captured
+  // into a graph (inside a capture an event record would only be a dependency).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (ctx->prof_calls < ctx->prof_max) (void)hipStreamIsCapturing(s, &cap);
+  const bool prof = ctx->prof_calls < ctx->prof_max && cap == hipStreamCaptureStatusNone;
+  const int call = ctx->prof_calls;
+  auto mark = [&](int slot, int end) {
+    if (!prof) return;
+    (void)hipEventRecord(ctx->ev[((size_t)call * MOE_PROFILE_SLOTS + slot) * 2 + end], s);
+    if (end) ctx->launched[(size_t)call * MOE_PROFILE_SLOTS + slot] = 1;
+  };
+  mark(0, 0);
   hipError_t e = launch_router(d, x, f32, n_tokens, 0, nullptr, ids_out, p_out, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "router launch");
-  e = launch_experts(d, f32, n_tokens, s);
-  if (e != hipSuccess) return hip_fail(ctx, e, "expert launch");
+  mark(0, 1);
+  mark(1, 0);
+  e = launch_gemv_up(d, f32, n_tokens, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "streaming gate/up launch");
+  mark(1, 1);
+  const bool mf = mfma_needed(d, n_tokens), nf = narrow_needed(d, n_tokens);
+  if (mf) {
+    mark(3, 0);
+    e = launch_mfma_up(d, f32, n_tokens, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core gate/up launch");
+    mark(3, 1);
+  }
+  if (nf) {
+    mark(6, 0);
+    e = launch_narrow_up(d, f32, n_tokens, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core gate/up launch");
+    mark(6, 1);
+  }
+  mark(2, 0);
+  e = launch_gemv_down(d, n_tokens, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "streaming down launch");
+  mark(2, 1);
+  if (mf) {
+    mark(4, 0);
+    e = launch_mfma_down(d, n_tokens, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core down launch");
+    mark(4, 1);
+  }
+  if (nf) {
+    mark(7, 0);
+    e = launch_narrow_down(d, n_tokens, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core down launch");
+    mark(7, 1);
+  }
+  mark(5, 0);
   e = launch_combine(d, n_tokens, reinterpret_cast<const float*>(d.ws + d.L.p), y, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "combine launch");
+  mark(5, 1);
+  if (prof) ctx->prof_calls++;
   if (next) {
     e = launch_router(next->d, x, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
   }
+  return MOE_OK;
+}
+
+int moe_profile_start(moe_ctx* ctx, int32_t max_calls) {
+  if (!ctx || max_calls < 1 || max_calls > 100000) return MOE_EINVAL;
+  prof_clear(ctx);
+  ctx->ev.resize((size_t)max_calls * MOE_PROFILE_SLOTS * 2);
+  for (auto& e : ctx->ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      prof_clear(ctx);
+      return hip_fail(ctx, r, "hipEventCreate");
+    }
+  }
+  ctx->launched.assign((size_t)max_calls * MOE_PROFILE_SLOTS, 0);
+  ctx->prof_max = max_calls;
+  return MOE_OK;
+}
+
+int moe_profile_read(moe_ctx* ctx, float* avg_ms, int32_t* n_calls, int32_t n_slots) {
+  if (!ctx || !avg_ms || !n_calls || n_slots < 0) return MOE_EINVAL;
+  const int calls = ctx->prof_calls;
+  for (int i = 0; i < n_slots; ++i) avg_ms[i] = 0.f;
+  for (int slot = 0; slot < MOE_PROFILE_SLOTS && slot < n_slots; ++slot) {
+    double sum = 0;
+    int n = 0;
+    for (int c = 0; c < calls; ++c) {
+      if (!ctx->launched[(size_t)c * MOE_PROFILE_SLOTS + slot]) continue;
+      hipEvent_t b = ctx->ev[((size_t)c * MOE_PROFILE_SLOTS + slot) * 2];
+      hipEvent_t e = ctx->ev[((size_t)c * MOE_PROFILE_SLOTS + slot) * 2 + 1];
+      hipError_t r = hipEventSynchronize(e);
+      float ms = 0.f;
+      if (r == hipSuccess) r = hipEventElapsedTime(&ms, b, e);
+      if (r != hipSuccess) {
+        prof_clear(ctx);
+        return hip_fail(ctx, r, "reading kernel timing events");
+      }
+      sum += ms;
+      ++n;
+    }
+    avg_ms[slot] = n ? (float)(sum / n) : 0.f;
+  }
+  *n_calls = calls;
+  prof_clear(ctx);
   return MOE_OK;
 }
 
@@ -247,14 +356,20 @@ int moe_router_logits(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_to
   return MOE_OK;
 }
 
-int moe_set_mfma_min_rows(moe_ctx* ctx, int32_t min_rows) {
+int moe_set_path_rows(moe_ctx* ctx, int32_t mfma_min_rows, int32_t wide_min_rows) {
   if (!ctx) return MOE_EINVAL;
-  if (min_rows < 1) return fail(ctx, MOE_EINVAL, "min_rows must be >= 1");
-  ctx->d.mfma_min_rows = min_rows;
+  if (mfma_min_rows < 1 || wide_min_rows < mfma_min_rows)
+    return fail(ctx, MOE_EINVAL, "need 1 <= mfma_min_rows <= wide_min_rows");
+  ctx->d.mfma_min_rows = mfma_min_rows;
+  ctx->d.wide_min_rows = wide_min_rows;
   return MOE_OK;
 }
 
-void moe_close(moe_ctx* ctx) { delete ctx; }
+void moe_close(moe_ctx* ctx) {
+  if (!ctx) return;
+  prof_clear(ctx);
+  delete ctx;
+}
 
 const char* moe_strerror(int code) {
   switch (code) {

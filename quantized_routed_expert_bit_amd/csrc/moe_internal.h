@@ -21,19 +21,23 @@ constexpr int kHeaderBytes = 256;
 constexpr uint32_t kMagic = 0x58455251u;
 constexpr uint32_t kVersion = 1;
 
-// Router launch geometry: one wave per 64-column group, four groups per
-// workgroup, up to kRouterTokMax tokens per workgroup.
+// Router launch geometry: four waves, eight 64-column groups per workgroup
+// (two per wave), up to kRouterTokMax tokens per workgroup.
 constexpr int kRouterWaves = 4;
+constexpr int kRouterGPW = 8;
 constexpr int kRouterTokMax = 16;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 
 // Streaming (GEMV) expert path: up to kGemvTok tokens per pass over the weights.
 constexpr int kGemvTok = 16;
+constexpr int kGemvTokV2 = 4;   // token rows per streaming pass (register accumulators)
 constexpr int kGemvWaves = 4;
 
-// Matrix-core (MFMA) expert path: rows (tokens) per tile.
-constexpr int kMfmaBM = 64;
+// Matrix-core (MFMA) expert path: rows (tokens) per wide tile, per narrow tile.
+constexpr int kMfmaBM = 128;
+constexpr int kNarrowBM = 32;
+constexpr int kMfmaWaves = 4;
 
 // misc[] slots (int32) in the workspace
 enum MiscSlot {
@@ -42,18 +46,19 @@ enum MiscSlot {
   kNMfma = 2,       // items on the matrix-core path
   kNTiles = 3,      // matrix-core row tiles
   kPredValid = 4,   // predicted slots a lookahead left for the next forward (0: none)
+  kNNarrow = 5,     // matrix-core narrow (32-row) tiles
   kMiscInts = 64,
 };
 
 struct WsLayout {
   size_t part, logits, x16, x16lo, xs, ids, p, rank, counts, offs, cnt_tb, misc,
-      slots, items, mitems, mtiles, pred, hbuf, hs, yslot, total;
+      slots, items, mitems, mtiles, ntiles, pred, hbuf, hs, yslot, total;
 };
 
 // All sizes derived from the config; identical on every call.
 WsLayout ws_layout(const moe_config& c);
 int router_ksplit(int hidden);            // k-splits of the router reduction
-int router_tok_block(int n_tokens);       // tokens per router workgroup
+int router_tok_block(int n_tokens, int e_pad);   // tokens per router workgroup
 
 struct LayerDev {
   // weights
@@ -64,7 +69,8 @@ struct LayerDev {
   const uint8_t* shared;
   // shape
   int H, E, Epad, k, I, Is, has_shared, max_tokens;
-  int mfma_min_rows;
+  int mfma_min_rows;   // rows at which an expert leaves the streaming path
+  int wide_min_rows;   // rows at which it uses 128-row instead of 32-row tiles
   // workspace
   uint8_t* ws;
   WsLayout L;
@@ -75,7 +81,14 @@ struct LayerDev {
 hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int mode,
                          float* logits_out, int32_t* ids_out, float* p_out,
                          hipStream_t s);
-hipError_t launch_experts(const LayerDev& d, int x_f32, int T, hipStream_t s);
+hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
+hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s);
+bool mfma_needed(const LayerDev& d, int T);
+hipError_t launch_mfma_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
+hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s);
+bool narrow_needed(const LayerDev& d, int T);
+hipError_t launch_narrow_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
+hipError_t launch_narrow_down(const LayerDev& d, int T, hipStream_t s);
 hipError_t launch_combine(const LayerDev& d, int T, const float* p, float* y, hipStream_t s);
 hipError_t launch_ws_init(const LayerDev& d, hipStream_t s);
 hipError_t launch_debug_dequant(const void* tiles, int bits, int rows, int cols, float* out,

@@ -129,10 +129,7 @@ struct RouterArgs {
   uint16_t* x16;
   uint16_t* x16lo;
   float* xs;
-  int* cnt_tb;
   int* misc;
-  int* counts;
-  int* rank;
   int* ids_ws;
   float* p_ws;
   int32_t* ids_out;
@@ -144,46 +141,53 @@ struct RouterArgs {
   int4* items;
   int4* mitems;
   int2* mtiles;
-  int mfma_min_rows, has_shared;
+  int2* ntiles;
+  int mfma_min_rows, wide_min_rows, has_shared;
 };
 
-// Runs in the single workgroup that finishes last: counts -> offsets -> slot
-// lists grouped by expert -> work lists.  Resets every counter it consumed.
-__device__ void bucket_final(const RouterArgs& a) {
-  __shared__ int s_cnt[kMaxExperts + 2];
-  __shared__ int s_off[kMaxExperts + 2];
-  __shared__ int s_flag[kMaxExperts + 2];
-  __shared__ unsigned char s_pred[kMaxExperts];
-  __shared__ int s_scan[256];
-  __shared__ int s_tot[4];
+// Bucketing, by one 256-thread workgroup once every token's top-k is known:
+// LDS histogram of the T*k selections -> exclusive scan -> slot lists grouped
+// by expert -> work lists for the two expert paths.  `ids` may point to LDS or
+// global memory.  Order inside one expert's list is whatever the LDS atomics
+// give; it never changes a result (every row is computed on its own).
+__device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem) {
+  int* s_cnt = reinterpret_cast<int*>(smem);                // [E]
+  int* s_off = s_cnt + kMaxExperts + 2;                      // [E + 1]
+  int* s_flag = s_off + kMaxExperts + 2;                     // [E + 1]
+  int* s_cur = s_flag + kMaxExperts + 2;                     // [E]
+  int* s_scan = s_cur + kMaxExperts + 2;                     // [256]
+  int* s_tot = s_scan + 256;                                 // [4]
+  unsigned char* s_pred = reinterpret_cast<unsigned char*>(s_tot + 4);   // [E]
   const int tid = threadIdx.x;
   const int E = a.E, Tk = a.T * a.k;
   const int R = a.mfma_min_rows;
   for (int e = tid; e < E; e += 256) {
-    int c = atomicExch(&a.counts[e], 0);
-    s_cnt[e] = c;
-    s_off[e] = c;
+    s_cnt[e] = 0;
     s_pred[e] = 0;
   }
   const int pv = a.misc[kPredValid];
   __syncthreads();
-  block_excl_scan(s_off, E, s_scan);
-  for (int e = tid; e < E; e += 256) a.offs[e] = s_off[e];
-  if (tid == 0) a.offs[E] = Tk;
-  for (int s = tid; s < Tk; s += 256) {
-    const int e = a.ids_ws[s];
-    a.slots[s_off[e] + a.rank[s]] = s;
-  }
-  if (a.has_shared)
-    for (int t = tid; t < a.T; t += 256) a.slots[Tk + t] = Tk + t;
+  for (int s = tid; s < Tk; s += 256) atomicAdd(&s_cnt[ids[s]], 1);
   for (int s = tid; s < pv; s += 256) {
     const int e = a.pred[s];
     if (e >= 0 && e < E) s_pred[e] = 1;
   }
   __syncthreads();
+  for (int e = tid; e < E; e += 256) s_off[e] = s_cnt[e];
+  __syncthreads();
+  block_excl_scan(s_off, E, s_scan);
+  for (int e = tid; e < E; e += 256) {
+    a.offs[e] = s_off[e];
+    s_cur[e] = s_off[e];
+  }
+  if (tid == 0) a.offs[E] = Tk;
+  __syncthreads();
+  for (int s = tid; s < Tk; s += 256) a.slots[atomicAdd(&s_cur[ids[s]], 1)] = s;
+  if (a.has_shared)
+    for (int t = tid; t < a.T; t += 256) a.slots[Tk + t] = Tk + t;
   // Work lists: streaming (0 < rows < R) and matrix-core (rows >= R).  With a
-  // lookahead prediction, predicted experts come first; order never changes a
-  // result, only when an expert's weights are streamed.
+  // lookahead prediction the predicted experts come first; the order decides
+  // only when an expert's weights are read, never a value.
   for (int path = 0; path < 2; ++path) {
     int base = 0;
     for (int pass = 0; pass < 2; ++pass) {
@@ -192,21 +196,12 @@ __device__ void bucket_final(const RouterArgs& a) {
         const bool on = path == 0 ? (c > 0 && c < R) : (c >= R);
         const bool first = pv ? s_pred[e] != 0 : true;
         s_flag[e] = on && (pass == 0 ? first : !first) ? 1 : 0;
+        s_cur[e] = s_flag[e];
       }
       __syncthreads();
-      // flags -> positions (scan keeps the flag in s_scan-derived order)
-      for (int e = tid; e < E; e += 256) s_off[e] = s_flag[e];
-      __syncthreads();
-      const int n = block_excl_scan(s_off, E, s_scan);
+      const int n = block_excl_scan(s_cur, E, s_scan);
       for (int e = tid; e < E; e += 256)
-        if (s_flag[e]) {
-          int4 it;
-          it.x = e;
-          it.y = s_cnt[e];
-          it.z = 0;  // list offset filled below
-          it.w = 0;
-          (path == 0 ? a.items : a.mitems)[base + s_off[e]] = it;
-        }
+        if (s_flag[e]) (path == 0 ? a.items : a.mitems)[base + s_cur[e]] = make_int4(e, s_cnt[e], s_off[e], 0);
       base += n;
       __syncthreads();
       if (!pv) break;
@@ -214,150 +209,262 @@ __device__ void bucket_final(const RouterArgs& a) {
     if (tid == 0) s_tot[path] = base;
     __syncthreads();
   }
-  // list offsets (exclusive scan of counts, recomputed) for each item
-  for (int e = tid; e < E; e += 256) s_off[e] = s_cnt[e];
-  __syncthreads();
-  block_excl_scan(s_off, E, s_scan);
   int n_gemv = s_tot[0], n_mfma = s_tot[1];
-  for (int i = tid; i < n_gemv; i += 256) a.items[i].z = s_off[a.items[i].x];
-  for (int i = tid; i < n_mfma; i += 256) a.mitems[i].z = s_off[a.mitems[i].x];
-  __syncthreads();
-  if (tid == 0 && a.has_shared) {
-    int4 it;
-    it.x = E;
-    it.y = a.T;
-    it.z = Tk;
-    it.w = 0;
-    if (a.T >= R) a.mitems[n_mfma++] = it;
-    else a.items[n_gemv++] = it;
+  if (a.has_shared) {
+    if (a.T >= R) {
+      if (tid == 0) a.mitems[n_mfma] = make_int4(E, a.T, Tk, 0);
+      ++n_mfma;
+    } else {
+      if (tid == 0) a.items[n_gemv] = make_int4(E, a.T, Tk, 0);
+      ++n_gemv;
+    }
   }
   __syncthreads();
-  if (tid == 0) s_tot[2] = n_mfma;
-  __syncthreads();
-  n_mfma = s_tot[2];
-  // matrix-core row tiles: (item, first row)
-  for (int i = tid; i < n_mfma; i += 256) s_flag[i] = (a.mitems[i].y + kMfmaBM - 1) / kMfmaBM;
-  __syncthreads();
-  for (int i = tid; i < n_mfma; i += 256) s_off[i] = s_flag[i];
-  __syncthreads();
-  const int n_tiles = block_excl_scan(s_off, n_mfma, s_scan);
-  for (int i = tid; i < n_mfma; i += 256)
-    for (int j = 0; j < s_flag[i]; ++j) a.mtiles[s_off[i] + j] = make_int2(i, j * kMfmaBM);
+  // matrix-core row tiles (item, first row): 128-row tiles for items with
+  // >= wide_min_rows rows, 32-row tiles for the others
+  int n_tiles = 0, n_narrow = 0;
+  for (int wide = 1; wide >= 0; --wide) {
+    const int bm = wide ? kMfmaBM : kNarrowBM;
+    for (int i = tid; i < n_mfma; i += 256) {
+      const int rows = i < s_tot[1] ? s_cnt[a.mitems[i].x] : a.T;
+      const bool mine = wide ? rows >= a.wide_min_rows : rows < a.wide_min_rows;
+      s_flag[i] = mine ? (rows + bm - 1) / bm : 0;
+      s_cur[i] = s_flag[i];
+    }
+    __syncthreads();
+    const int n = block_excl_scan(s_cur, n_mfma, s_scan);
+    int2* out = wide ? a.mtiles : a.ntiles;
+    for (int i = tid; i < n_mfma; i += 256)
+      for (int j = 0; j < s_flag[i]; ++j) out[s_cur[i] + j] = make_int2(i, j * bm);
+    __syncthreads();
+    if (wide) n_tiles = n; else n_narrow = n;
+  }
   if (tid == 0) {
     a.misc[kNGemv] = n_gemv;
     a.misc[kNMfma] = n_mfma;
     a.misc[kNTiles] = n_tiles;
+    a.misc[kNNarrow] = n_narrow;
     a.misc[kPredValid] = 0;
     a.misc[kCntAll] = 0;
   }
 }
 
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  __shared__ uint16_t xr[kRouterTokMax][kRouterWaves][64];
-  __shared__ uint16_t xrl[kRouterTokMax][kRouterWaves][64];
-  __shared__ float xsum[kRouterTokMax][kRouterWaves];
-  __shared__ float red[kRouterWaves][kRouterTokMax][64];
-  __shared__ int flag;
-
+// Router GEMV: workgroup = (64-expert row block, k-split of kRouterGPW groups,
+// token block of up to kRouterTokMax tokens).  Writes one fp32 partial logit
+// per (k-split, token, expert); the rb == 0 workgroups also publish x in fp16
+// (4-bit pair order) and its per-group sums for the expert kernels.
+__global__ __launch_bounds__(256) void router_gemv_kernel(RouterArgs a) {
+  __shared__ __align__(16) uint16_t xr[kRouterTokMax * kRouterGPW * 64];    // 8-bit pair order
+  __shared__ __align__(16) uint16_t xrl[kRouterTokMax * kRouterGPW * 64];   // lo halves
+  __shared__ float xsum[kRouterTokMax * kRouterGPW];
+  __shared__ float red[kRouterWaves * kRouterTokMax * 64];
   const int rb = blockIdx.x, ks = blockIdx.y, tb = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = tb * a.TBR;
   const int nt = min(a.TBR, a.T - t0);
-  const int g0 = ks * kRouterWaves;
-  const int ng = min(kRouterWaves, a.G - g0);
+  const int g0 = ks * kRouterGPW;
+  const int ng = min(kRouterGPW, a.G - g0);
   const bool wx = a.write_x && rb == 0;
 
-  // 1. x -> fp16 hi (+ lo for fp32 input) in the 8-bit pair order; the rb == 0
-  //    workgroups also publish it in the 4-bit pair order for the experts.
-  for (int i = tid; i < nt * ng * 64; i += 256) {
-    const int t = i / (ng * 64), r = i - t * (ng * 64), gl = r >> 6, c = r & 63;
-    const size_t src = (size_t)(t0 + t) * a.H + (size_t)(g0 + gl) * 64 + c;
-    const float v = a.x_f32 ? static_cast<const float*>(a.x)[src]
-                            : bf16f(static_cast<const uint16_t*>(a.x)[src]);
-    const _Float16 hi = (_Float16)v;
-    const _Float16 lo = (_Float16)(v - (float)hi);
-    xr[t][gl][pair_pos8(c)] = f16bits(hi);
-    xrl[t][gl][pair_pos8(c)] = f16bits(lo);
-    if (wx) {
-      const size_t dst = (size_t)(t0 + t) * a.H + (size_t)(g0 + gl) * 64 + pair_pos4(c);
-      a.x16[dst] = f16bits(hi);
-      if (a.x_f32) a.x16lo[dst] = f16bits(lo);
+  // weight tiles first (two groups per wave), so they are in flight while x is staged
+  constexpr int GW = kRouterGPW / kRouterWaves;
+  uint4 c[GW][4];
+  uint32_t sbw[GW];
+#pragma unroll
+  for (int j = 0; j < GW; ++j) {
+    const int gl = wave + j * kRouterWaves;
+    if (gl < ng) {
+      const uint8_t* tile = a.router + ((size_t)rb * a.G + g0 + gl) * kQ8TileBytes;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) c[j][cc] = ld16(tile + cc * 1024 + lane * 16);
+      sbw[j] = ld4(tile + kQ8CodeBytes + lane * 4);
+    }
+  }
+  // x -> fp16 hi (+ lo for fp32 input), 8 columns per chunk, loads batched
+  {
+    const int nch = nt * ng * 8;   // <= 1024
+    constexpr int CH = kRouterTokMax * kRouterGPW * 8 / 256;
+    uint4 raw[CH][2];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int i = tid + 256 * j;
+      if (i < nch) {
+        const int t = i / (ng * 8), r = i - t * (ng * 8);
+        const size_t src = (size_t)(t0 + t) * a.H + (size_t)g0 * 64 + r * 8;
+        if (a.x_f32) {
+          raw[j][0] = reinterpret_cast<const uint4*>(static_cast<const float*>(a.x) + src)[0];
+          raw[j][1] = reinterpret_cast<const uint4*>(static_cast<const float*>(a.x) + src)[1];
+        } else {
+          raw[j][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + src);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int i = tid + 256 * j;
+      if (i < nch) {
+        const int t = i / (ng * 8), r = i - t * (ng * 8), gl = r >> 3, c8 = (r & 7) * 8;
+        float v[8];
+        if (a.x_f32) {
+          const uint32_t w[8] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
+                                 raw[j][1].x, raw[j][1].y, raw[j][1].z, raw[j][1].w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = __builtin_bit_cast(float, w[q]);
+        } else {
+          const uint32_t w[4] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] = __builtin_bit_cast(float, w[q] << 16);
+            v[2 * q + 1] = __builtin_bit_cast(float, w[q] & 0xffff0000u);
+          }
+        }
+        uint16_t hi[8], lo[8], hi4[8], lo4[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const _Float16 h = (_Float16)v[q];
+          const uint16_t hb = f16bits(h), lb = f16bits((_Float16)(v[q] - (float)h));
+          hi[pair_pos8(q)] = hb;     // q and c8 + q share their 8-block position map
+          lo[pair_pos8(q)] = lb;
+          hi4[pair_pos4(q)] = hb;
+          lo4[pair_pos4(q)] = lb;
+        }
+        uint16_t* dh = xr + (t * kRouterGPW + gl) * 64 + c8;
+        uint16_t* dl = xrl + (t * kRouterGPW + gl) * 64 + c8;
+        *reinterpret_cast<uint4*>(dh) = *reinterpret_cast<const uint4*>(hi);
+        *reinterpret_cast<uint4*>(dl) = *reinterpret_cast<const uint4*>(lo);
+        if (wx) {
+          const size_t dst = (size_t)(t0 + t) * a.H + (size_t)(g0 + gl) * 64 + c8;
+          *reinterpret_cast<uint4*>(a.x16 + dst) = *reinterpret_cast<const uint4*>(hi4);
+          if (a.x_f32) *reinterpret_cast<uint4*>(a.x16lo + dst) = *reinterpret_cast<const uint4*>(lo4);
+        }
+      }
     }
   }
   __syncthreads();
   if (tid < nt * ng) {
     const int t = tid / ng, gl = tid - t * ng;
-    float s = 0.f;
-    for (int c = 0; c < 64; ++c) s += f16f(xr[t][gl][c]) + f16f(xrl[t][gl][c]);
-    xsum[t][gl] = s;
-    if (wx) a.xs[(size_t)(t0 + t) * a.G + g0 + gl] = s;
+    const uint16_t* xh = xr + (t * kRouterGPW + gl) * 64;
+    const uint16_t* xq = xrl + (t * kRouterGPW + gl) * 64;
+    float sum = 0.f;
+    for (int q = 0; q < 64; ++q) sum += f16f(xh[q]) + f16f(xq[q]);
+    xsum[t * kRouterGPW + gl] = sum;
+    if (wx) a.xs[(size_t)(t0 + t) * a.G + g0 + gl] = sum;
   }
   __syncthreads();
 
-  // 2. one wave per group: lane = expert row
-  if (wave < ng) {
-    const uint8_t* tile = a.router + ((size_t)rb * a.G + g0 + wave) * kQ8TileBytes;
+  {
     const Lift L;
-    uint32_t w[32];
+    float acc[kRouterTokMax];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const uint4 c = ld16(tile + cc * 1024 + lane * 16);
-      const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+    for (int t = 0; t < kRouterTokMax; ++t) acc[t] = 0.f;
 #pragma unroll
-      for (int dw = 0; dw < 4; ++dw)
+    for (int j = 0; j < GW; ++j) {
+      const int gl = wave + j * kRouterWaves;
+      if (gl < ng) {
+        uint32_t w[32];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) w[(cc * 4 + dw) * 2 + p] = L.q8(d[dw], p);
-    }
-    const uint32_t sb = ld4(tile + kQ8CodeBytes + lane * 4);
-    const float s = f16f(sb & 0xffffu), b = f16f(sb >> 16);
-    const float cf = fmaf(-1024.f, s, b);
-    for (int t = 0; t < nt; ++t) {
-      const uint32_t* xp = reinterpret_cast<const uint32_t*>(&xr[t][wave][0]);
-      float d = 0.f;
+        for (int cc = 0; cc < 4; ++cc) {
+          const uint32_t d[4] = {c[j][cc].x, c[j][cc].y, c[j][cc].z, c[j][cc].w};
 #pragma unroll
-      for (int i = 0; i < 32; ++i) d = dot2(w[i], xp[i], d);
-      if (a.x_f32) {
-        const uint32_t* xq = reinterpret_cast<const uint32_t*>(&xrl[t][wave][0]);
+          for (int dw = 0; dw < 4; ++dw)
 #pragma unroll
-        for (int i = 0; i < 32; ++i) d = dot2(w[i], xq[i], d);
+            for (int p = 0; p < 2; ++p) w[(cc * 4 + dw) * 2 + p] = L.q8(d[dw], p);
+        }
+        const float s = f16f(sbw[j] & 0xffffu), b = f16f(sbw[j] >> 16);
+        const float cf = fmaf(-1024.f, s, b);
+#pragma unroll
+        for (int t = 0; t < kRouterTokMax; ++t) {
+          if (t < nt) {
+            const uint4* xp = reinterpret_cast<const uint4*>(xr + (t * kRouterGPW + gl) * 64);
+            float d = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const uint4 xv = xp[i];
+              d = dot2(w[4 * i + 0], xv.x, d);
+              d = dot2(w[4 * i + 1], xv.y, d);
+              d = dot2(w[4 * i + 2], xv.z, d);
+              d = dot2(w[4 * i + 3], xv.w, d);
+            }
+            if (a.x_f32) {
+              const uint4* xq = reinterpret_cast<const uint4*>(xrl + (t * kRouterGPW + gl) * 64);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const uint4 xv = xq[i];
+                d = dot2(w[4 * i + 0], xv.x, d);
+                d = dot2(w[4 * i + 1], xv.y, d);
+                d = dot2(w[4 * i + 2], xv.z, d);
+                d = dot2(w[4 * i + 3], xv.w, d);
+              }
+            }
+            acc[t] += fmaf(s, d, cf * xsum[t * kRouterGPW + gl]);
+          }
+        }
       }
-      red[wave][t][lane] = fmaf(s, d, cf * xsum[t][wave]);
     }
+#pragma unroll
+    for (int t = 0; t < kRouterTokMax; ++t)
+      if (t < nt) red[(wave * kRouterTokMax + t) * 64 + lane] = acc[t];
   }
   __syncthreads();
   for (int i = tid; i < nt * 64; i += 256) {
     const int t = i >> 6, l = i & 63;
     float v = 0.f;
-    for (int w = 0; w < ng; ++w) v += red[w][t][l];
+    for (int w = 0; w < kRouterWaves; ++w) v += red[(w * kRouterTokMax + t) * 64 + l];
     a.part[((size_t)ks * a.T + t0 + t) * a.Epad + rb * 64 + l] = v;
   }
+}
 
-  // 3. last workgroup of this token block: top-k
-  __threadfence();
+// Top-k: workgroup = TPW tokens (TPW * Epad <= 512).  Sums the k-split
+// partials in fixed order (all loads of a thread issued together), adds the
+// logit bias, then one wave per token selects k experts by (logit desc,
+// index asc) with wave64 shuffles and takes the softmax over them.
+__global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a, int tpw) {
+  __shared__ float s_lg[512];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * tpw;
+  const int nt = min(tpw, a.T - t0);
+  const int npair = nt * a.Epad;   // <= 512: at most 2 per thread
+  float acc[2] = {0.f, 0.f};
+  for (int k0 = 0; k0 < a.KS; k0 += 16) {
+    float pv[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = tid + 256 * j;
+      const int t = i / a.Epad, e = i - t * a.Epad;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        pv[j][q] = (i < npair && e < a.E && k0 + q < a.KS)
+                       ? a.part[((size_t)(k0 + q) * a.T + t0 + t) * a.Epad + e]
+                       : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[j] += pv[j][q];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 256 * j;
+    if (i < npair) {
+      const int t = i / a.Epad, e = i - t * a.Epad;
+      float v = -INFINITY;
+      if (e < a.E) {
+        const float sum = a.bias ? acc[j] + a.bias[e] : acc[j];
+        if (a.mode == 1) a.logits_out[(size_t)(t0 + t) * a.E + e] = sum;
+        v = sum == sum ? sum : -INFINITY;   // a NaN logit (out of contract) ranks last
+      }
+      s_lg[i] = v;
+    }
+  }
+  if (a.mode == 1) return;
   __syncthreads();
-  if (tid == 0) flag = (atomicAdd(&a.cnt_tb[tb], 1) == a.n_rb * a.KS - 1);
-  __syncthreads();
-  if (!flag) return;
-  __threadfence();
-  if (tid == 0) a.cnt_tb[tb] = 0;
-
   const int NE = a.Epad >> 6;
   for (int t = wave; t < nt; t += kRouterWaves) {
     const int tok = t0 + t;
     float v[kMaxExperts / 64];
 #pragma unroll
-    for (int i = 0; i < kMaxExperts / 64; ++i) {
-      v[i] = -INFINITY;
-      const int e = lane + 64 * i;
-      if (i < NE && e < a.E) {
-        float s = 0.f;
-        for (int k2 = 0; k2 < a.KS; ++k2) s += a.part[((size_t)k2 * a.T + tok) * a.Epad + e];
-        if (a.bias) s += a.bias[e];
-        v[i] = s == s ? s : -INFINITY;   // a NaN logit (out of contract) ranks last
-        if (a.mode == 1) a.logits_out[(size_t)tok * a.E + e] = s;
-      }
-    }
-    if (a.mode == 1) continue;
+    for (int i = 0; i < kMaxExperts / 64; ++i)
+      v[i] = i < NE ? s_lg[t * a.Epad + lane + 64 * i] : -INFINITY;
     uint32_t taken = 0;
     float myv = 0.f;
     int myi = 0;
@@ -387,11 +494,11 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
         myi = bi;
       }
     }
+    myi = myi < a.E ? myi : 0;        // always an expert index, whatever the inputs
     const float mx = __shfl(myv, 0);
     const float z = lane < a.k ? expf(myv - mx) : 0.f;
     float sum = 0.f;
     for (int j = 0; j < a.k; ++j) sum += __shfl(z, j);
-    myi = myi < a.E ? myi : 0;        // always an expert index, whatever the inputs
     if (lane < a.k) {
       const size_t o = (size_t)tok * a.k + lane;
       if (a.mode == 0) {
@@ -400,29 +507,17 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
         a.p_ws[o] = p;
         if (a.ids_out) a.ids_out[o] = myi;
         if (a.p_out) a.p_out[o] = p;
-        a.rank[o] = atomicAdd(&a.counts[myi], 1);
       } else {
         a.pred[o] = myi;
       }
     }
   }
-  if (a.mode == 1) return;
+  if (a.mode == 2 && blockIdx.x == 0 && tid == 0) a.misc[kPredValid] = a.T * a.k;
+}
 
-  // 4. last token block: bucketing (forward) or publish the prediction
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) flag = (atomicAdd(&a.misc[kCntAll], 1) == a.n_tb - 1);
-  __syncthreads();
-  if (!flag) return;
-  __threadfence();
-  if (a.mode == 2) {
-    if (tid == 0) {
-      a.misc[kPredValid] = a.T * a.k;   // number of predicted slots
-      a.misc[kCntAll] = 0;
-    }
-    return;
-  }
-  bucket_final(a);
+__global__ __launch_bounds__(256) void bucket_kernel(RouterArgs a) {
+  __shared__ __align__(16) uint8_t smem[4 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + kMaxExperts];
+  bucket_tokens(a, a.ids_ws, smem);
 }
 
 // --------------------------------------------------------- streaming path --
@@ -434,15 +529,107 @@ __device__ __forceinline__ size_t hs_off(int slot, int Tk, int I, int Is) {
   return slot < Tk ? (size_t)slot * (I >> 6) : (size_t)Tk * (I >> 6) + (size_t)(slot - Tk) * (Is >> 6);
 }
 
+// One wave's share of a row-per-lane streaming GEMV: NMAT matrices (gate and
+// up, or down) over the groups [gbeg, gend) of one 64-row block, for nt <= MT
+// token rows held in LDS.  Weight tiles are loaded P groups ahead, so P*NMAT
+// 2.3 KB tiles per wave are in flight while earlier ones are consumed.
+// acc[m][t] += sum over the groups of (s * dot(x, 1024 + q) + (b - 1024 s) * sum(x)).
+// With LO, each staged row holds fp16 hi halves then lo halves (fp32 input);
+// both enter the same dot product, and xsl already sums hi + lo.
+template <int NMAT, int P>
+struct GemvStream {
+  const uint8_t* mat[NMAT];
+  int gbeg, gend, lane;
+  uint4 c0[P][NMAT], c1[P][NMAT];
+  uint32_t sb[P][NMAT];
+
+  __device__ __forceinline__ void load(int p, int g) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const uint8_t* t = mat[m] + (size_t)g * kQ4TileBytes;
+      c0[p][m] = ld16(t + lane * 16);
+      c1[p][m] = ld16(t + 1024 + lane * 16);
+      sb[p][m] = ld4(t + kQ4CodeBytes + lane * 4);
+    }
+  }
+  // Issue the first P groups' loads.  Every load is unconditional (a group
+  // index past the end is clamped to the last group) so the number of loads
+  // in flight is static and the compiler waits only for the buffer it reads.
+  // Requires gbeg < gend.
+  __device__ __forceinline__ void prefetch() {
+#pragma unroll
+    for (int p = 0; p < P; ++p) load(p, min(gbeg + p, gend - 1));
+  }
+  template <int MT, bool LO>
+  __device__ __forceinline__ void run(const uint32_t* xl, int xrow_dw, int lo_dw, const float* xsl,
+                                      int G, int nt, float (&acc)[NMAT][MT]) {
+    const Lift L;
+    for (int g0 = gbeg; g0 < gend; g0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int g = g0 + p;
+        {
+          uint32_t w[NMAT][32];
+          float s[NMAT], cf[NMAT];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
+            unpack16_q4(L, c0[p][m], w[m]);
+            unpack16_q4(L, c1[p][m], w[m] + 16);
+            s[m] = f16f(sb[p][m] & 0xffffu);
+            cf[m] = fmaf(-1024.f, s[m], f16f(sb[p][m] >> 16));
+          }
+          load(p, min(g + P, gend - 1));
+          if (g < gend) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            if (t < nt) {
+              float d[NMAT];
+#pragma unroll
+              for (int m = 0; m < NMAT; ++m) d[m] = 0.f;
+#pragma unroll
+              for (int half = 0; half < (LO ? 2 : 1); ++half) {
+                const uint4* xp =
+                    reinterpret_cast<const uint4*>(xl + t * xrow_dw + half * lo_dw + g * 32);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                  const uint4 xv = xp[i];
+#pragma unroll
+                  for (int m = 0; m < NMAT; ++m) {
+                    d[m] = dot2(w[m][4 * i + 0], xv.x, d[m]);
+                    d[m] = dot2(w[m][4 * i + 1], xv.y, d[m]);
+                    d[m] = dot2(w[m][4 * i + 2], xv.z, d[m]);
+                    d[m] = dot2(w[m][4 * i + 3], xv.w, d[m]);
+                  }
+                }
+              }
+              const float xsv = xsl[t * G + g];
+#pragma unroll
+              for (int m = 0; m < NMAT; ++m) acc[m][t] += fmaf(s[m], d[m], cf[m] * xsv);
+            }
+          }
+          }
+        }
+      }
+    }
+  }
+};
+
+constexpr int kGemvP = 4;   // groups in flight per wave
+
+// Streaming gate/up: workgroup = (work item, 64-row block of the expert's
+// intermediate dimension); 4 waves split the H/64 groups; token rows of x
+// (fp16 in the paired order) and their group sums are staged in LDS.
+template <bool LO>
 __global__ __launch_bounds__(256) void gemv_up_kernel(
     const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
-    int H, int E, int k, int I, int Is, int T, int x_f32, const uint32_t* __restrict__ x16,
+    int H, int E, int k, int I, int Is, int T, const uint32_t* __restrict__ x16,
     const uint32_t* __restrict__ x16lo, const float* __restrict__ xs,
     const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
-    uint16_t* __restrict__ hbuf, float* __restrict__ hs) {
+    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int mt) {
+  extern __shared__ uint32_t dyn[];
   __shared__ int s_tok[kGemvTok];
   __shared__ int s_slot[kGemvTok];
-  __shared__ float red[kGemvWaves][2][kGemvTok][64];
+  __shared__ float red[kGemvWaves][2][kGemvTokV2][64];
   const int item_i = blockIdx.y;
   if (item_i >= misc[kNGemv]) return;
   const int4 it = items[item_i];
@@ -453,71 +640,56 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(
   if (rb * 64 >= inter) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H >> 6, Tk = T * k;
+  const int xrow = LO ? H : H >> 1;               // dwords per staged row (hi [+ lo])
+  uint32_t* xl = dyn;                              // [mt][xrow]
+  float* xsl = reinterpret_cast<float*>(dyn + mt * xrow);   // [mt][G]
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
   const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
-  const uint8_t* gate = rec + kHeaderBytes + (size_t)rb * G * kQ4TileBytes;
-  const uint8_t* up = gate + sec;
-  const int gbeg = (G * wave) / kGemvWaves, gend = (G * (wave + 1)) / kGemvWaves;
-  const int hw = H >> 1;  // dwords per x16 row
-  const Lift L;
+  GemvStream<2, kGemvP> st;
+  st.mat[0] = rec + kHeaderBytes + (size_t)rb * G * kQ4TileBytes;
+  st.mat[1] = st.mat[0] + sec;
+  st.gbeg = (G * wave) / kGemvWaves;
+  st.gend = (G * (wave + 1)) / kGemvWaves;
+  st.lane = lane;
 
-  for (int p0 = 0; p0 < m; p0 += kGemvTok) {
-    const int nt = min(kGemvTok, m - p0);
+  for (int p0 = 0; p0 < m; p0 += mt) {
+    const int nt = min(mt, m - p0);
+    if (p0 > 0) __syncthreads();
     if (tid < nt) {
       const int slot = slots[loff + p0 + tid];
       s_slot[tid] = slot;
       s_tok[tid] = slot < Tk ? slot / k : slot - Tk;
     }
     __syncthreads();
-    float ag[kGemvTok], au[kGemvTok];
-#pragma unroll
-    for (int t = 0; t < kGemvTok; ++t) ag[t] = au[t] = 0.f;
-    for (int g = gbeg; g < gend; ++g) {
-      const uint8_t* tg = gate + (size_t)g * kQ4TileBytes;
-      const uint8_t* tu = up + (size_t)g * kQ4TileBytes;
-      const uint4 cg0 = ld16(tg + lane * 16), cg1 = ld16(tg + 1024 + lane * 16);
-      const uint4 cu0 = ld16(tu + lane * 16), cu1 = ld16(tu + 1024 + lane * 16);
-      const uint32_t sbg = ld4(tg + kQ4CodeBytes + lane * 4);
-      const uint32_t sbu = ld4(tu + kQ4CodeBytes + lane * 4);
-      uint32_t wg[32], wu[32];
-      unpack16_q4(L, cg0, wg);
-      unpack16_q4(L, cg1, wg + 16);
-      unpack16_q4(L, cu0, wu);
-      unpack16_q4(L, cu1, wu + 16);
-      const float sg = f16f(sbg & 0xffffu), cg = fmaf(-1024.f, sg, f16f(sbg >> 16));
-      const float su = f16f(sbu & 0xffffu), cu = fmaf(-1024.f, su, f16f(sbu >> 16));
-#pragma unroll
-      for (int t = 0; t < kGemvTok; ++t) {
-        if (t < nt) {
-          const int tok = __builtin_amdgcn_readfirstlane(s_tok[t]);
-          const cu32p xp = as_const(x16 + (size_t)tok * hw + g * 32);
-          float dg = 0.f, du = 0.f;
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const uint32_t xv = xp[i];
-            dg = dot2(wg[i], xv, dg);
-            du = dot2(wu[i], xv, du);
-          }
-          if (x_f32) {
-            const cu32p xq = as_const(x16lo + (size_t)tok * hw + g * 32);
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-              const uint32_t xv = xq[i];
-              dg = dot2(wg[i], xv, dg);
-              du = dot2(wu[i], xv, du);
-            }
-          }
-          const float xsv = as_const(xs)[(size_t)tok * G + g];
-          ag[t] += fmaf(sg, dg, cg * xsv);
-          au[t] += fmaf(su, du, cu * xsv);
-        }
-      }
+    // stage x rows (hi, then lo for fp32 input) and group sums
+    const int hq = H >> 3;   // uint4 per half-row
+    for (int i = tid; i < nt * hq; i += 256) {
+      const int t = i / hq, c = i - t * hq;
+      reinterpret_cast<uint4*>(xl + t * xrow)[c] =
+          reinterpret_cast<const uint4*>(x16 + (size_t)s_tok[t] * (H >> 1))[c];
     }
+    if (LO)
+      for (int i = tid; i < nt * hq; i += 256) {
+        const int t = i / hq, c = i - t * hq;
+        reinterpret_cast<uint4*>(xl + t * xrow + (H >> 1))[c] =
+            reinterpret_cast<const uint4*>(x16lo + (size_t)s_tok[t] * (H >> 1))[c];
+      }
+    for (int i = tid; i < nt * G; i += 256) {
+      const int t = i / G, g = i - t * G;
+      xsl[i] = xs[(size_t)s_tok[t] * G + g];
+    }
+    const bool busy = st.gbeg < st.gend;
+    if (busy) st.prefetch();
+    __syncthreads();
+    float acc[2][kGemvTokV2];
 #pragma unroll
-    for (int t = 0; t < kGemvTok; ++t)
+    for (int t = 0; t < kGemvTokV2; ++t) acc[0][t] = acc[1][t] = 0.f;
+    if (busy) st.run<kGemvTokV2, LO>(xl, xrow, H >> 1, xsl, G, nt, acc);
+#pragma unroll
+    for (int t = 0; t < kGemvTokV2; ++t)
       if (t < nt) {
-        red[wave][0][t][lane] = ag[t];
-        red[wave][1][t][lane] = au[t];
+        red[wave][0][t][lane] = acc[0][t];
+        red[wave][1][t][lane] = acc[1][t];
       }
     __syncthreads();
     for (int t = wave; t < nt; t += kGemvWaves) {
@@ -539,14 +711,18 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(
   }
 }
 
+// Streaming down: workgroup = (work item, 64-row block of H); 4 waves split
+// the inter/64 groups; the slots' h rows (fp16, paired order) and their group
+// sums are staged in LDS.  Writes one fp32 row per slot.
 __global__ __launch_bounds__(256) void gemv_down_kernel(
     const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
     int H, int E, int k, int I, int Is, int T, const int4* __restrict__ items,
     const int* __restrict__ misc, const int* __restrict__ slots,
     const uint32_t* __restrict__ hbuf32, const float* __restrict__ hs,
-    float* __restrict__ yslot) {
+    float* __restrict__ yslot, int mt) {
+  extern __shared__ uint32_t dyn[];
   __shared__ int s_slot[kGemvTok];
-  __shared__ float red[kGemvWaves][kGemvTok][64];
+  __shared__ float red[kGemvWaves][kGemvTokV2][64];
   const int item_i = blockIdx.y;
   if (item_i >= misc[kNGemv]) return;
   const int4 it = items[item_i];
@@ -556,42 +732,42 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
   const int rb = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H >> 6, G2 = inter >> 6, Tk = T * k;
+  const int hrow = inter >> 1;
+  uint32_t* hl = dyn;                                        // [mt][hrow]
+  float* hsl = reinterpret_cast<float*>(dyn + mt * hrow);    // [mt][G2]
   const size_t sec = (size_t)G2 * G * kQ4TileBytes;
   const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
-  const uint8_t* down = rec + kHeaderBytes + 2 * sec + (size_t)rb * G2 * kQ4TileBytes;
-  const int gbeg = (G2 * wave) / kGemvWaves, gend = (G2 * (wave + 1)) / kGemvWaves;
-  const Lift L;
+  GemvStream<1, kGemvP> st;
+  st.mat[0] = rec + kHeaderBytes + 2 * sec + (size_t)rb * G2 * kQ4TileBytes;
+  st.gbeg = (G2 * wave) / kGemvWaves;
+  st.gend = (G2 * (wave + 1)) / kGemvWaves;
+  st.lane = lane;
 
-  for (int p0 = 0; p0 < m; p0 += kGemvTok) {
-    const int nt = min(kGemvTok, m - p0);
+  for (int p0 = 0; p0 < m; p0 += mt) {
+    const int nt = min(mt, m - p0);
+    if (p0 > 0) __syncthreads();
     if (tid < nt) s_slot[tid] = slots[loff + p0 + tid];
     __syncthreads();
-    float acc[kGemvTok];
-#pragma unroll
-    for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.f;
-    for (int g = gbeg; g < gend; ++g) {
-      const uint8_t* td = down + (size_t)g * kQ4TileBytes;
-      const uint4 c0 = ld16(td + lane * 16), c1 = ld16(td + 1024 + lane * 16);
-      const uint32_t sb = ld4(td + kQ4CodeBytes + lane * 4);
-      uint32_t w[32];
-      unpack16_q4(L, c0, w);
-      unpack16_q4(L, c1, w + 16);
-      const float s = f16f(sb & 0xffffu), c = fmaf(-1024.f, s, f16f(sb >> 16));
-#pragma unroll
-      for (int t = 0; t < kGemvTok; ++t) {
-        if (t < nt) {
-          const int slot = __builtin_amdgcn_readfirstlane(s_slot[t]);
-          const cu32p hp = as_const(hbuf32 + (h_off(slot, Tk, I, Is) >> 1) + g * 32);
-          float d = 0.f;
-#pragma unroll
-          for (int i = 0; i < 32; ++i) d = dot2(w[i], hp[i], d);
-          acc[t] += fmaf(s, d, c * as_const(hs)[hs_off(slot, Tk, I, Is) + g]);
-        }
-      }
+    const int hq = inter >> 3;
+    for (int i = tid; i < nt * hq; i += 256) {
+      const int t = i / hq, c = i - t * hq;
+      reinterpret_cast<uint4*>(hl + t * hrow)[c] =
+          reinterpret_cast<const uint4*>(hbuf32 + (h_off(s_slot[t], Tk, I, Is) >> 1))[c];
     }
+    for (int i = tid; i < nt * G2; i += 256) {
+      const int t = i / G2, g = i - t * G2;
+      hsl[i] = hs[hs_off(s_slot[t], Tk, I, Is) + g];
+    }
+    const bool busy = st.gbeg < st.gend;
+    if (busy) st.prefetch();
+    __syncthreads();
+    float acc[1][kGemvTokV2];
 #pragma unroll
-    for (int t = 0; t < kGemvTok; ++t)
-      if (t < nt) red[wave][t][lane] = acc[t];
+    for (int t = 0; t < kGemvTokV2; ++t) acc[0][t] = 0.f;
+    if (busy) st.run<kGemvTokV2, false>(hl, hrow, 0, hsl, G2, nt, acc);
+#pragma unroll
+    for (int t = 0; t < kGemvTokV2; ++t)
+      if (t < nt) red[wave][t][lane] = acc[0][t];
     __syncthreads();
     for (int t = wave; t < nt; t += kGemvWaves) {
       float v = 0.f;
@@ -600,6 +776,369 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
       yslot[(size_t)s_slot[t] * H + rb * 64 + lane] = v;
     }
     __syncthreads();
+  }
+}
+
+// ------------------------------------------------------- matrix-core path --
+//
+// One workgroup = one 128-row tile of one expert's slot list x one column
+// block (gate/up: 128 intermediate columns; down: 256 output columns).  Each
+// of the 4 waves owns 32 gate+up columns (or 64 down columns), dequantizes its
+// weight rows to fp16 in registers (fp16(s*q + b), one rounding) and runs
+// v_mfma_f32_32x32x16_f16 against the gathered token rows, which the workgroup
+// stages once per 64-wide group in double-buffered LDS.  Within a group the
+// 64 k-values are taken in the paired order the fp16 activations are stored
+// in, so the MFMA slots of A and B line up without any shuffling: step ks of
+// lane half hi covers the codes of dword ks of 16-byte half hi of the row.
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kALdsRow = 72;   // halfs per staged row: 64 + 8 of padding
+
+struct MfmaArgs {
+  const uint8_t* bank;
+  uint64_t stride;
+  const uint8_t* shared;
+  int H, E, k, I, Is, T;
+  const uint16_t* x16;
+  const uint16_t* x16lo;
+  const uint16_t* hsrc;    // down: h rows
+  uint16_t* hdst;          // up: h rows
+  const int4* mitems;
+  const int2* mtiles;
+  const int2* ntiles;
+  const int* misc;
+  const int* slots;
+  float* yslot;
+};
+
+// 8 nibbles (one dword of codes) -> 8 fp16 weights s*q + b in MFMA slot order.
+__device__ __forceinline__ f16x8 dequant8(const Lift& L, uint32_t dw, f16x2 s2, f16x2 b2) {
+  const f16x2 off = {(_Float16)1024.f, (_Float16)1024.f};
+  f16x8 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const f16x2 q = __builtin_bit_cast(f16x2, L.q4(dw, p)) - off;   // exact
+    const f16x2 w = __builtin_elementwise_fma(q, s2, b2);           // one rounding
+    r[2 * p] = w[0];
+    r[2 * p + 1] = w[1];
+  }
+  return r;
+}
+
+template <bool UP, bool LO>
+__global__ __launch_bounds__(256) void mfma_expert_kernel(MfmaArgs a) {
+  constexpr int NA = LO ? 2 : 1;
+  __shared__ __align__(16) uint16_t As[2][NA][kMfmaBM * kALdsRow];
+  __shared__ int s_src[kMfmaBM];    // element offset of each row's A source
+  __shared__ int s_slot[kMfmaBM];
+  const int tile_i = blockIdx.y;
+  if (tile_i >= a.misc[kNTiles]) return;
+  const int2 tl = a.mtiles[tile_i];
+  const int4 it = a.mitems[tl.x];
+  const int e = it.x, m_tot = it.y, loff = it.z, m0 = tl.y;
+  const int mrows = min(kMfmaBM, m_tot - m0);
+  const bool sh = e == a.E;
+  const int inter = sh ? a.Is : a.I;
+  const int G = a.H >> 6;
+  const int Kg = UP ? G : inter >> 6;
+  constexpr int CB = UP ? 128 : 256;            // columns per workgroup
+  const int ncols = UP ? inter : a.H;
+  if (blockIdx.x * CB >= ncols) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int n0 = blockIdx.x * CB + wave * (UP ? 32 : 64);
+  const bool won = n0 < ncols;
+  const int Tk = a.T * a.k;
+  if (tid < kMfmaBM) {
+    const int slot = a.slots[loff + m0 + (tid < mrows ? tid : 0)];
+    s_slot[tid] = slot;
+    s_src[tid] = UP ? (slot < Tk ? slot / a.k : slot - Tk) * a.H : (int)h_off(slot, Tk, a.I, a.Is);
+  }
+  const uint8_t* rec = sh ? a.shared : a.bank + (size_t)e * a.stride;
+  const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
+  const uint8_t* bb[2];
+  int brow[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    // a wave past the last column still issues (unused) loads: point them at row 0
+    const int r = won ? (UP ? n0 : n0 + nb * 32) : 0;
+    const uint8_t* mat = rec + kHeaderBytes + (UP ? (nb ? sec : 0) : 2 * sec);
+    bb[nb] = mat + (size_t)(r >> 6) * Kg * kQ4TileBytes;
+    brow[nb] = (r & 63) + l32;
+  }
+  const uint16_t* asrc = UP ? a.x16 : a.hsrc;
+  __syncthreads();
+
+  // A staging: 128 rows x 8 sixteen-byte segments per group = 4 per thread.
+  size_t a_off[4];
+  int a_lds[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + 256 * j, r = i >> 3, sgm = i & 7;
+    a_off[j] = (size_t)s_src[r] + sgm * 8;
+    a_lds[j] = r * kALdsRow + sgm * 8;
+  }
+  const Lift L;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mb][nb][j] = 0.f;
+  const int nmb = (mrows + 31) >> 5;
+
+  // Weight fragments: a ring of PB groups loaded ahead.  Loads are never
+  // behind a branch (indexes past the end are clamped), so the compiler waits
+  // only for the ring entry it consumes; the group loop is padded to a
+  // multiple of PB and the padding iterations skip the math.
+  constexpr int PB = 4;
+  uint4 bc[PB][2];
+  uint32_t bs[PB][2];
+#pragma unroll
+  for (int q = 0; q < PB; ++q) {
+    const int gq = min(q, Kg - 1);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint8_t* t = bb[nb] + (size_t)gq * kQ4TileBytes;
+      bc[q][nb] = ld16(t + hi * 1024 + brow[nb] * 16);
+      bs[q][nb] = ld4(t + kQ4CodeBytes + brow[nb] * 4);
+    }
+  }
+  uint4 ar[4], al[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ar[j] = *reinterpret_cast<const uint4*>(asrc + a_off[j]);
+    if (LO) al[j] = *reinterpret_cast<const uint4*>(a.x16lo + a_off[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<uint4*>(&As[0][0][a_lds[j]]) = ar[j];
+    if (LO) *reinterpret_cast<uint4*>(&As[0][NA - 1][a_lds[j]]) = al[j];
+  }
+  __syncthreads();
+  const int Kp = (Kg + PB - 1) / PB * PB;
+  for (int g0 = 0; g0 < Kp; g0 += PB) {
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      const int g = g0 + q;
+      const int cur = q & 1;             // g0 is even, so this is g & 1
+      const int gn = min(g + 1, Kg - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ar[j] = *reinterpret_cast<const uint4*>(asrc + a_off[j] + gn * 64);
+        if (LO) al[j] = *reinterpret_cast<const uint4*>(a.x16lo + a_off[j] + gn * 64);
+      }
+      if (won && g < Kg) {
+        f16x8 bf[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const uint32_t sv = bs[q][nb] & 0xffffu, bv = bs[q][nb] >> 16;
+          const f16x2 s2 = __builtin_bit_cast(f16x2, sv | (sv << 16));
+          const f16x2 b2 = __builtin_bit_cast(f16x2, bv | (bv << 16));
+          bf[nb][0] = dequant8(L, bc[q][nb].x, s2, b2);
+          bf[nb][1] = dequant8(L, bc[q][nb].y, s2, b2);
+          bf[nb][2] = dequant8(L, bc[q][nb].z, s2, b2);
+          bf[nb][3] = dequant8(L, bc[q][nb].w, s2, b2);
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          if (mb < nmb) {
+#pragma unroll
+            for (int qa = 0; qa < NA; ++qa) {
+              const uint16_t* arow = &As[cur][qa][(mb * 32 + l32) * kALdsRow + hi * 32];
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks) {
+                const f16x8 af = *reinterpret_cast<const f16x8*>(arow + ks * 8);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                  acc[mb][nb] =
+                      __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nb][ks], acc[mb][nb], 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+      {
+        const int gr = min(g + PB, Kg - 1);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const uint8_t* t = bb[nb] + (size_t)gr * kQ4TileBytes;
+          bc[q][nb] = ld16(t + hi * 1024 + brow[nb] * 16);
+          bs[q][nb] = ld4(t + kQ4CodeBytes + brow[nb] * 4);
+        }
+      }
+      if (g + 1 < Kg) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          *reinterpret_cast<uint4*>(&As[cur ^ 1][0][a_lds[j]]) = ar[j];
+          if (LO) *reinterpret_cast<uint4*>(&As[cur ^ 1][NA - 1][a_lds[j]]) = al[j];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!won) return;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if (mb < nmb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int row = mb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+        if (row < mrows) {
+          const int slot = s_slot[row];
+          if (UP) {
+            const float gv = acc[mb][0][j], uv = acc[mb][1][j];
+            const float hv = gv / (1.f + expf(-gv)) * uv;
+            const int col = n0 + l32;
+            a.hdst[h_off(slot, Tk, a.I, a.Is) + pair_pos4(col)] = f16bits((_Float16)hv);
+          } else {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              a.yslot[(size_t)slot * a.H + n0 + nb * 32 + l32] = acc[mb][nb][j];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Narrow matrix-core kernel, for experts with a few tens of rows: one
+// workgroup = one 32-row tile x 32 gate+up columns (or 64 down columns); the
+// 4 waves split the K groups, so each wave streams a quarter of the weights
+// with a PN-deep register ring for both operands (A straight from global, no
+// LDS, no barriers in the loop) and the partial accumulators are summed across
+// waves in fixed order at the end.
+template <bool UP, bool LO>
+__global__ __launch_bounds__(256) void mfma_narrow_kernel(MfmaArgs a) {
+  constexpr int PN = 4;
+  constexpr int NA = LO ? 2 : 1;
+  __shared__ float red[kMfmaWaves][2][16][64];
+  __shared__ int s_slot[32];
+  const int tile_i = blockIdx.y;
+  if (tile_i >= a.misc[kNNarrow]) return;
+  const int2 tl = a.ntiles[tile_i];
+  const int4 it = a.mitems[tl.x];
+  const int e = it.x, m_tot = it.y, loff = it.z, m0 = tl.y;
+  const int mrows = min(32, m_tot - m0);
+  const bool sh = e == a.E;
+  const int inter = sh ? a.Is : a.I;
+  const int G = a.H >> 6;
+  const int Kg = UP ? G : inter >> 6;
+  constexpr int CB = UP ? 32 : 64;
+  const int ncols = UP ? inter : a.H;
+  const int n0 = blockIdx.x * CB;
+  if (n0 >= ncols) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int Tk = a.T * a.k;
+  if (tid < 32) s_slot[tid] = a.slots[loff + m0 + (tid < mrows ? tid : 0)];
+  __syncthreads();
+  // this lane's A row (row l32 of the tile; rows past the tile repeat row 0)
+  const int slot = s_slot[l32];
+  const size_t a_row = UP ? (size_t)(slot < Tk ? slot / a.k : slot - Tk) * a.H
+                          : h_off(slot, Tk, a.I, a.Is);
+  const uint16_t* asrc = (UP ? a.x16 : a.hsrc) + a_row + hi * 32;
+  const uint16_t* asrc_lo = a.x16lo + a_row + hi * 32;
+  const uint8_t* rec = sh ? a.shared : a.bank + (size_t)e * a.stride;
+  const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
+  const uint8_t* bb[2];
+  int brow[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = UP ? n0 : n0 + nb * 32;
+    const uint8_t* mat = rec + kHeaderBytes + (UP ? (nb ? sec : 0) : 2 * sec);
+    bb[nb] = mat + (size_t)(r >> 6) * Kg * kQ4TileBytes;
+    brow[nb] = (r & 63) + l32;
+  }
+  const int gbeg = (Kg * wave) / kMfmaWaves, gend = (Kg * (wave + 1)) / kMfmaWaves;
+  f32x16 acc[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[nb][j] = 0.f;
+  if (gbeg < gend) {
+    uint4 ra[PN][NA][4];      // A: the lane's 64 bytes of a group (4 k-steps)
+    uint4 rb[PN][2];
+    uint32_t rs[PN][2];
+#define QREB_NARROW_LOAD(q, g)                                                         \
+  do {                                                                                 \
+    _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                 \
+      ra[q][0][ks] = *reinterpret_cast<const uint4*>(asrc + (g) * 64 + ks * 8);       \
+      if (LO) ra[q][NA - 1][ks] = *reinterpret_cast<const uint4*>(asrc_lo + (g) * 64 + ks * 8); \
+    }                                                                                  \
+    _Pragma("unroll") for (int nb = 0; nb < 2; ++nb) {                                 \
+      const uint8_t* t_ = bb[nb] + (size_t)(g) * kQ4TileBytes;                         \
+      rb[q][nb] = ld16(t_ + hi * 1024 + brow[nb] * 16);                                \
+      rs[q][nb] = ld4(t_ + kQ4CodeBytes + brow[nb] * 4);                               \
+    }                                                                                  \
+  } while (0)
+#pragma unroll
+    for (int q = 0; q < PN; ++q) QREB_NARROW_LOAD(q, min(gbeg + q, gend - 1));
+    const Lift L;
+    for (int g0 = gbeg; g0 < gend; g0 += PN) {
+#pragma unroll
+      for (int q = 0; q < PN; ++q) {
+        const int g = g0 + q;
+        f16x8 bf[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const uint32_t sv = rs[q][nb] & 0xffffu, bv = rs[q][nb] >> 16;
+          const f16x2 s2 = __builtin_bit_cast(f16x2, sv | (sv << 16));
+          const f16x2 b2 = __builtin_bit_cast(f16x2, bv | (bv << 16));
+          bf[nb][0] = dequant8(L, rb[q][nb].x, s2, b2);
+          bf[nb][1] = dequant8(L, rb[q][nb].y, s2, b2);
+          bf[nb][2] = dequant8(L, rb[q][nb].z, s2, b2);
+          bf[nb][3] = dequant8(L, rb[q][nb].w, s2, b2);
+        }
+        f16x8 af[NA][4];
+#pragma unroll
+        for (int qa = 0; qa < NA; ++qa)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) af[qa][ks] = __builtin_bit_cast(f16x8, ra[q][qa][ks]);
+        QREB_NARROW_LOAD(q, min(g + PN, gend - 1));
+        if (g < gend) {
+#pragma unroll
+          for (int qa = 0; qa < NA; ++qa)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[qa][ks], bf[nb][ks], acc[nb], 0, 0, 0);
+        }
+      }
+    }
+#undef QREB_NARROW_LOAD
+  }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) red[wave][nb][j][lane] = acc[nb][j];
+  __syncthreads();
+  // wave w finishes rows j in {4w .. 4w+3} of each lane's 16 (fixed-order sum over waves)
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = wave * 4 + jj;
+    const int row = 8 * (j >> 2) + 4 * hi + (j & 3);
+    float v[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      v[nb] = 0.f;
+#pragma unroll
+      for (int w = 0; w < kMfmaWaves; ++w) v[nb] += red[w][nb][j][lane];
+    }
+    if (row < mrows) {
+      const int sl = s_slot[row];
+      if (UP) {
+        const float hv = v[0] / (1.f + expf(-v[0])) * v[1];
+        a.hdst[h_off(sl, Tk, a.I, a.Is) + pair_pos4(n0 + l32)] = f16bits((_Float16)hv);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) a.yslot[(size_t)sl * a.H + n0 + nb * 32 + l32] = v[nb];
+      }
+    }
   }
 }
 
@@ -614,7 +1153,18 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, int T, int h
   if (c >= H) return;
   const int Tk = T * k;
   float acc = 0.f;
-  for (int j = 0; j < k; ++j) acc = fmaf(p[t * k + j], yslot[(size_t)(t * k + j) * H + c], acc);
+  for (int j0 = 0; j0 < k; j0 += 8) {        // loads issued in batches of 8
+    float pv[8], yv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool on = j0 + j < k;
+      pv[j] = on ? p[t * k + j0 + j] : 0.f;
+      yv[j] = on ? yslot[(size_t)(t * k + j0 + j) * H + c] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j0 + j < k) acc = fmaf(pv[j], yv[j], acc);     // fixed order: j ascending
+  }
   if (has_shared) acc += yslot[(size_t)(Tk + t) * H + c];
   y[(size_t)t * H + c] = acc;
 }
@@ -683,7 +1233,7 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   a.Epad = d.Epad;
   a.k = d.k;
   a.KS = router_ksplit(d.H);
-  a.TBR = router_tok_block(T);
+  a.TBR = router_tok_block(T, d.Epad);
   a.n_tb = (T + a.TBR - 1) / a.TBR;
   a.n_rb = d.Epad / kTileRows;
   a.mode = mode;
@@ -692,10 +1242,7 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   a.x16 = reinterpret_cast<uint16_t*>(wsp(d, d.L.x16));
   a.x16lo = reinterpret_cast<uint16_t*>(wsp(d, d.L.x16lo));
   a.xs = reinterpret_cast<float*>(wsp(d, d.L.xs));
-  a.cnt_tb = reinterpret_cast<int*>(wsp(d, d.L.cnt_tb));
   a.misc = reinterpret_cast<int*>(wsp(d, d.L.misc));
-  a.counts = reinterpret_cast<int*>(wsp(d, d.L.counts));
-  a.rank = reinterpret_cast<int*>(wsp(d, d.L.rank));
   a.ids_ws = reinterpret_cast<int*>(wsp(d, d.L.ids));
   a.p_ws = reinterpret_cast<float*>(wsp(d, d.L.p));
   a.ids_out = ids_out;
@@ -707,34 +1254,175 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   a.items = reinterpret_cast<int4*>(wsp(d, d.L.items));
   a.mitems = reinterpret_cast<int4*>(wsp(d, d.L.mitems));
   a.mtiles = reinterpret_cast<int2*>(wsp(d, d.L.mtiles));
+  a.ntiles = reinterpret_cast<int2*>(wsp(d, d.L.ntiles));
   a.mfma_min_rows = d.mfma_min_rows;
+  a.wide_min_rows = d.wide_min_rows;
   a.has_shared = d.has_shared;
-  dim3 grid(a.n_rb, a.KS, a.n_tb);
-  hipLaunchKernelGGL(router_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(router_gemv_kernel, dim3(a.n_rb, a.KS, a.n_tb), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int tpw = 512 / d.Epad;
+  if (tpw < 1) tpw = 1;
+  if (tpw > kRouterTokMax) tpw = kRouterTokMax;
+  hipLaunchKernelGGL(router_topk_kernel, dim3((T + tpw - 1) / tpw), dim3(256), 0, s, a, tpw);
+  e = hipGetLastError();
+  if (e != hipSuccess || mode != 0) return e;
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_experts(const LayerDev& d, int x_f32, int T, hipStream_t s) {
-  const int Tk = T * d.k;
-  const int ni = (Tk < d.E ? Tk : d.E) + (d.has_shared ? 1 : 0);
+struct ExpertPtrs {
+  const uint32_t* x16;
+  const uint32_t* x16lo;
+  const float* xs;
+  const int4* items;
+  const int* misc;
+  const int* slots;
+  uint16_t* hbuf;
+  float* hs;
+  float* yslot;
+  int ni;
+};
+
+// Token rows per streaming pass: at most kGemvTokV2, never more than T, and
+// few enough that the staged rows fit 64 KB of LDS.
+static int gemv_tokens_per_pass(const LayerDev& d, int T) {
   const int imax = d.Is > d.I ? d.Is : d.I;
-  const uint32_t* x16 = reinterpret_cast<const uint32_t*>(wsp(d, d.L.x16));
-  const uint32_t* x16lo = reinterpret_cast<const uint32_t*>(wsp(d, d.L.x16lo));
-  const float* xs = reinterpret_cast<const float*>(wsp(d, d.L.xs));
-  const int4* items = reinterpret_cast<const int4*>(wsp(d, d.L.items));
-  const int* misc = reinterpret_cast<const int*>(wsp(d, d.L.misc));
-  const int* slots = reinterpret_cast<const int*>(wsp(d, d.L.slots));
-  uint16_t* hbuf = reinterpret_cast<uint16_t*>(wsp(d, d.L.hbuf));
-  float* hs = reinterpret_cast<float*>(wsp(d, d.L.hs));
-  float* yslot = reinterpret_cast<float*>(wsp(d, d.L.yslot));
-  hipLaunchKernelGGL(gemv_up_kernel, dim3(imax / 64, ni), dim3(256), 0, s, d.bank, d.stride,
-                     d.shared, d.H, d.E, d.k, d.I, d.Is, T, x_f32, x16, x16lo, xs, items, misc,
-                     slots, hbuf, hs);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gemv_down_kernel, dim3(d.H / 64, ni), dim3(256), 0, s, d.bank, d.stride,
-                     d.shared, d.H, d.E, d.k, d.I, d.Is, T, items, misc, slots,
-                     reinterpret_cast<const uint32_t*>(hbuf), hs, yslot);
+  const int row_bytes = (d.H > imax ? d.H : imax) * 4;   // fp32 input: hi + lo halves
+  int mt = kGemvTokV2;
+  while (mt > 1 && mt * row_bytes > 56 * 1024) --mt;
+  return T < mt ? T : mt;
+}
+
+static ExpertPtrs expert_ptrs(const LayerDev& d, int T) {
+  ExpertPtrs p;
+  const int Tk = T * d.k;
+  p.ni = (Tk < d.E ? Tk : d.E) + (d.has_shared ? 1 : 0);
+  p.x16 = reinterpret_cast<const uint32_t*>(wsp(d, d.L.x16));
+  p.x16lo = reinterpret_cast<const uint32_t*>(wsp(d, d.L.x16lo));
+  p.xs = reinterpret_cast<const float*>(wsp(d, d.L.xs));
+  p.items = reinterpret_cast<const int4*>(wsp(d, d.L.items));
+  p.misc = reinterpret_cast<const int*>(wsp(d, d.L.misc));
+  p.slots = reinterpret_cast<const int*>(wsp(d, d.L.slots));
+  p.hbuf = reinterpret_cast<uint16_t*>(wsp(d, d.L.hbuf));
+  p.hs = reinterpret_cast<float*>(wsp(d, d.L.hs));
+  p.yslot = reinterpret_cast<float*>(wsp(d, d.L.yslot));
+  return p;
+}
+
+hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
+  const ExpertPtrs p = expert_ptrs(d, T);
+  const int imax = d.Is > d.I ? d.Is : d.I;
+  const int mt = gemv_tokens_per_pass(d, T);
+  const size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + d.H / 64) * 4;
+  if (x_f32)
+    hipLaunchKernelGGL((gemv_up_kernel<true>), dim3(imax / 64, p.ni), dim3(256), lds, s, d.bank,
+                       d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs,
+                       p.items, p.misc, p.slots, p.hbuf, p.hs, mt);
+  else
+    hipLaunchKernelGGL((gemv_up_kernel<false>), dim3(imax / 64, p.ni), dim3(256), lds, s, d.bank,
+                       d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs,
+                       p.items, p.misc, p.slots, p.hbuf, p.hs, mt);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
+  const ExpertPtrs p = expert_ptrs(d, T);
+  const int mt = gemv_tokens_per_pass(d, T);
+  const int imax = d.Is > d.I ? d.Is : d.I;
+  const size_t lds = (size_t)mt * (imax / 2 + imax / 64) * 4;
+  hipLaunchKernelGGL(gemv_down_kernel, dim3(d.H / 64, p.ni), dim3(256), lds, s, d.bank, d.stride,
+                     d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.items, p.misc, p.slots,
+                     reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, mt);
+  return hipGetLastError();
+}
+
+// Upper bounds of matrix-core row tiles in one forward (the exact counts are
+// in misc[kNTiles] / misc[kNNarrow]): an item with r rows adds ceil(r / BM).
+static int tiles_max(const LayerDev& d, int T, int lo, int hi, int bm) {
+  const int Tk = T * d.k;
+  if (T < lo) return 0;                     // no expert (nor the shared one) reaches lo rows
+  int items = Tk / lo;
+  if (items > d.E) items = d.E;
+  int n = (Tk + bm - 1) / bm + items;
+  if (d.has_shared) n += (T + bm - 1) / bm + 1;
+  (void)hi;
+  return n;
+}
+static int mfma_tiles_max(const LayerDev& d, int T) {
+  return tiles_max(d, T, d.wide_min_rows, 0, kMfmaBM);
+}
+static int narrow_tiles_max(const LayerDev& d, int T) {
+  return tiles_max(d, T, d.mfma_min_rows, d.wide_min_rows, kNarrowBM);
+}
+
+static MfmaArgs mfma_args(const LayerDev& d, int T) {
+  MfmaArgs m;
+  m.bank = d.bank;
+  m.stride = d.stride;
+  m.shared = d.shared;
+  m.H = d.H;
+  m.E = d.E;
+  m.k = d.k;
+  m.I = d.I;
+  m.Is = d.Is;
+  m.T = T;
+  m.x16 = reinterpret_cast<const uint16_t*>(wsp(d, d.L.x16));
+  m.x16lo = reinterpret_cast<const uint16_t*>(wsp(d, d.L.x16lo));
+  m.hsrc = reinterpret_cast<const uint16_t*>(wsp(d, d.L.hbuf));
+  m.hdst = reinterpret_cast<uint16_t*>(wsp(d, d.L.hbuf));
+  m.mitems = reinterpret_cast<const int4*>(wsp(d, d.L.mitems));
+  m.mtiles = reinterpret_cast<const int2*>(wsp(d, d.L.mtiles));
+  m.ntiles = reinterpret_cast<const int2*>(wsp(d, d.L.ntiles));
+  m.misc = reinterpret_cast<const int*>(wsp(d, d.L.misc));
+  m.slots = reinterpret_cast<const int*>(wsp(d, d.L.slots));
+  m.yslot = reinterpret_cast<float*>(wsp(d, d.L.yslot));
+  return m;
+}
+
+bool mfma_needed(const LayerDev& d, int T) { return mfma_tiles_max(d, T) > 0; }
+bool narrow_needed(const LayerDev& d, int T) { return narrow_tiles_max(d, T) > 0; }
+
+hipError_t launch_narrow_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
+  const int nt = narrow_tiles_max(d, T);
+  if (nt == 0) return hipSuccess;
+  const int imax = d.Is > d.I ? d.Is : d.I;
+  const MfmaArgs m = mfma_args(d, T);
+  const dim3 grid(imax / 32, nt);
+  if (x_f32)
+    hipLaunchKernelGGL((mfma_narrow_kernel<true, true>), grid, dim3(256), 0, s, m);
+  else
+    hipLaunchKernelGGL((mfma_narrow_kernel<true, false>), grid, dim3(256), 0, s, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_narrow_down(const LayerDev& d, int T, hipStream_t s) {
+  const int nt = narrow_tiles_max(d, T);
+  if (nt == 0) return hipSuccess;
+  const MfmaArgs m = mfma_args(d, T);
+  hipLaunchKernelGGL((mfma_narrow_kernel<false, false>), dim3(d.H / 64, nt), dim3(256), 0, s, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
+  const int nt = mfma_tiles_max(d, T);
+  if (nt == 0) return hipSuccess;
+  const int imax = d.Is > d.I ? d.Is : d.I;
+  const MfmaArgs m = mfma_args(d, T);
+  const dim3 grid((imax + 127) / 128, nt);
+  if (x_f32)
+    hipLaunchKernelGGL((mfma_expert_kernel<true, true>), grid, dim3(256), 0, s, m);
+  else
+    hipLaunchKernelGGL((mfma_expert_kernel<true, false>), grid, dim3(256), 0, s, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s) {
+  const int nt = mfma_tiles_max(d, T);
+  if (nt == 0) return hipSuccess;
+  const MfmaArgs m = mfma_args(d, T);
+  hipLaunchKernelGGL((mfma_expert_kernel<false, false>), dim3((d.H + 255) / 256, nt), dim3(256), 0,
+                     s, m);
   return hipGetLastError();
 }
 

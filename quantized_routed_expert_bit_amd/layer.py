@@ -39,6 +39,7 @@ class MoELayer:
         if rc != 0:
             raise MoEError(rc, f"moe_open: {self.lib.moe_strerror(rc).decode()}")
         self.workspace_bytes = int(self.lib.moe_workspace_bytes(ctypes.byref(self.cfg)))
+        self.mfma_min_rows, self.wide_min_rows = 4, 64      # the library's defaults
         self._keep = ()
 
     def _check(self, rc, what):
@@ -90,8 +91,24 @@ class MoELayer:
                                                _stream()), "moe_router_logits")
         return out
 
-    def set_mfma_min_rows(self, n):
-        self._check(self.lib.moe_set_mfma_min_rows(self.ctx, n), "moe_set_mfma_min_rows")
+    def profile_start(self, max_calls):
+        self._check(self.lib.moe_profile_start(self.ctx, max_calls), "moe_profile_start")
+
+    def profile_read(self):
+        """-> ({slot name: average ms per launch}, number of profiled forwards)."""
+        n = len(L.PROFILE_SLOTS)
+        arr = (ctypes.c_float * n)()
+        calls = ctypes.c_int32()
+        self._check(self.lib.moe_profile_read(self.ctx, arr, ctypes.byref(calls), n),
+                    "moe_profile_read")
+        return dict(zip(L.PROFILE_SLOTS, list(arr))), calls.value
+
+    def set_path_rows(self, mfma_min_rows, wide_min_rows=None):
+        if wide_min_rows is None:
+            wide_min_rows = max(mfma_min_rows, self.wide_min_rows)
+        self._check(self.lib.moe_set_path_rows(self.ctx, mfma_min_rows, wide_min_rows),
+                    "moe_set_path_rows")
+        self.mfma_min_rows, self.wide_min_rows = mfma_min_rows, wide_min_rows
 
     def close(self):
         if self.ctx:

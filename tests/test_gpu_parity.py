@@ -17,14 +17,14 @@ def torch_dev():
     return torch.device("cuda", 0)
 
 
-def _layer(li, dev, max_tokens, mfma_min_rows=None):
+def _layer(li, dev, max_tokens, mfma_min_rows=None, wide_min_rows=None):
     from quantized_routed_expert_bit_amd import MoELayer
     sh = li.shape
     w = P.upload_layer(li, dev)
     m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, max_tokens)
     m.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
     if mfma_min_rows is not None:
-        m.set_mfma_min_rows(mfma_min_rows)
+        m.set_path_rows(mfma_min_rows, wide_min_rows)
     m._w = w
     return m
 
@@ -158,3 +158,67 @@ def test_error_paths(torch_dev):
     with pytest.raises(MoEError) as ei:
         m.set_weights(w["router"], w["bank"], w["stride"], shared=w["bank"][:4096])
     assert ei.value.code == -1                                     # shared without the flag
+
+
+@pytest.mark.parametrize("cfg,min_rows,wide_rows", [(0, 1, 1), (1, 1, 1), (0, 1, 64), (1, 1, 64),
+                                                    (1, 4, 64), (1, 2, 8)])
+def test_layer_parity_matrix_core(torch_dev, cfg, min_rows, wide_rows):
+    """Experts with >= min_rows rows take the matrix-core path (1: every
+    expert), in 128-row tiles from wide_rows rows on, else in 32-row tiles."""
+    wl = synth.WORKLOADS[cfg]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, 16, mfma_min_rows=min_rows, wide_min_rows=wide_rows)
+    ol = P.oracle_layer(li)
+    for T in (1, 5, 16):
+        P.log(f"cfg{cfg} min_rows={min_rows} T={T}")
+        xb = synth.make_hidden(0, cfg, T, wl.shape.hidden, tag=7)
+        y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+        P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                        p.cpu().numpy(), f"cfg{cfg} mfma>={min_rows} T={T}")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(H=320, E=65, k=3, I=192, Is=0, T=200),      # partial 128-column blocks, ragged tiles
+    dict(H=192, E=8, k=2, I=64, Is=320, T=300),      # >128 rows per expert: several row tiles
+])
+def test_matrix_core_edge_shapes(torch_dev, shape):
+    H, E, k, I, Is, T = (shape[n] for n in ("H", "E", "k", "I", "Is", "T"))
+    P.log(f"mfma edge shape {shape}")
+    li = synth.LayerInputs(13, 91, 0, synth.LayerShape(H, E, k, I, Is), "normal0.5")
+    ol = P.oracle_layer(li)
+    xb = synth.make_hidden(13, 91, T, H)
+    for wide in (2, 40):
+        m = _layer(li, torch_dev, T, mfma_min_rows=2, wide_min_rows=wide)
+        y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+        P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                        p.cpu().numpy(), f"mfma edge wide>={wide}")
+    m = _layer(li, torch_dev, T, mfma_min_rows=2)
+    y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+    P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                    p.cpu().numpy(), "mfma edge")
+
+
+def test_matrix_core_fp32_input(torch_dev):
+    import torch
+    li = synth.layer_inputs(synth.WORKLOADS[0])
+    ol = P.oracle_layer(li)
+    x32 = (np.random.default_rng(6).standard_normal((64, 512)) * 1.3).astype(np.float32)
+    for wide in (1, 64):
+        m = _layer(li, torch_dev, 64, mfma_min_rows=1, wide_min_rows=wide)
+        y, ids, p = m.forward(torch.from_numpy(x32).to(torch_dev), return_selection=True)
+        P.check_forward(ol, x32.astype(np.float64), y.cpu().numpy(), ids.cpu().numpy(),
+                        p.cpu().numpy(), f"mfma fp32 input wide>={wide}")
+
+
+def test_prefill_2048_tokens(torch_dev):
+    """The prefill workload: 16 chunks of 128 tokens in one forward, router
+    logit bias N(0, 0.5) (skewed expert load), default path split."""
+    wl = synth.WORKLOADS[2]
+    li = synth.layer_inputs(wl)
+    T = wl.batches[0]
+    m = _layer(li, torch_dev, T)
+    ol = P.oracle_layer(li)
+    xb = synth.make_hidden(0, 2, T, wl.shape.hidden)
+    y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+    P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                    p.cpu().numpy(), "prefill T=2048")
