@@ -117,6 +117,51 @@ def run_case(layers, sh, T, steps, warmup, tag=0):
                 eager_ms_per_step=eager_ms)
 
 
+def path_flops(ids, sh, T, rmin, rwide):
+    """FLOPs of the expert FFNs on each path, from the actual routing."""
+    cnt = np.bincount(ids.reshape(-1), minlength=sh.n_experts)
+    per_row = 2 * 3 * sh.hidden * sh.inter
+    out = {"stream": 0.0, "narrow": 0.0, "wide": 0.0}
+    for c in cnt[cnt > 0]:
+        out["stream" if c < rmin else ("narrow" if c < rwide else "wide")] += c * per_row
+    if sh.has_shared:
+        out["stream" if T < rmin else ("narrow" if T < rwide else "wide")] += \
+            T * 2 * 3 * sh.hidden * sh.shared_inter
+    return out, cnt
+
+
+def run_prefill(args, dev):
+    """The prefill workload: 16 chunks of 128 tokens (2048) per forward, router
+    logit bias N(0, 0.5); bound by the matrix cores."""
+    import torch
+    import synth
+    from tests.parity import bf16_tensor
+    wl, layers = build_layers(2, 2, 2048, dev)
+    sh = wl.shape
+    T = wl.batches[0]
+    r = run_case(layers, sh, T, max(4, args.steps // 20), 2, tag=50)
+    _, ids, _ = layers[0].forward(bf16_tensor(synth.make_hidden(0, 2, T, sh.hidden, tag=150), dev),
+                                  return_selection=True)
+    fl, cnt = path_flops(ids.cpu().numpy(), sh, T, layers[0].mfma_min_rows, layers[0].wide_min_rows)
+    k = r["kern_ms"]
+    wide_ms = k["mfma_up"] + k["mfma_down"]
+    total_flops = T * 2 * (sh.top_k * 3 * sh.hidden * sh.inter + 3 * sh.hidden * sh.shared_inter
+                           + sh.n_experts * sh.hidden)
+    res = {"tokens_s": round(r["tok_s"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2),
+           "layer_TFLOP_s": round(total_flops / (r["ms_per_step"] * 1e-3) / 1e12, 1),
+           "layer_frac_mfma_peak": round(total_flops / (r["ms_per_step"] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFS, 4),
+           "wide_mfma_TFLOP_s": round(fl["wide"] / (wide_ms * 1e-3) / 1e12, 1) if wide_ms else None,
+           "wide_frac_mfma_peak": round(fl["wide"] / (wide_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFS, 4) if wide_ms else None,
+           "path_gflop": {kk: round(v / 1e9, 2) for kk, v in fl.items()},
+           "rows_per_expert": {"min": int(cnt.min()), "median": float(np.median(cnt)), "max": int(cnt.max())},
+           "kernel_us": {kk: round(v * 1e3, 3) for kk, v in k.items()},
+           "distinct_experts": r["distinct"]}
+    log(f"prefill: {res}")
+    for m in layers:
+        m.close()
+    return res
+
+
 def cpu_baseline(layer0, sh, T):
     """The oracle (fp64 NumPy) on one forward of the same workload."""
     import oracle
@@ -151,6 +196,7 @@ def main():
     ap.add_argument("--copies", type=int, default=6, help="layer copies the steps rotate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the T=1 and T=4 lines")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -221,6 +267,12 @@ def main():
         out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers[0], sh, T)
+    if not args.no_prefill:
+        for m in layers:
+            m.close()
+        del layers
+        torch.cuda.empty_cache()
+        out["prefill"] = run_prefill(args, dev)
     print(json.dumps(out), flush=True)
 
 

@@ -96,7 +96,9 @@ extern "C" {
 #define MOE_BF16 1              /* x dtype: bf16 [T, H]                           */
 #define MOE_F32  2              /* x dtype: fp32 [T, H] (e.g. a residual stream)  */
 
-#define MOE_F_SHARED 1u         /* config flag: an always-on shared expert exists */
+#define MOE_F_SHARED  1u        /* config flag: an always-on shared expert exists */
+#define MOE_F_RMSNORM 2u        /* config flag: the layer runs on x / sqrt(mean(x^2) + 1e-6),
+                                   per token (a parameter-free pre-norm, for residual stacks) */
 
 #define MOE_ABI_VERSION 1
 
@@ -113,7 +115,7 @@ typedef struct moe_config {
     int32_t  group;         /* must be 64 */
     int32_t  max_tokens;    /* largest T a forward may pass, 1..65536 */
     int32_t  device;        /* HIP device ordinal the context runs on */
-    uint32_t flags;         /* MOE_F_SHARED */
+    uint32_t flags;         /* MOE_F_SHARED | MOE_F_RMSNORM */
 } moe_config;
 
 /* Weights and workspace, all device pointers (borrowed). */
@@ -146,15 +148,20 @@ int moe_open(const moe_config *cfg, moe_ctx **out);
 int moe_set_weights(moe_ctx *ctx, const moe_weights *w, void *stream);
 
 /* Run the layer on T = n_tokens rows of x (x_dtype MOE_BF16 or MOE_F32,
- * row-major [T, H]).  Writes y (fp32 [T, H]); ids_out (int32 [T, k]) and p_out
+ * row-major [T, H]).  Writes y (fp32 [T, H]) = layer(x), or residual +
+ * layer(x) when residual (fp32 [T, H]) is non-NULL -- the residual stream
+ * update r_{l+1} = r_l + y_l of a stack of layers (with MOE_F_RMSNORM the layer
+ * sees the normalized x, the residual add does not); y may alias residual (an
+ * in-place update), and with fp32 x also x.  ids_out (int32 [T, k]) and p_out
  * (fp32 [T, k]) receive the selection when non-NULL.  If lookahead_next is a
- * context of the same shape with weights bound, its router also runs on this
- * x and its next forward orders expert work by that prediction; the selected
- * experts and every output are unchanged by it.  T = 0 is a no-op.  Errors:
- * MOE_EINVAL (null x/y, T < 0 or > max_tokens, bad dtype, mismatched
- * lookahead context), MOE_ESTATE (no weights), MOE_EHIP (launch failure). */
+ * context of the same hidden size and flags with weights bound, its router also
+ * runs on this x ("one residual ahead") and its next forward orders expert work by
+ * that prediction; the selected experts and every output are unchanged by it.
+ * T = 0 is a no-op.  Errors: MOE_EINVAL (null x/y, T < 0 or > max_tokens, bad
+ * dtype, mismatched lookahead context), MOE_ESTATE (no weights), MOE_EHIP
+ * (launch failure). */
 int moe_forward(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
-                float *y, int32_t *ids_out, float *p_out,
+                float *y, const float *residual, int32_t *ids_out, float *p_out,
                 moe_ctx *lookahead_next, void *stream);
 
 /* Router step only: logits fp32 [T, E] (including router_bias).  Same

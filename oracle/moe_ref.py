@@ -33,7 +33,7 @@ import numpy as np
 __all__ = [
     "f16_bits_to_f64", "bf16_bits_to_f64", "read_record_header", "dequant_tiled",
     "expert_matrices", "router_matrix", "router_logits", "select_topk",
-    "softmax_selected", "silu", "expert_ffn", "OracleLayer", "oracle_stack",
+    "softmax_selected", "silu", "expert_ffn", "OracleLayer", "oracle_stack", "rms_normalize",
 ]
 
 _GROUP = 64
@@ -86,10 +86,10 @@ def dequant_tiled(buf, offset: int, rows: int, cols: int, bits: int) -> np.ndarr
     else:
         raise ValueError("bits must be 4 or 8")
     sb = np.ascontiguousarray(t[:, :, code_bytes:]).view(np.uint16).reshape(n_rb, n_g, _ROWS, 2)
-    s = f16_bits_to_f64(sb[..., 0]).transpose(0, 2, 1).reshape(rows, n_g)   # [row, g]
-    b = f16_bits_to_f64(sb[..., 1]).transpose(0, 2, 1).reshape(rows, n_g)
-    g_of_col = np.arange(cols) // _GROUP
-    return s[:, g_of_col] * q.astype(np.float64) + b[:, g_of_col]
+    s = f16_bits_to_f64(sb[..., 0]).transpose(0, 2, 1).reshape(rows, n_g, 1)   # [row, g, 1]
+    b = f16_bits_to_f64(sb[..., 1]).transpose(0, 2, 1).reshape(rows, n_g, 1)
+    w = q.reshape(rows, n_g, _GROUP) * s + b          # column c = g*64 + (c % 64)
+    return w.reshape(rows, cols)
 
 
 def expert_matrices(rec, hidden: int, inter: int):
@@ -194,17 +194,26 @@ class OracleLayer:
         return dict(y=y, ids=ids, p=p, gap=gap, logits=lg)
 
 
-def oracle_stack(layers, x0: np.ndarray, lookahead_k: int | None = None) -> dict:
-    """r_0 = x0; y_l = layer_l(r_l); r_{l+1} = r_l + y_l.  With lookahead_k, also
-    the next layer's router on r_l (its top-lookahead_k ids), for reporting only:
-    it never feeds back into the result."""
+def rms_normalize(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) per row (a parameter-free RMS norm)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+
+
+def oracle_stack(layers, x0: np.ndarray, lookahead_k: int | None = None,
+                 norm: bool = False) -> dict:
+    """r_0 = x0; y_l = layer_l(n(r_l)); r_{l+1} = r_l + y_l, with n the RMS norm
+    when ``norm`` (else the identity).  With lookahead_k, also the next layer's
+    router on n(r_l) (its top-lookahead_k ids), for reporting only: it never
+    feeds back into the result."""
     r = np.asarray(x0, dtype=np.float64)
     per_layer = []
     for li, layer in enumerate(layers):
-        res = layer.forward(r)
+        xin = rms_normalize(r) if norm else r
+        res = layer.forward(xin)
         res["input"] = r
         if lookahead_k is not None and li + 1 < len(layers):
-            pred, _ = select_topk(layers[li + 1].logits(r), lookahead_k)
+            pred, _ = select_topk(layers[li + 1].logits(xin), lookahead_k)
             res["lookahead_ids"] = pred
         per_layer.append(res)
         r = r + res["y"]

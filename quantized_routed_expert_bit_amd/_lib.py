@@ -12,6 +12,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EBADRECORD, MOE_ESTATE, MO
     0, -1, -2, -3, -4, -5, -6
 MOE_BF16, MOE_F32 = 1, 2
 MOE_F_SHARED = 1
+MOE_F_RMSNORM = 2
 
 # every function include/moe.h declares
 EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
@@ -55,7 +56,7 @@ def load() -> ctypes.CDLL:
     lib.moe_set_weights.argtypes = [c_void_p, P(MoeWeights), c_void_p]
     lib.moe_set_weights.restype = c_int
     lib.moe_forward.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
-                                c_void_p, c_void_p, c_void_p]
+                                c_void_p, c_void_p, c_void_p, c_void_p]
     lib.moe_forward.restype = c_int
     lib.moe_router_logits.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]
     lib.moe_router_logits.restype = c_int
@@ -79,7 +80,8 @@ def load() -> ctypes.CDLL:
     return lib
 
 
-def make_config(hidden, n_experts, top_k, inter, shared_inter=0, max_tokens=1, device=0):
+def make_config(hidden, n_experts, top_k, inter, shared_inter=0, max_tokens=1, device=0,
+                rmsnorm=False):
     return MoeConfig(ctypes.sizeof(MoeConfig), hidden, n_experts, top_k, inter,
                      shared_inter, 64, max_tokens, device,
-                     MOE_F_SHARED if shared_inter else 0)
+                     (MOE_F_SHARED if shared_inter else 0) | (MOE_F_RMSNORM if rmsnorm else 0))

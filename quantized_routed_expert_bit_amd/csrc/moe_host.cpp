@@ -88,6 +88,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.hbuf = take((Tk * I + Ts * Is) * 2);
   L.hs = take((Tk * (I / 64) + Ts * (Is / 64)) * 4);
   L.yslot = take((Tk + Ts) * H * 4);
+  L.xn = take((c.flags & MOE_F_RMSNORM) ? T * H * 4 : 0);
   L.total = o;
   return L;
 }
@@ -102,7 +103,7 @@ static int check_config(const moe_config* c) {
   if (c->n_experts < 1 || c->n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
   if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > kMaxTopK) return MOE_EUNSUPPORTED;
   if (c->max_tokens < 1 || c->max_tokens > 65536) return MOE_EUNSUPPORTED;
-  if (c->flags & ~MOE_F_SHARED) return MOE_EUNSUPPORTED;
+  if (c->flags & ~(MOE_F_SHARED | MOE_F_RMSNORM)) return MOE_EUNSUPPORTED;
   if (c->flags & MOE_F_SHARED) {
     if (c->shared_inter < 64 || c->shared_inter > 16384 || c->shared_inter % 64)
       return MOE_EUNSUPPORTED;
@@ -151,6 +152,7 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
   d.I = cfg->inter;
   d.has_shared = (cfg->flags & MOE_F_SHARED) ? 1 : 0;
   d.Is = d.has_shared ? cfg->shared_inter : 0;
+  d.rmsnorm = (cfg->flags & MOE_F_RMSNORM) ? 1 : 0;
   d.max_tokens = cfg->max_tokens;
   d.mfma_min_rows = 4;
   d.wide_min_rows = 64;
@@ -227,18 +229,19 @@ static int check_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n
 }
 
 int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
-                int32_t* ids_out, float* p_out, moe_ctx* next, void* stream) {
+                const float* residual, int32_t* ids_out, float* p_out, moe_ctx* next,
+                void* stream) {
   int rc = check_forward(ctx, x, x_dtype, n_tokens, y);
   if (rc != MOE_OK) return rc;
   if (next) {
     if (next == ctx) return fail(ctx, MOE_EINVAL, "lookahead context is this context");
     if (!next->has_weights) return fail(ctx, MOE_ESTATE, "lookahead context has no weights");
-    if (next->cfg.hidden != ctx->cfg.hidden || next->cfg.max_tokens < n_tokens)
+    if (next->cfg.hidden != ctx->cfg.hidden || next->cfg.max_tokens < n_tokens ||
+        next->d.rmsnorm != ctx->d.rmsnorm)
       return fail(ctx, MOE_EINVAL, "lookahead context does not match this layer");
   }
   if (n_tokens == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int f32 = x_dtype == MOE_F32;
   const LayerDev& d = ctx->d;
   // Timing events are recorded only on a stream that is not being captured
   // into a graph (inside a capture an event record would only be a dependency).
@@ -252,7 +255,16 @@ int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, 
     if (end) ctx->launched[(size_t)call * MOE_PROFILE_SLOTS + slot] = 1;
   };
   mark(0, 0);
-  hipError_t e = launch_router(d, x, f32, n_tokens, 0, nullptr, ids_out, p_out, s);
+  hipError_t e = hipSuccess;
+  const void* xin = x;
+  int f32 = x_dtype == MOE_F32;
+  if (d.rmsnorm) {   // the layer (and a lookahead router) sees the normalized rows
+    e = launch_rmsnorm(d, x, f32, n_tokens, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "rmsnorm launch");
+    xin = d.ws + d.L.xn;
+    f32 = 1;
+  }
+  e = launch_router(d, xin, f32, n_tokens, 0, nullptr, ids_out, p_out, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "router launch");
   mark(0, 1);
   mark(1, 0);
@@ -288,15 +300,16 @@ int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, 
     if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core down launch");
     mark(7, 1);
   }
+  // The lookahead reads x before the combine writes y, so y may alias x.
+  if (next) {
+    e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
+  }
   mark(5, 0);
-  e = launch_combine(d, n_tokens, reinterpret_cast<const float*>(d.ws + d.L.p), y, s);
+  e = launch_combine(d, n_tokens, reinterpret_cast<const float*>(d.ws + d.L.p), residual, y, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "combine launch");
   mark(5, 1);
   if (prof) ctx->prof_calls++;
-  if (next) {
-    e = launch_router(next->d, x, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
-  }
   return MOE_OK;
 }
 

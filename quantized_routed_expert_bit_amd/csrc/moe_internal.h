@@ -52,7 +52,7 @@ enum MiscSlot {
 
 struct WsLayout {
   size_t part, logits, x16, x16lo, xs, ids, p, rank, counts, offs, cnt_tb, misc,
-      slots, items, mitems, mtiles, ntiles, pred, hbuf, hs, yslot, total;
+      slots, items, mitems, mtiles, ntiles, pred, hbuf, hs, yslot, xn, total;
 };
 
 // All sizes derived from the config; identical on every call.
@@ -68,7 +68,7 @@ struct LayerDev {
   uint64_t stride;
   const uint8_t* shared;
   // shape
-  int H, E, Epad, k, I, Is, has_shared, max_tokens;
+  int H, E, Epad, k, I, Is, has_shared, rmsnorm, max_tokens;
   int mfma_min_rows;   // rows at which an expert leaves the streaming path
   int wide_min_rows;   // rows at which it uses 128-row instead of 32-row tiles
   // workspace
@@ -89,8 +89,10 @@ hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s);
 bool narrow_needed(const LayerDev& d, int T);
 hipError_t launch_narrow_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
 hipError_t launch_narrow_down(const LayerDev& d, int T, hipStream_t s);
-hipError_t launch_combine(const LayerDev& d, int T, const float* p, float* y, hipStream_t s);
+hipError_t launch_combine(const LayerDev& d, int T, const float* p, const float* residual, float* y,
+                          hipStream_t s);
 hipError_t launch_ws_init(const LayerDev& d, hipStream_t s);
+hipError_t launch_rmsnorm(const LayerDev& d, const void* x, int x_f32, int T, hipStream_t s);
 hipError_t launch_debug_dequant(const void* tiles, int bits, int rows, int cols, float* out,
                                 hipStream_t s);
 

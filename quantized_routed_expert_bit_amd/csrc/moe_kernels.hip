@@ -157,7 +157,8 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   int* s_cur = s_flag + kMaxExperts + 2;                     // [E]
   int* s_scan = s_cur + kMaxExperts + 2;                     // [256]
   int* s_tot = s_scan + 256;                                 // [4]
-  unsigned char* s_pred = reinterpret_cast<unsigned char*>(s_tot + 4);   // [E]
+  int* s_mrows = s_tot + 4;                                  // [E + 1] rows per matrix-core item
+  unsigned char* s_pred = reinterpret_cast<unsigned char*>(s_mrows + kMaxExperts + 2);   // [E]
   const int tid = threadIdx.x;
   const int E = a.E, Tk = a.T * a.k;
   const int R = a.mfma_min_rows;
@@ -185,6 +186,7 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   for (int s = tid; s < Tk; s += 256) a.slots[atomicAdd(&s_cur[ids[s]], 1)] = s;
   if (a.has_shared)
     for (int t = tid; t < a.T; t += 256) a.slots[Tk + t] = Tk + t;
+  __syncthreads();   // every placement is done before s_cur is reused below
   // Work lists: streaming (0 < rows < R) and matrix-core (rows >= R).  With a
   // lookahead prediction the predicted experts come first; the order decides
   // only when an expert's weights are read, never a value.
@@ -201,7 +203,10 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
       __syncthreads();
       const int n = block_excl_scan(s_cur, E, s_scan);
       for (int e = tid; e < E; e += 256)
-        if (s_flag[e]) (path == 0 ? a.items : a.mitems)[base + s_cur[e]] = make_int4(e, s_cnt[e], s_off[e], 0);
+        if (s_flag[e]) {
+          (path == 0 ? a.items : a.mitems)[base + s_cur[e]] = make_int4(e, s_cnt[e], s_off[e], 0);
+          if (path == 1) s_mrows[base + s_cur[e]] = s_cnt[e];
+        }
       base += n;
       __syncthreads();
       if (!pv) break;
@@ -212,7 +217,10 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   int n_gemv = s_tot[0], n_mfma = s_tot[1];
   if (a.has_shared) {
     if (a.T >= R) {
-      if (tid == 0) a.mitems[n_mfma] = make_int4(E, a.T, Tk, 0);
+      if (tid == 0) {
+        a.mitems[n_mfma] = make_int4(E, a.T, Tk, 0);
+        s_mrows[n_mfma] = a.T;
+      }
       ++n_mfma;
     } else {
       if (tid == 0) a.items[n_gemv] = make_int4(E, a.T, Tk, 0);
@@ -226,7 +234,7 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   for (int wide = 1; wide >= 0; --wide) {
     const int bm = wide ? kMfmaBM : kNarrowBM;
     for (int i = tid; i < n_mfma; i += 256) {
-      const int rows = i < s_tot[1] ? s_cnt[a.mitems[i].x] : a.T;
+      const int rows = s_mrows[i];
       const bool mine = wide ? rows >= a.wide_min_rows : rows < a.wide_min_rows;
       s_flag[i] = mine ? (rows + bm - 1) / bm : 0;
       s_cur[i] = s_flag[i];
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a, int tpw)
 }
 
 __global__ __launch_bounds__(256) void bucket_kernel(RouterArgs a) {
-  __shared__ __align__(16) uint8_t smem[4 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + kMaxExperts];
+  __shared__ __align__(16) uint8_t smem[5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + kMaxExperts];
   bucket_tokens(a, a.ids_ws, smem);
 }
 
@@ -1144,10 +1152,12 @@ __global__ __launch_bounds__(256) void mfma_narrow_kernel(MfmaArgs a) {
 
 // ------------------------------------------------------------- combine ----
 
+// y[t] = [residual[t] +] sum_j p[t,j] y_slot[t,j] + y_shared[t].  residual
+// may alias y (each element is read and written by one thread).
 __global__ __launch_bounds__(256) void combine_kernel(int H, int k, int T, int has_shared,
                                                       const float* __restrict__ p,
                                                       const float* __restrict__ yslot,
-                                                      float* __restrict__ y) {
+                                                      const float* residual, float* y) {
   const int t = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= H) return;
@@ -1166,7 +1176,44 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, int T, int h
       if (j0 + j < k) acc = fmaf(pv[j], yv[j], acc);     // fixed order: j ascending
   }
   if (has_shared) acc += yslot[(size_t)(Tk + t) * H + c];
+  if (residual) acc = residual[(size_t)t * H + c] + acc;
   y[(size_t)t * H + c] = acc;
+}
+
+// ------------------------------------------------------------- rmsnorm ----
+
+constexpr float kRmsEps = 1e-6f;
+
+// xn[t] = x[t] / sqrt(mean(x[t]^2) + eps), fp32; one workgroup per token, the
+// sum of squares reduced in a fixed order (deterministic).
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x, int x_f32, int H,
+                                                      float* __restrict__ xn) {
+  __shared__ float red[256];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float* xf = static_cast<const float*>(x) + (size_t)t * H;
+  const uint16_t* xb = static_cast<const uint16_t*>(x) + (size_t)t * H;
+  float ss = 0.f;
+  for (int c = tid; c < H; c += 256) {
+    const float v = x_f32 ? xf[c] : bf16f(xb[c]);
+    ss = fmaf(v, v, ss);
+  }
+  red[tid] = ss;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const float inv = 1.f / sqrtf(red[0] / (float)H + kRmsEps);
+  for (int c = tid; c < H; c += 256) {
+    const float v = x_f32 ? xf[c] : bf16f(xb[c]);
+    xn[(size_t)t * H + c] = v * inv;
+  }
+}
+
+hipError_t launch_rmsnorm(const LayerDev& d, const void* x, int x_f32, int T, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, s, x, x_f32, d.H,
+                     reinterpret_cast<float*>(d.ws + d.L.xn));
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- misc ----
@@ -1426,10 +1473,11 @@ hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const LayerDev& d, int T, const float* p, float* y, hipStream_t s) {
+hipError_t launch_combine(const LayerDev& d, int T, const float* p, const float* residual, float* y,
+                          hipStream_t s) {
   const float* yslot = reinterpret_cast<const float*>(wsp(d, d.L.yslot));
   hipLaunchKernelGGL(combine_kernel, dim3((d.H + 255) / 256, T), dim3(256), 0, s, d.H, d.k, T,
-                     d.has_shared, p, yslot, y);
+                     d.has_shared, p, yslot, residual, y);
   return hipGetLastError();
 }
 

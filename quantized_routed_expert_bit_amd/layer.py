@@ -27,10 +27,10 @@ class MoELayer:
     """One routed-expert layer: router (8-bit), top-k, 4-bit experts, combine."""
 
     def __init__(self, hidden, n_experts, top_k, inter, shared_inter=0, max_tokens=1,
-                 device=0):
+                 device=0, rmsnorm=False):
         self.lib = L.load()
         self.cfg = L.make_config(hidden, n_experts, top_k, inter, shared_inter, max_tokens,
-                                 device)
+                                 device, rmsnorm)
         self.hidden, self.n_experts, self.top_k = hidden, n_experts, top_k
         self.max_tokens = max_tokens
         self.device = torch.device("cuda", device)
@@ -67,7 +67,8 @@ class MoELayer:
             return L.MOE_F32
         raise TypeError("x must be bfloat16 or float32")
 
-    def forward(self, x, return_selection=False, lookahead=None, y=None):
+    def forward(self, x, return_selection=False, lookahead=None, y=None, residual=None):
+        """y = layer(x), or residual + layer(x); y may be the residual tensor."""
         T = x.shape[0]
         x = x.contiguous()
         if y is None:
@@ -78,7 +79,8 @@ class MoELayer:
             p = torch.empty((T, self.top_k), dtype=torch.float32, device=self.device)
         nxt = lookahead.ctx if lookahead is not None else None
         self._check(self.lib.moe_forward(self.ctx, _ptr(x), self._dtype(x), T, _ptr(y),
-                                         _ptr(ids), _ptr(p), nxt, _stream()), "moe_forward")
+                                         _ptr(residual), _ptr(ids), _ptr(p), nxt, _stream()),
+                    "moe_forward")
         return (y, ids, p) if return_selection else y
 
     __call__ = forward

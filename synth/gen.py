@@ -238,3 +238,42 @@ def layer_inputs(wl: Workload, layer: int = 0, seed: int = 0) -> LayerInputs:
 
 
 __all__.append("layer_inputs")
+
+
+# ---------------------------------------------------------------------------
+# Device-side generation for banks too large to generate on the host in
+# reasonable time (tens to hundreds of GB).  Same value recipe as above, drawn
+# with torch's seeded device generator instead of PCG64, so the bytes differ
+# from make_record's; the header layout is identical.  A consumer that needs a
+# record on the host (the oracle) copies it back from the bank.
+# ---------------------------------------------------------------------------
+
+def gpu_bank(seed: int, cfg: int, layer: int, hidden: int, inter: int, n_records: int,
+             device, shared: bool = False):
+    """A bank of n_records expert records (uint8 device tensor) and its stride.
+    With shared=True, one record with expert id -1 (n_records must be 1)."""
+    import torch
+    lay = record_layout(hidden, inter)
+    stride, n_tiles = lay["stride"], lay["tiles"]
+    bank = torch.zeros(n_records * stride, dtype=torch.uint8, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(((seed * 1000003 + cfg) * 1000003 + layer) * 8 + (_T_SHARED if shared else _T_EXPERT))
+    rec = bank.view(n_records, stride)
+    sec = n_tiles * Q4_TILE_BYTES
+    for e in range(n_records):
+        hdr = np.zeros(HEADER_BYTES, dtype=np.uint8)
+        _pack_header(hdr, SHARED_ID if shared else e, hidden, inter, lay)
+        rec[e, :HEADER_BYTES].copy_(torch.from_numpy(hdr))
+        for off in (lay["gate"], lay["up"], lay["down"]):
+            tiles = rec[e, off: off + sec].view(n_tiles, Q4_TILE_BYTES)
+            tiles[:, :Q4_CODE_BYTES] = torch.randint(0, 256, (n_tiles, Q4_CODE_BYTES), generator=gen,
+                                                     device=device, dtype=torch.uint8)
+            z = torch.randn(n_tiles * TILE_ROWS, generator=gen, device=device, dtype=torch.float64)
+            s = (z.abs() * 0.02 / 8.0).to(torch.float16)
+            b = (-8.0 * s.to(torch.float64)).to(torch.float16)
+            sb = torch.stack([s, b], dim=1).contiguous().view(torch.uint8)
+            tiles[:, Q4_CODE_BYTES:] = sb.view(n_tiles, Q4_TILE_BYTES - Q4_CODE_BYTES)
+    return bank, stride
+
+
+__all__.append("gpu_bank")

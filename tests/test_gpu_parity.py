@@ -222,3 +222,20 @@ def test_prefill_2048_tokens(torch_dev):
     y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
     P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
                     p.cpu().numpy(), "prefill T=2048")
+
+
+def test_rmsnorm_input(torch_dev):
+    """MOE_F_RMSNORM: the layer runs on x / sqrt(mean(x^2) + 1e-6)."""
+    import torch
+    from quantized_routed_expert_bit_amd import MoELayer
+    wl = synth.WORKLOADS[1]
+    li = synth.layer_inputs(wl)
+    sh = wl.shape
+    w = P.upload_layer(li, torch_dev)
+    m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, 16, rmsnorm=True)
+    m.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
+    ol = P.oracle_layer(li)
+    x32 = (np.random.default_rng(8).standard_normal((16, sh.hidden)) * 37.0).astype(np.float32)
+    y, ids, p = m.forward(torch.from_numpy(x32).to(torch_dev), return_selection=True)
+    P.check_forward(ol, oracle.rms_normalize(x32.astype(np.float64)), y.cpu().numpy(),
+                    ids.cpu().numpy(), p.cpu().numpy(), "rmsnorm input")

@@ -334,3 +334,28 @@ def test_stack_lookahead_does_not_change_result():
     assert "lookahead_ids" in b["layers"][0] and "lookahead_ids" not in a["layers"][0]
     # residual identity: out = x + y_0 + y_1 + y_2
     assert np.allclose(a["out"], x + sum(r["y"] for r in a["layers"]), rtol=1e-15, atol=1e-15)
+
+
+def test_rms_normalize_closed_forms():
+    """c * 1 -> sign(c) / sqrt(1 + eps/c^2); rows scale-invariant; unit RMS."""
+    x = np.full((1, 64), 3.0)
+    assert np.allclose(oracle.rms_normalize(x), 1.0 / np.sqrt(1 + 1e-6 / 9), rtol=1e-15, atol=0)
+    r = np.random.default_rng(3).standard_normal((4, 256)) * np.array([[0.1], [1], [10], [1e3]])
+    n = oracle.rms_normalize(r)
+    assert np.allclose(np.sqrt(np.mean(n * n, axis=1)), 1.0, rtol=1e-4, atol=0)
+    assert np.allclose(oracle.rms_normalize(r * 7.0)[1:], n[1:], rtol=1e-6, atol=0)
+    e = np.zeros((1, 64))
+    e[0, 5] = 2.0
+    assert np.isclose(oracle.rms_normalize(e)[0, 5], 2.0 / np.sqrt(4 / 64 + 1e-6), rtol=1e-15)
+
+
+def test_stack_without_norm_grows_quadratically():
+    """Random-weight SwiGLU layers roughly square the activation scale, so an
+    un-normalized residual stack blows up: the reason the stack normalizes."""
+    H, I = 128, 64
+    rec = synth.make_record(2, 96, 0, 0, H, I)
+    mats = oracle.expert_matrices(rec, H, I)
+    x = np.random.default_rng(0).standard_normal((1, H))
+    small = oracle.expert_ffn(10 * x, *mats)
+    big = oracle.expert_ffn(100 * x, *mats)
+    assert 50 < np.abs(big).max() / np.abs(small).max() < 200      # ~ 10^2
