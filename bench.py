@@ -197,6 +197,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the T=1 and T=4 lines")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
+    ap.add_argument("--workload", choices=("all", "decode", "prefill"), default="all",
+                    help="decode: only the 16-token decode line; prefill: only the prefill line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -207,6 +209,11 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
+    if args.workload == "prefill":
+        print(json.dumps({"prefill": run_prefill(args, dev)}), flush=True)
+        return
+    if args.workload == "decode":
+        args.no_extra = args.no_prefill = args.no_cpu_baseline = True
     T = args.batch
     wl, layers = build_layers(1, args.copies, max(T, 16), dev)
     sh = wl.shape
