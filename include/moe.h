@@ -68,9 +68,13 @@
  * Every buffer is caller-owned device memory unless stated otherwise.  The
  * library owns only the context.  Weight pointers passed to moe_set_weights
  * are borrowed until the next moe_set_weights or moe_close and are never
- * written or freed.  All device work of a call is enqueued on the caller's
- * hipStream_t (passed as void*, NULL = the null stream); moe_forward performs
- * no host synchronisation and no allocation.  A context is not thread-safe and
+ * written or freed.  All device work of a call is ordered on the caller's
+ * hipStream_t (passed as void*, NULL = the null stream): it starts after work
+ * already enqueued there and finishes before work enqueued later.  Inside a
+ * forward, the matrix-core kernels run on a stream the context owns, forked
+ * from and joined back into the caller's stream with events (so a forward can
+ * be captured into a HIP graph).  moe_forward performs no host synchronisation
+ * and no allocation.  A context is not thread-safe and
  * two calls on one context must not overlap on different streams (they share
  * the workspace).  Functions return MOE_OK (0) or a negative status; the
  * context keeps a message for the last failure (moe_last_error).  Asynchronous

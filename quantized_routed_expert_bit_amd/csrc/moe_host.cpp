@@ -23,6 +23,10 @@ struct moe_ctx {
   std::vector<hipEvent_t> ev;
   std::vector<uint8_t> launched;  // [call][slot]
   int prof_max = 0, prof_calls = 0;
+  // matrix-core work runs on this stream, forked from and joined back into the
+  // caller's stream with two events (created at open, default priority)
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 static void prof_clear(moe_ctx* c) {
@@ -157,6 +161,13 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
   d.mfma_min_rows = 4;
   d.wide_min_rows = 64;
   d.L = ws_layout(*cfg);
+  if (hipSetDevice(cfg->device) != hipSuccess ||
+      hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&c->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->join, hipEventDisableTiming) != hipSuccess) {
+    moe_close(c);
+    return MOE_EHIP;
+  }
   *out = c;
   return MOE_OK;
 }
@@ -249,12 +260,12 @@ int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, 
   if (ctx->prof_calls < ctx->prof_max) (void)hipStreamIsCapturing(s, &cap);
   const bool prof = ctx->prof_calls < ctx->prof_max && cap == hipStreamCaptureStatusNone;
   const int call = ctx->prof_calls;
-  auto mark = [&](int slot, int end) {
+  auto mark = [&](int slot, int end, hipStream_t st) {
     if (!prof) return;
-    (void)hipEventRecord(ctx->ev[((size_t)call * MOE_PROFILE_SLOTS + slot) * 2 + end], s);
+    (void)hipEventRecord(ctx->ev[((size_t)call * MOE_PROFILE_SLOTS + slot) * 2 + end], st);
     if (end) ctx->launched[(size_t)call * MOE_PROFILE_SLOTS + slot] = 1;
   };
-  mark(0, 0);
+  mark(0, 0, s);
   hipError_t e = hipSuccess;
   const void* xin = x;
   int f32 = x_dtype == MOE_F32;
@@ -266,49 +277,66 @@ int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, 
   }
   e = launch_router(d, xin, f32, n_tokens, 0, nullptr, ids_out, p_out, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "router launch");
-  mark(0, 1);
-  mark(1, 0);
+  mark(0, 1, s);
+  // Matrix-core work (experts with many rows, and the shared expert at T >= 4)
+  // and streaming work touch disjoint slots: run them concurrently.
+  const bool mf = mfma_needed(d, n_tokens), nf = narrow_needed(d, n_tokens);
+  hipStream_t ms = s;
+  if (mf || nf) {
+    ms = ctx->side;
+    if ((e = hipEventRecord(ctx->fork, s)) != hipSuccess ||
+        (e = hipStreamWaitEvent(ms, ctx->fork, 0)) != hipSuccess)
+      return hip_fail(ctx, e, "forking the matrix-core stream");
+  }
+  if (mf) {
+    mark(3, 0, ms);
+    e = launch_mfma_up(d, f32, n_tokens, ms);
+    if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core gate/up launch");
+    mark(3, 1, ms);
+  }
+  if (nf) {
+    mark(6, 0, ms);
+    e = launch_narrow_up(d, f32, n_tokens, ms);
+    if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core gate/up launch");
+    mark(6, 1, ms);
+  }
+  if (mf) {
+    mark(4, 0, ms);
+    e = launch_mfma_down(d, n_tokens, ms);
+    if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core down launch");
+    mark(4, 1, ms);
+  }
+  if (nf) {
+    mark(7, 0, ms);
+    e = launch_narrow_down(d, n_tokens, ms);
+    if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core down launch");
+    mark(7, 1, ms);
+  }
+  if (mf || nf) {
+    if ((e = hipEventRecord(ctx->join, ms)) != hipSuccess)
+      return hip_fail(ctx, e, "joining the matrix-core stream");
+  }
+  mark(1, 0, s);
   e = launch_gemv_up(d, f32, n_tokens, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "streaming gate/up launch");
-  mark(1, 1);
-  const bool mf = mfma_needed(d, n_tokens), nf = narrow_needed(d, n_tokens);
-  if (mf) {
-    mark(3, 0);
-    e = launch_mfma_up(d, f32, n_tokens, s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core gate/up launch");
-    mark(3, 1);
-  }
-  if (nf) {
-    mark(6, 0);
-    e = launch_narrow_up(d, f32, n_tokens, s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core gate/up launch");
-    mark(6, 1);
-  }
-  mark(2, 0);
+  mark(1, 1, s);
+  mark(2, 0, s);
   e = launch_gemv_down(d, n_tokens, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "streaming down launch");
-  mark(2, 1);
-  if (mf) {
-    mark(4, 0);
-    e = launch_mfma_down(d, n_tokens, s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core down launch");
-    mark(4, 1);
-  }
-  if (nf) {
-    mark(7, 0);
-    e = launch_narrow_down(d, n_tokens, s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core down launch");
-    mark(7, 1);
-  }
+  mark(2, 1, s);
   // The lookahead reads x before the combine writes y, so y may alias x.
   if (next) {
     e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
   }
-  mark(5, 0);
+  if (mf || nf) {
+    if ((e = hipStreamWaitEvent(s, ctx->join, 0)) != hipSuccess)
+      return hip_fail(ctx, e, "joining the matrix-core stream");
+  }
+  mark(5, 0, s);
   e = launch_combine(d, n_tokens, reinterpret_cast<const float*>(d.ws + d.L.p), residual, y, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "combine launch");
-  mark(5, 1);
+  mark(5, 1, s);
   if (prof) ctx->prof_calls++;
   return MOE_OK;
 }
@@ -381,6 +409,9 @@ int moe_set_path_rows(moe_ctx* ctx, int32_t mfma_min_rows, int32_t wide_min_rows
 void moe_close(moe_ctx* ctx) {
   if (!ctx) return;
   prof_clear(ctx);
+  if (ctx->join) (void)hipEventDestroy(ctx->join);
+  if (ctx->fork) (void)hipEventDestroy(ctx->fork);
+  if (ctx->side) (void)hipStreamDestroy(ctx->side);
   delete ctx;
 }
 

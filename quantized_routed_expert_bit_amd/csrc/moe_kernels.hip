@@ -91,26 +91,62 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __shfl(v, 0);
 }
 
+// ---- wave64 cross-lane operations on DPP (no LDS round trips) ----
+// DPP controls (gfx9): quad_perm xor1 0xB1, xor2 0x4E, row_shr:n 0x110+n,
+// row_mirror 0x140, row_half_mirror 0x141, row_bcast15 0x142, row_bcast31 0x143.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int old, int src) {
+  return __builtin_amdgcn_update_dpp(old, src, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = __builtin_bit_cast(float, dpp_i<CTRL, ROWS>(__builtin_bit_cast(int, v),
+                                                               __builtin_bit_cast(int, v)));
+  const int oi = dpp_i<CTRL, ROWS>(i, i);
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+// (value desc, index asc) maximum over the wave; every lane gets the winner.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<0xB1, 0xF>(v, i);
+  argmax_step<0x4E, 0xF>(v, i);
+  argmax_step<0x141, 0xF>(v, i);
+  argmax_step<0x140, 0xF>(v, i);
+  argmax_step<0x142, 0xA>(v, i);
+  argmax_step<0x143, 0xC>(v, i);
+  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+// Inclusive prefix sum over the wave (lane order).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111, 0xF>(0, x);
+  x += dpp_i<0x112, 0xF>(0, x);
+  x += dpp_i<0x114, 0xF>(0, x);
+  x += dpp_i<0x118, 0xF>(0, x);
+  x += dpp_i<0x142, 0xA>(0, x);
+  x += dpp_i<0x143, 0xC>(0, x);
+  return x;
+}
+
 // Exclusive scan of n ints held in LDS (n <= 256 * 8), by a 256-thread block.
 // Returns the total.  All threads must call it.
 __device__ int block_excl_scan(int* data, int n, int* scratch256) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n + 255) / 256;
   const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
   int s = 0;
   for (int i = b0; i < b1; ++i) s += data[i];
-  scratch256[tid] = s;
+  const int incl = wave_incl_scan(s);
+  if (lane == 63) scratch256[wave] = incl;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    int v = tid >= off ? scratch256[tid - off] : 0;
-    __syncthreads();
-    scratch256[tid] += v;
-    __syncthreads();
-  }
-  int run = scratch256[tid] - s;  // exclusive prefix of this thread's chunk
-  const int total = scratch256[255];
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += scratch256[w];
+  const int total = scratch256[0] + scratch256[1] + scratch256[2] + scratch256[3];
+  int run = before + incl - s;  // exclusive prefix of this thread's chunk
   for (int i = b0; i < b1; ++i) {
-    int v = data[i];
+    const int v = data[i];
     data[i] = run;
     run += v;
   }
@@ -144,6 +180,8 @@ struct RouterArgs {
   int2* ntiles;
   int mfma_min_rows, wide_min_rows, has_shared;
 };
+
+constexpr int kBucketSmem = 5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + kMaxExperts;
 
 // Bucketing, by one 256-thread workgroup once every token's top-k is known:
 // LDS histogram of the T*k selections -> exclusive scan -> slot lists grouped
@@ -189,29 +227,27 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   __syncthreads();   // every placement is done before s_cur is reused below
   // Work lists: streaming (0 < rows < R) and matrix-core (rows >= R).  With a
   // lookahead prediction the predicted experts come first; the order decides
-  // only when an expert's weights are read, never a value.
+  // only when an expert's weights are read, never a value.  One scan per path
+  // counts both halves at once: predicted in the low 16 bits, the rest in the
+  // high 16 (each total <= kMaxExperts, so the halves never carry).
   for (int path = 0; path < 2; ++path) {
-    int base = 0;
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int e = tid; e < E; e += 256) {
-        const int c = s_cnt[e];
-        const bool on = path == 0 ? (c > 0 && c < R) : (c >= R);
-        const bool first = pv ? s_pred[e] != 0 : true;
-        s_flag[e] = on && (pass == 0 ? first : !first) ? 1 : 0;
-        s_cur[e] = s_flag[e];
-      }
-      __syncthreads();
-      const int n = block_excl_scan(s_cur, E, s_scan);
-      for (int e = tid; e < E; e += 256)
-        if (s_flag[e]) {
-          (path == 0 ? a.items : a.mitems)[base + s_cur[e]] = make_int4(e, s_cnt[e], s_off[e], 0);
-          if (path == 1) s_mrows[base + s_cur[e]] = s_cnt[e];
-        }
-      base += n;
-      __syncthreads();
-      if (!pv) break;
+    for (int e = tid; e < E; e += 256) {
+      const int c = s_cnt[e];
+      const bool on = path == 0 ? (c > 0 && c < R) : (c >= R);
+      const bool first = pv ? s_pred[e] != 0 : true;
+      s_flag[e] = on ? (first ? 1 : 2) : 0;
+      s_cur[e] = on ? (first ? 1 : 0x10000) : 0;
     }
-    if (tid == 0) s_tot[path] = base;
+    __syncthreads();
+    const int tot = block_excl_scan(s_cur, E, s_scan);
+    const int n_first = tot & 0xffff;
+    for (int e = tid; e < E; e += 256)
+      if (s_flag[e]) {
+        const int pos = s_flag[e] == 1 ? (s_cur[e] & 0xffff) : n_first + (s_cur[e] >> 16);
+        (path == 0 ? a.items : a.mitems)[pos] = make_int4(e, s_cnt[e], s_off[e], 0);
+        if (path == 1) s_mrows[pos] = s_cnt[e];
+      }
+    if (tid == 0) s_tot[path] = n_first + (tot >> 16);
     __syncthreads();
   }
   int n_gemv = s_tot[0], n_mfma = s_tot[1];
@@ -231,21 +267,23 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   // matrix-core row tiles (item, first row): 128-row tiles for items with
   // >= wide_min_rows rows, 32-row tiles for the others
   int n_tiles = 0, n_narrow = 0;
-  for (int wide = 1; wide >= 0; --wide) {
-    const int bm = wide ? kMfmaBM : kNarrowBM;
-    for (int i = tid; i < n_mfma; i += 256) {
-      const int rows = s_mrows[i];
-      const bool mine = wide ? rows >= a.wide_min_rows : rows < a.wide_min_rows;
-      s_flag[i] = mine ? (rows + bm - 1) / bm : 0;
-      s_cur[i] = s_flag[i];
+  if (n_mfma > 0) {   // uniform across the workgroup
+    for (int wide = 1; wide >= 0; --wide) {
+      const int bm = wide ? kMfmaBM : kNarrowBM;
+      for (int i = tid; i < n_mfma; i += 256) {
+        const int rows = s_mrows[i];
+        const bool mine = wide ? rows >= a.wide_min_rows : rows < a.wide_min_rows;
+        s_flag[i] = mine ? (rows + bm - 1) / bm : 0;
+        s_cur[i] = s_flag[i];
+      }
+      __syncthreads();
+      const int n = block_excl_scan(s_cur, n_mfma, s_scan);
+      int2* out = wide ? a.mtiles : a.ntiles;
+      for (int i = tid; i < n_mfma; i += 256)
+        for (int j = 0; j < s_flag[i]; ++j) out[s_cur[i] + j] = make_int2(i, j * bm);
+      __syncthreads();
+      if (wide) n_tiles = n; else n_narrow = n;
     }
-    __syncthreads();
-    const int n = block_excl_scan(s_cur, n_mfma, s_scan);
-    int2* out = wide ? a.mtiles : a.ntiles;
-    for (int i = tid; i < n_mfma; i += 256)
-      for (int j = 0; j < s_flag[i]; ++j) out[s_cur[i] + j] = make_int2(i, j * bm);
-    __syncthreads();
-    if (wide) n_tiles = n; else n_narrow = n;
   }
   if (tid == 0) {
     a.misc[kNGemv] = n_gemv;
@@ -426,105 +464,160 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouterArgs a) {
 // partials in fixed order (all loads of a thread issued together), adds the
 // logit bias, then one wave per token selects k experts by (logit desc,
 // index asc) with wave64 shuffles and takes the softmax over them.
+// Selection key of expert e with logit v: the float's order-preserving bit
+// pattern above ~e, so that the largest key is the largest logit and, among
+// equal logits, the lowest index.  0 is below every real key.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int topk_key_index(uint64_t key) {
+  return (int)(0xFFFFFFFFu - (uint32_t)key);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void key_max_step(uint64_t& key) {
+  const uint32_t lo = (uint32_t)dpp_i<CTRL, ROWS>((int)(uint32_t)key, (int)(uint32_t)key);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL, ROWS>((int)(uint32_t)(key >> 32), (int)(uint32_t)(key >> 32));
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  key = o > key ? o : key;
+}
+// Maximum key over each group of LPT lanes (16: one DPP row; 64: the wave);
+// every lane of the group gets it.
+template <int LPT>
+__device__ __forceinline__ uint64_t group_key_max(uint64_t key) {
+  key_max_step<0xB1, 0xF>(key);
+  key_max_step<0x4E, 0xF>(key);
+  key_max_step<0x141, 0xF>(key);
+  key_max_step<0x140, 0xF>(key);
+  if constexpr (LPT == 64) {
+    key_max_step<0x142, 0xA>(key);
+    key_max_step<0x143, 0xC>(key);
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
+    key = ((uint64_t)hi << 32) | lo;
+  }
+  return key;
+}
+
+// Top-k of the logits of nt tokens held in LDS (s_lg[t * Epad + e]).  A group
+// of LPT lanes owns one token, lane l holding experts l + LPT*i (i < NV); the
+// k winners come out one at a time as group maxima of the per-lane best key.
+// The softmax over the selected logits is summed in selection order.
+template <int LPT, int NV>
+__device__ void topk_select(const RouterArgs& a, const float* s_lg, int* s_ids, int nt, int t0) {
+  constexpr int NG = 256 / LPT;          // token groups per workgroup
+  const int tid = threadIdx.x, l = tid % LPT;
+  for (int t = tid / LPT; t < nt; t += NG) {
+    uint64_t key[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = l + LPT * i;
+      key[i] = e < a.E ? topk_key(s_lg[t * a.Epad + e], e) : 0ull;
+    }
+    uint64_t mine = 0, first = 0;
+    float sum = 0.f;
+    for (int j = 0; j < a.k; ++j) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int i = 1; i < NV; ++i) best = key[i] > best ? key[i] : best;
+      best = group_key_max<LPT>(best);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) key[i] = key[i] == best ? 0ull : key[i];
+      if (j == 0) first = best;
+      if (l == j) mine = best;
+      sum += expf(topk_key_value(best) - topk_key_value(first));
+    }
+    if (l < a.k) {
+      const int tok = t0 + t;
+      int id = topk_key_index(mine);
+      id = id >= 0 && id < a.E ? id : 0;   // always an expert index, whatever the inputs
+      const size_t o = (size_t)tok * a.k + l;
+      if (a.mode == 0) {
+        const float pr = expf(topk_key_value(mine) - topk_key_value(first)) / sum;
+        a.ids_ws[o] = id;
+        a.p_ws[o] = pr;
+        s_ids[t * a.k + l] = id;
+        if (a.ids_out) a.ids_out[o] = id;
+        if (a.p_out) a.p_out[o] = pr;
+      } else {
+        a.pred[o] = id;
+      }
+    }
+  }
+}
+
+// Top-k: workgroup = tpw tokens (tpw * Epad <= 4096).  Sums the k-split
+// partials in fixed (split-ascending) order, adds the logit bias, then selects
+// k experts per token by (logit desc, index asc) and takes the softmax over
+// them.  A batch that one workgroup covers (decode) is bucketed in the same
+// launch.  LPT/NV: lanes per token and logits per lane (LPT * NV >= Epad).
+template <int LPT, int NV>
 __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a, int tpw) {
-  __shared__ float s_lg[512];
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ float s_lg[4096];
+  __shared__ int s_ids[kRouterTokMax * kMaxTopK];
+  const int tid = threadIdx.x;
   const int t0 = blockIdx.x * tpw;
   const int nt = min(tpw, a.T - t0);
-  const int npair = nt * a.Epad;   // <= 512: at most 2 per thread
-  float acc[2] = {0.f, 0.f};
-  for (int k0 = 0; k0 < a.KS; k0 += 16) {
-    float pv[2][16];
+  const int npair = nt * a.Epad;
+  // every load unconditional (indices clamped into the buffer), so a batch of
+  // 4 pairs x 8 splits is in flight at once
+  for (int p0 = 0; p0 < npair; p0 += 1024) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int pt[4], pe[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = tid + 256 * j;
-      const int t = i / a.Epad, e = i - t * a.Epad;
+    for (int j = 0; j < 4; ++j) {
+      const int i = min(p0 + tid + 256 * j, npair - 1);
+      pt[j] = i / a.Epad;
+      pe[j] = i - pt[j] * a.Epad;
+    }
+    for (int k0 = 0; k0 < a.KS; k0 += 8) {
+      float pv[4][8];
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        pv[j][q] = (i < npair && e < a.E && k0 + q < a.KS)
-                       ? a.part[((size_t)(k0 + q) * a.T + t0 + t) * a.Epad + e]
-                       : 0.f;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int ks = min(k0 + q, a.KS - 1);
+          pv[j][q] = a.part[((size_t)ks * a.T + t0 + pt[j]) * a.Epad + pe[j]];
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[j] += k0 + q < a.KS ? pv[j][q] : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[j] += pv[j][q];
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = tid + 256 * j;
-    if (i < npair) {
-      const int t = i / a.Epad, e = i - t * a.Epad;
-      float v = -INFINITY;
-      if (e < a.E) {
-        const float sum = a.bias ? acc[j] + a.bias[e] : acc[j];
-        if (a.mode == 1) a.logits_out[(size_t)(t0 + t) * a.E + e] = sum;
-        v = sum == sum ? sum : -INFINITY;   // a NaN logit (out of contract) ranks last
+    for (int j = 0; j < 4; ++j) {
+      const int i = p0 + tid + 256 * j;
+      if (i < npair) {
+        const int t = pt[j], e = pe[j];
+        float v = -INFINITY;
+        if (e < a.E) {
+          const float sum = a.bias ? acc[j] + a.bias[e] : acc[j];
+          if (a.mode == 1) a.logits_out[(size_t)(t0 + t) * a.E + e] = sum;
+          // a NaN logit (out of contract) ranks last; -0 ranks as +0
+          v = sum == sum ? sum + 0.f : -INFINITY;
+        }
+        s_lg[i] = v;
       }
-      s_lg[i] = v;
     }
   }
   if (a.mode == 1) return;
   __syncthreads();
-  const int NE = a.Epad >> 6;
-  for (int t = wave; t < nt; t += kRouterWaves) {
-    const int tok = t0 + t;
-    float v[kMaxExperts / 64];
-#pragma unroll
-    for (int i = 0; i < kMaxExperts / 64; ++i)
-      v[i] = i < NE ? s_lg[t * a.Epad + lane + 64 * i] : -INFINITY;
-    uint32_t taken = 0;
-    float myv = 0.f;
-    int myi = 0;
-    for (int j = 0; j < a.k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < kMaxExperts / 64; ++i) {
-        const int e = lane + 64 * i;
-        if (i < NE && e < a.E && !((taken >> i) & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
-          bv = v[i];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == j) {
-        myv = bv;
-        myi = bi;
-      }
-    }
-    myi = myi < a.E ? myi : 0;        // always an expert index, whatever the inputs
-    const float mx = __shfl(myv, 0);
-    const float z = lane < a.k ? expf(myv - mx) : 0.f;
-    float sum = 0.f;
-    for (int j = 0; j < a.k; ++j) sum += __shfl(z, j);
-    if (lane < a.k) {
-      const size_t o = (size_t)tok * a.k + lane;
-      if (a.mode == 0) {
-        const float p = z / sum;
-        a.ids_ws[o] = myi;
-        a.p_ws[o] = p;
-        if (a.ids_out) a.ids_out[o] = myi;
-        if (a.p_out) a.p_out[o] = p;
-      } else {
-        a.pred[o] = myi;
-      }
-    }
-  }
+  topk_select<LPT, NV>(a, s_lg, s_ids, nt, t0);
   if (a.mode == 2 && blockIdx.x == 0 && tid == 0) a.misc[kPredValid] = a.T * a.k;
+  if (a.mode == 0 && gridDim.x == 1) {
+    __shared__ __align__(16) uint8_t smem[kBucketSmem];
+    __syncthreads();
+    bucket_tokens(a, s_ids, smem);
+  }
 }
 
 __global__ __launch_bounds__(256) void bucket_kernel(RouterArgs a) {
-  __shared__ __align__(16) uint8_t smem[5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + kMaxExperts];
+  __shared__ __align__(16) uint8_t smem[kBucketSmem];
   bucket_tokens(a, a.ids_ws, smem);
 }
 
@@ -660,9 +753,13 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(
   st.gend = (G * (wave + 1)) / kGemvWaves;
   st.lane = lane;
 
+  const bool busy = st.gbeg < st.gend;
   for (int p0 = 0; p0 < m; p0 += mt) {
     const int nt = min(mt, m - p0);
     if (p0 > 0) __syncthreads();
+    // weights first: they depend only on the work item, so their loads are in
+    // flight while the token rows are looked up and staged
+    if (busy) st.prefetch();
     if (tid < nt) {
       const int slot = slots[loff + p0 + tid];
       s_slot[tid] = slot;
@@ -686,8 +783,6 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(
       const int t = i / G, g = i - t * G;
       xsl[i] = xs[(size_t)s_tok[t] * G + g];
     }
-    const bool busy = st.gbeg < st.gend;
-    if (busy) st.prefetch();
     __syncthreads();
     float acc[2][kGemvTokV2];
 #pragma unroll
@@ -751,9 +846,11 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
   st.gend = (G2 * (wave + 1)) / kGemvWaves;
   st.lane = lane;
 
+  const bool busy = st.gbeg < st.gend;
   for (int p0 = 0; p0 < m; p0 += mt) {
     const int nt = min(mt, m - p0);
     if (p0 > 0) __syncthreads();
+    if (busy) st.prefetch();
     if (tid < nt) s_slot[tid] = slots[loff + p0 + tid];
     __syncthreads();
     const int hq = inter >> 3;
@@ -766,8 +863,6 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
       const int t = i / G2, g = i - t * G2;
       hsl[i] = hs[hs_off(s_slot[t], Tk, I, Is) + g];
     }
-    const bool busy = st.gbeg < st.gend;
-    if (busy) st.prefetch();
     __syncthreads();
     float acc[1][kGemvTokV2];
 #pragma unroll
@@ -1308,12 +1403,20 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   hipLaunchKernelGGL(router_gemv_kernel, dim3(a.n_rb, a.KS, a.n_tb), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int tpw = 512 / d.Epad;
+  int tpw = 4096 / d.Epad;
   if (tpw < 1) tpw = 1;
   if (tpw > kRouterTokMax) tpw = kRouterTokMax;
-  hipLaunchKernelGGL(router_topk_kernel, dim3((T + tpw - 1) / tpw), dim3(256), 0, s, a, tpw);
+  const int n_wg = (T + tpw - 1) / tpw;
+  // a 16-lane group per token where the logits fit 8 per lane and the k
+  // winners fit the group's lanes; else the whole wave
+  if (d.Epad <= 128 && d.k <= 16)
+    hipLaunchKernelGGL((router_topk_kernel<16, 8>), dim3(n_wg), dim3(256), 0, s, a, tpw);
+  else if (d.Epad <= 512)
+    hipLaunchKernelGGL((router_topk_kernel<64, 8>), dim3(n_wg), dim3(256), 0, s, a, tpw);
+  else
+    hipLaunchKernelGGL((router_topk_kernel<64, 16>), dim3(n_wg), dim3(256), 0, s, a, tpw);
   e = hipGetLastError();
-  if (e != hipSuccess || mode != 0) return e;
+  if (e != hipSuccess || mode != 0 || n_wg == 1) return e;   // one workgroup buckets itself
   hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
