@@ -32,7 +32,8 @@ constexpr int kMaxExperts = 1024;
 // Streaming (GEMV) expert path: up to kGemvTok tokens per pass over the weights.
 constexpr int kGemvTok = 16;
 constexpr int kGemvTokV2 = 4;   // token rows per streaming pass (register accumulators)
-constexpr int kGemvWaves = 4;
+constexpr int kGemvWaves = 4;   // waves per streaming workgroup (they split the K groups)
+constexpr int kGemvThreads = 64 * kGemvWaves;
 
 // Matrix-core (MFMA) expert path: rows (tokens) per wide tile, per narrow tile.
 constexpr int kMfmaBM = 128;

@@ -715,29 +715,95 @@ struct GemvStream {
   }
 };
 
-constexpr int kGemvP = 4;   // groups in flight per wave
+constexpr int kGemvP = 2;   // groups in flight per wave
+
+// Which (work item, row block) a streaming workgroup owns.  The grid is flat:
+// the first nsh workgroups are the row blocks of the shared expert (the last
+// streaming item when it streams), started first because it is the largest;
+// then nrb row blocks per routed item.  Returns false for a workgroup past
+// the routed items of this forward.
+__device__ __forceinline__ bool gemv_work(const int* misc, int nsh, int nrb, int& item_i, int& rb) {
+  const int n_items = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNGemv];
+  const int b = blockIdx.x;
+  if (b < nsh) {
+    item_i = n_items - 1;
+    rb = b;
+    return item_i >= 0;
+  }
+  item_i = (b - nsh) / nrb;
+  rb = (b - nsh) - item_i * nrb;
+  return item_i < n_items - (nsh > 0 ? 1 : 0);
+}
+
+// Four wave-uniform values (one per token row of a streaming pass) selected
+// by a runtime row index without indexing a register array.
+static_assert(kGemvTokV2 == 4, "streaming passes hold four token rows");
+struct Four {
+  int v0, v1, v2, v3;
+  __device__ __forceinline__ int operator[](int i) const {
+    return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3;
+  }
+};
+
+// Stage nt rows of `row_u4` uint4 each into LDS (row t at dst + t * dst_row_dw
+// dwords) from src_row(t).  Each batch issues all its loads before the first
+// LDS write (every load unconditional, index clamped into the last row), so a
+// batch costs one memory round trip.
+// src_row(t) must be a value-capturing callable (no arrays captured by
+// reference: they would live in scratch memory).
+template <typename SrcRow>
+__device__ __forceinline__ void stage_rows(uint32_t* dst, int dst_row_dw, int nt, int row_u4,
+                                           const SrcRow& src_row) {
+  // (a native vector type: an array of HIP's uint4 is not split into
+  // registers and would live in scratch memory)
+  // The first batch is straight-line code: inside a loop the compiler's
+  // waits for the registers the previous iteration loaded also wait for the
+  // weight loads issued before the staging.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int NB = 8;
+  const int tid = threadIdx.x, tot = nt * row_u4;
+  auto batch = [&](int base) {
+    u32x4 v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = min(base + tid + j * kGemvThreads, tot - 1);
+      const int t = i / row_u4;
+      v[j] = reinterpret_cast<const u32x4*>(src_row(t))[i - t * row_u4];
+    }
+    // stores clamped like the loads (a clamped lane rewrites the last
+    // element with the value it holds), so every load is consumed on every
+    // path and no wait for it is left pending at a loop back edge
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = min(base + tid + j * kGemvThreads, tot - 1);
+      const int t = i / row_u4;
+      reinterpret_cast<u32x4*>(dst + t * dst_row_dw)[i - t * row_u4] = v[j];
+    }
+  };
+  batch(0);
+  for (int base = NB * kGemvThreads; base < tot; base += NB * kGemvThreads) batch(base);
+}
 
 // Streaming gate/up: workgroup = (work item, 64-row block of the expert's
-// intermediate dimension); 4 waves split the H/64 groups; token rows of x
-// (fp16 in the paired order) and their group sums are staged in LDS.
+// intermediate dimension); its waves split the H/64 groups; token rows of x
+// (fp16 in the paired order) and their group sums are staged in LDS.  The
+// item and its slots are scalar loads; the weight prefetch is issued before
+// the token rows are staged.
 template <bool LO>
-__global__ __launch_bounds__(256) void gemv_up_kernel(
+__global__ __launch_bounds__(kGemvThreads) void gemv_up_kernel(
     const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
     int H, int E, int k, int I, int Is, int T, const uint32_t* __restrict__ x16,
     const uint32_t* __restrict__ x16lo, const float* __restrict__ xs,
     const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
-    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int mt) {
+    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nrb, int mt) {
   extern __shared__ uint32_t dyn[];
-  __shared__ int s_tok[kGemvTok];
-  __shared__ int s_slot[kGemvTok];
   __shared__ float red[kGemvWaves][2][kGemvTokV2][64];
-  const int item_i = blockIdx.y;
-  if (item_i >= misc[kNGemv]) return;
-  const int4 it = items[item_i];
-  const int e = it.x, m = it.y, loff = it.z;
+  int item_i, rb;
+  if (!gemv_work(misc, nsh, nrb, item_i, rb)) return;
+  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
+  const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
   const bool sh = e == E;
   const int inter = sh ? Is : I;
-  const int rb = blockIdx.x;
   if (rb * 64 >= inter) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H >> 6, Tk = T * k;
@@ -752,37 +818,37 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(
   st.gbeg = (G * wave) / kGemvWaves;
   st.gend = (G * (wave + 1)) / kGemvWaves;
   st.lane = lane;
+  const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
 
   const bool busy = st.gbeg < st.gend;
   for (int p0 = 0; p0 < m; p0 += mt) {
     const int nt = min(mt, m - p0);
     if (p0 > 0) __syncthreads();
-    // weights first: they depend only on the work item, so their loads are in
-    // flight while the token rows are looked up and staged
     if (busy) st.prefetch();
-    if (tid < nt) {
-      const int slot = slots[loff + p0 + tid];
-      s_slot[tid] = slot;
-      s_tok[tid] = slot < Tk ? slot / k : slot - Tk;
-    }
-    __syncthreads();
-    // stage x rows (hi, then lo for fp32 input) and group sums
-    const int hq = H >> 3;   // uint4 per half-row
-    for (int i = tid; i < nt * hq; i += 256) {
-      const int t = i / hq, c = i - t * hq;
-      reinterpret_cast<uint4*>(xl + t * xrow)[c] =
-          reinterpret_cast<const uint4*>(x16 + (size_t)s_tok[t] * (H >> 1))[c];
-    }
+    Four slot, tok;
+    slot.v0 = (int)sl[loff + p0];
+    slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
+    slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
+    slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
+    tok.v0 = slot.v0 < Tk ? slot.v0 / k : slot.v0 - Tk;
+    tok.v1 = slot.v1 < Tk ? slot.v1 / k : slot.v1 - Tk;
+    tok.v2 = slot.v2 < Tk ? slot.v2 / k : slot.v2 - Tk;
+    tok.v3 = slot.v3 < Tk ? slot.v3 / k : slot.v3 - Tk;
+    // group sums: the first kGemvThreads entries are loaded with the rows
+    const int nxs = nt * G;
+    const int i0 = min(tid, nxs - 1);
+    const float xs0 = xs[(size_t)tok[i0 / G] * G + (i0 % G)];
+    const int hdw = H >> 1;
+    stage_rows(xl, xrow, nt, H >> 3, [=](int t) {
+      return reinterpret_cast<const uint4*>(x16 + (size_t)tok[t] * hdw);
+    });
     if (LO)
-      for (int i = tid; i < nt * hq; i += 256) {
-        const int t = i / hq, c = i - t * hq;
-        reinterpret_cast<uint4*>(xl + t * xrow + (H >> 1))[c] =
-            reinterpret_cast<const uint4*>(x16lo + (size_t)s_tok[t] * (H >> 1))[c];
-      }
-    for (int i = tid; i < nt * G; i += 256) {
-      const int t = i / G, g = i - t * G;
-      xsl[i] = xs[(size_t)s_tok[t] * G + g];
-    }
+      stage_rows(xl + hdw, xrow, nt, H >> 3, [=](int t) {
+        return reinterpret_cast<const uint4*>(x16lo + (size_t)tok[t] * hdw);
+      });
+    xsl[i0] = xs0;
+    for (int i = tid + kGemvThreads; i < nxs; i += kGemvThreads)
+      xsl[i] = xs[(size_t)tok[i / G] * G + (i % G)];
     __syncthreads();
     float acc[2][kGemvTokV2];
 #pragma unroll
@@ -804,35 +870,32 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(
       }
       const float hv = gs / (1.f + expf(-gs)) * us;
       const _Float16 h16 = (_Float16)hv;
-      const int slot = s_slot[t];
+      const int sv = slot[t];
       const int col = rb * 64 + lane;
-      hbuf[h_off(slot, Tk, I, Is) + pair_pos4(col)] = f16bits(h16);
+      hbuf[h_off(sv, Tk, I, Is) + pair_pos4(col)] = f16bits(h16);
       const float hsum = wave_sum((float)h16);
-      if (lane == 0) hs[hs_off(slot, Tk, I, Is) + rb] = hsum;
+      if (lane == 0) hs[hs_off(sv, Tk, I, Is) + rb] = hsum;
     }
-    __syncthreads();
   }
 }
 
-// Streaming down: workgroup = (work item, 64-row block of H); 4 waves split
+// Streaming down: workgroup = (work item, 64-row block of H); its waves split
 // the inter/64 groups; the slots' h rows (fp16, paired order) and their group
 // sums are staged in LDS.  Writes one fp32 row per slot.
-__global__ __launch_bounds__(256) void gemv_down_kernel(
+__global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(
     const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
     int H, int E, int k, int I, int Is, int T, const int4* __restrict__ items,
     const int* __restrict__ misc, const int* __restrict__ slots,
     const uint32_t* __restrict__ hbuf32, const float* __restrict__ hs,
-    float* __restrict__ yslot, int mt) {
+    float* __restrict__ yslot, int nsh, int nrb, int mt) {
   extern __shared__ uint32_t dyn[];
-  __shared__ int s_slot[kGemvTok];
   __shared__ float red[kGemvWaves][kGemvTokV2][64];
-  const int item_i = blockIdx.y;
-  if (item_i >= misc[kNGemv]) return;
-  const int4 it = items[item_i];
-  const int e = it.x, m = it.y, loff = it.z;
+  int item_i, rb;
+  if (!gemv_work(misc, nsh, nrb, item_i, rb)) return;
+  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
+  const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
   const bool sh = e == E;
   const int inter = sh ? Is : I;
-  const int rb = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H >> 6, G2 = inter >> 6, Tk = T * k;
   const int hrow = inter >> 1;
@@ -845,24 +908,27 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
   st.gbeg = (G2 * wave) / kGemvWaves;
   st.gend = (G2 * (wave + 1)) / kGemvWaves;
   st.lane = lane;
+  const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
 
   const bool busy = st.gbeg < st.gend;
   for (int p0 = 0; p0 < m; p0 += mt) {
     const int nt = min(mt, m - p0);
     if (p0 > 0) __syncthreads();
     if (busy) st.prefetch();
-    if (tid < nt) s_slot[tid] = slots[loff + p0 + tid];
-    __syncthreads();
-    const int hq = inter >> 3;
-    for (int i = tid; i < nt * hq; i += 256) {
-      const int t = i / hq, c = i - t * hq;
-      reinterpret_cast<uint4*>(hl + t * hrow)[c] =
-          reinterpret_cast<const uint4*>(hbuf32 + (h_off(s_slot[t], Tk, I, Is) >> 1))[c];
-    }
-    for (int i = tid; i < nt * G2; i += 256) {
-      const int t = i / G2, g = i - t * G2;
-      hsl[i] = hs[hs_off(s_slot[t], Tk, I, Is) + g];
-    }
+    Four slot;
+    slot.v0 = (int)sl[loff + p0];
+    slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
+    slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
+    slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
+    const int nhs = nt * G2;
+    const int i0 = min(tid, nhs - 1);
+    const float hs0 = hs[hs_off(slot[i0 / G2], Tk, I, Is) + (i0 % G2)];
+    stage_rows(hl, hrow, nt, inter >> 3, [=](int t) {
+      return reinterpret_cast<const uint4*>(hbuf32 + (h_off(slot[t], Tk, I, Is) >> 1));
+    });
+    hsl[i0] = hs0;
+    for (int i = tid + kGemvThreads; i < nhs; i += kGemvThreads)
+      hsl[i] = hs[hs_off(slot[i / G2], Tk, I, Is) + (i % G2)];
     __syncthreads();
     float acc[1][kGemvTokV2];
 #pragma unroll
@@ -876,9 +942,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < kGemvWaves; ++w) v += red[w][t][lane];
-      yslot[(size_t)s_slot[t] * H + rb * 64 + lane] = v;
+      yslot[(size_t)slot[t] * H + rb * 64 + lane] = v;
     }
-    __syncthreads();
   }
 }
 
@@ -1460,19 +1525,28 @@ static ExpertPtrs expert_ptrs(const LayerDev& d, int T) {
   return p;
 }
 
+// The shared expert streams when the batch is below the matrix-core threshold
+// (the bucketing pass then appends it as the last streaming item).
+static bool shared_streams(const LayerDev& d, int T) { return d.has_shared && T < d.mfma_min_rows; }
+static int routed_stream_items(const LayerDev& d, int T) {
+  const int Tk = T * d.k;
+  return Tk < d.E ? Tk : d.E;
+}
+
 hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
-  const int imax = d.Is > d.I ? d.Is : d.I;
   const int mt = gemv_tokens_per_pass(d, T);
   const size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + d.H / 64) * 4;
+  const int nsh = shared_streams(d, T) ? d.Is / 64 : 0, nrb = d.I / 64;
+  const dim3 grid(nsh + routed_stream_items(d, T) * nrb);
   if (x_f32)
-    hipLaunchKernelGGL((gemv_up_kernel<true>), dim3(imax / 64, p.ni), dim3(256), lds, s, d.bank,
+    hipLaunchKernelGGL((gemv_up_kernel<true>), grid, dim3(kGemvThreads), lds, s, d.bank,
                        d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs,
-                       p.items, p.misc, p.slots, p.hbuf, p.hs, mt);
+                       p.items, p.misc, p.slots, p.hbuf, p.hs, nsh, nrb, mt);
   else
-    hipLaunchKernelGGL((gemv_up_kernel<false>), dim3(imax / 64, p.ni), dim3(256), lds, s, d.bank,
+    hipLaunchKernelGGL((gemv_up_kernel<false>), grid, dim3(kGemvThreads), lds, s, d.bank,
                        d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs,
-                       p.items, p.misc, p.slots, p.hbuf, p.hs, mt);
+                       p.items, p.misc, p.slots, p.hbuf, p.hs, nsh, nrb, mt);
   return hipGetLastError();
 }
 
@@ -1481,9 +1555,11 @@ hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
   const int mt = gemv_tokens_per_pass(d, T);
   const int imax = d.Is > d.I ? d.Is : d.I;
   const size_t lds = (size_t)mt * (imax / 2 + imax / 64) * 4;
-  hipLaunchKernelGGL(gemv_down_kernel, dim3(d.H / 64, p.ni), dim3(256), lds, s, d.bank, d.stride,
+  const int nrb = d.H / 64, nsh = shared_streams(d, T) ? nrb : 0;
+  const dim3 grid(nsh + routed_stream_items(d, T) * nrb);
+  hipLaunchKernelGGL(gemv_down_kernel, grid, dim3(kGemvThreads), lds, s, d.bank, d.stride,
                      d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.items, p.misc, p.slots,
-                     reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, mt);
+                     reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, nsh, nrb, mt);
   return hipGetLastError();
 }
 
