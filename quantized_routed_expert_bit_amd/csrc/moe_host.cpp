@@ -40,12 +40,14 @@ namespace qreb {
 
 int router_ksplit(int hidden) { return (hidden / kGroup + kRouterGPW - 1) / kRouterGPW; }
 
-// Tokens per router workgroup: all of a decode batch when it fits (then one
-// workgroup finishes top-k and bucketing without a second hand-off), bounded
-// so the token block's logits fit the workgroup's LDS (tokens * Epad <= 4096).
+// Tokens per router GEMV workgroup: at most kRouterTokMax, and at most
+// 4096 / Epad (the top-k pass holds a token block's logits in LDS).
 int router_tok_block(int n_tokens, int e_pad) {
   int tb = 4096 / e_pad;
   if (tb > kRouterTokMax) tb = kRouterTokMax;
+  // decode-sized batches: 4 tokens per workgroup, for more workgroups on the
+  // router weights (each re-reads them from cache)
+  if (n_tokens <= 64 && tb > 4) tb = 4;
   if (tb < 1) tb = 1;
   return n_tokens < tb ? n_tokens : tb;
 }
@@ -70,7 +72,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.logits = take(0);
   L.x16 = take(T * H * 2);
   L.x16lo = take(T * H * 2);
-  L.xs = take(T * G * 4);
+  L.xs = take(T * G * 8);
   L.ids = take(Tk * 4);
   L.p = take(Tk * 4);
   L.rank = take(Tk * 4);
@@ -90,7 +92,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.ntiles = take(((Tk + kNarrowBM - 1) / kNarrowBM + E + (T + kNarrowBM - 1) / kNarrowBM + 1) * 8);
   L.pred = take(Tk * 4);
   L.hbuf = take((Tk * I + Ts * Is) * 2);
-  L.hs = take((Tk * (I / 64) + Ts * (Is / 64)) * 4);
+  L.hs = take((Tk * (I / 64) + Ts * (Is / 64)) * 8);
   L.yslot = take((Tk + Ts) * H * 4);
   L.xn = take((c.flags & MOE_F_RMSNORM) ? T * H * 4 : 0);
   L.total = o;
@@ -346,7 +348,9 @@ int moe_profile_start(moe_ctx* ctx, int32_t max_calls) {
   prof_clear(ctx);
   ctx->ev.resize((size_t)max_calls * MOE_PROFILE_SLOTS * 2);
   for (auto& e : ctx->ev) {
-    hipError_t r = hipEventCreate(&e);
+    // timing-only events: no system-scope fence (cache writeback and
+    // invalidation) around the kernel they bracket
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
     if (r != hipSuccess) {
       e = nullptr;
       prof_clear(ctx);

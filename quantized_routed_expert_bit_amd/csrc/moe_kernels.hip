@@ -58,6 +58,12 @@ struct Lift {
     asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w >> (4 * p)), "s"(0x000F000Fu), "v"(magic));
     return r;
   }
+  // 4-bit, nibbles 1 and 5 in place: the fp16 pair (1024 + 16 q[8d+1], 1024 + 16 q[8d+5]).
+  __device__ __forceinline__ uint32_t q4x16(uint32_t w) const {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(0x00F000F0u), "v"(magic));
+    return r;
+  }
   // 8-bit: dword holds columns 4d..4d+3; pair p = (1024 + q[4d+p], 1024 + q[4d+p+2]).
   __device__ __forceinline__ uint32_t q8(uint32_t w, int p) const {
     uint32_t r;
@@ -75,6 +81,22 @@ __device__ __forceinline__ uint32_t ld4(const uint8_t* p) {
   return *reinterpret_cast<const uint32_t*>(p);
 }
 
+// Streaming unpack of one 16-byte 4-bit piece (32 columns) into 16 fp16
+// pairs with one shift per dword: pairs 0 and 2 of a dword are
+// (1024 + q, 1024 + q); pairs 1 and 3 (the odd columns) are taken in place
+// from bits 4..7 of each byte half, i.e. (1024 + 16q, 1024 + 16q).  The
+// activations of the odd columns are staged divided by 16 to match.
+__device__ __forceinline__ void unpack16_q4s(const Lift& L, uint4 c, uint32_t* w) {
+  const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t d8 = d[i] >> 8;
+    w[i * 4 + 0] = L.q4(d[i], 0);
+    w[i * 4 + 1] = L.q4x16(d[i]);
+    w[i * 4 + 2] = L.q4(d8, 0);
+    w[i * 4 + 3] = L.q4x16(d8);
+  }
+}
 // Unpack one 16-byte 4-bit piece (32 columns) into 16 fp16 pairs.
 __device__ __forceinline__ void unpack16_q4(const Lift& L, uint4 c, uint32_t* w) {
   const uint32_t d[4] = {c.x, c.y, c.z, c.w};
@@ -128,6 +150,14 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   x += dpp_i<0x142, 0xA>(0, x);
   x += dpp_i<0x143, 0xC>(0, x);
   return x;
+}
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets it.
+__device__ __forceinline__ float sum8_lanes(float v) {
+  v += __builtin_bit_cast(float, dpp_i<0xB1, 0xF>(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp_i<0x4E, 0xF>(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp_i<0x141, 0xF>(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v)));
+  return v;
 }
 
 // Exclusive scan of n ints held in LDS (n <= 256 * 8), by a 256-thread block.
@@ -365,6 +395,10 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouterArgs a) {
           }
         }
         uint16_t hi[8], lo[8], hi4[8], lo4[8];
+        // group sums of this chunk: the router's own (hi + lo), and for the
+        // streaming path S1 over what it stages (the hi part, + lo for fp32
+        // input; odd columns divided by 16) and S2 over the values those stand for
+        float sum = 0.f, s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const _Float16 h = (_Float16)v[q];
@@ -373,6 +407,27 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouterArgs a) {
           lo[pair_pos8(q)] = lb;
           hi4[pair_pos4(q)] = hb;
           lo4[pair_pos4(q)] = lb;
+          const float vh = f16f(hb), vl = f16f(lb);
+          sum += vh + vl;
+          if (q & 1) {
+            const float sh = f16f(f16bits((_Float16)(vh * 0.0625f)));
+            const float sl = a.x_f32 ? f16f(f16bits((_Float16)(vl * 0.0625f))) : 0.f;
+            s1 += sh + sl;
+            s2 += 16.f * (sh + sl);
+          } else {
+            const float e = vh + (a.x_f32 ? vl : 0.f);
+            s1 += e;
+            s2 += e;
+          }
+        }
+        // the 8 chunks of a group sit in 8 consecutive lanes (aligned)
+        sum = sum8_lanes(sum);
+        s1 = sum8_lanes(s1);
+        s2 = sum8_lanes(s2);
+        if ((tid & 7) == 0) {
+          xsum[t * kRouterGPW + gl] = sum;
+          if (wx)
+            reinterpret_cast<float2*>(a.xs)[(size_t)(t0 + t) * a.G + g0 + gl] = make_float2(s1, s2);
         }
         uint16_t* dh = xr + (t * kRouterGPW + gl) * 64 + c8;
         uint16_t* dl = xrl + (t * kRouterGPW + gl) * 64 + c8;
@@ -385,16 +440,6 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouterArgs a) {
         }
       }
     }
-  }
-  __syncthreads();
-  if (tid < nt * ng) {
-    const int t = tid / ng, gl = tid - t * ng;
-    const uint16_t* xh = xr + (t * kRouterGPW + gl) * 64;
-    const uint16_t* xq = xrl + (t * kRouterGPW + gl) * 64;
-    float sum = 0.f;
-    for (int q = 0; q < 64; ++q) sum += f16f(xh[q]) + f16f(xq[q]);
-    xsum[t * kRouterGPW + gl] = sum;
-    if (wx) a.xs[(size_t)(t0 + t) * a.G + g0 + gl] = sum;
   }
   __syncthreads();
 
@@ -634,9 +679,12 @@ __device__ __forceinline__ size_t hs_off(int slot, int Tk, int I, int Is) {
 // up, or down) over the groups [gbeg, gend) of one 64-row block, for nt <= MT
 // token rows held in LDS.  Weight tiles are loaded P groups ahead, so P*NMAT
 // 2.3 KB tiles per wave are in flight while earlier ones are consumed.
-// acc[m][t] += sum over the groups of (s * dot(x, 1024 + q) + (b - 1024 s) * sum(x)).
+// The staged activations x~ hold the odd columns divided by 16 and the lifted
+// codes of those columns are 1024 + 16q, so dot(x~, lifted) = 1024 S1 + sum(q x)
+// with S1 = sum(x~) and S2 = sum(x) (both per group, in xsl):
+// acc[m][t] += sum over the groups of (s * dot - 1024 s * S1 + b * S2).
 // With LO, each staged row holds fp16 hi halves then lo halves (fp32 input);
-// both enter the same dot product, and xsl already sums hi + lo.
+// both enter the same dot product, and the sums cover hi + lo.
 template <int NMAT, int P>
 struct GemvStream {
   const uint8_t* mat[NMAT];
@@ -662,7 +710,7 @@ struct GemvStream {
     for (int p = 0; p < P; ++p) load(p, min(gbeg + p, gend - 1));
   }
   template <int MT, bool LO>
-  __device__ __forceinline__ void run(const uint32_t* xl, int xrow_dw, int lo_dw, const float* xsl,
+  __device__ __forceinline__ void run(const uint32_t* xl, int xrow_dw, int lo_dw, const float2* xsl,
                                       int G, int nt, float (&acc)[NMAT][MT]) {
     const Lift L;
     for (int g0 = gbeg; g0 < gend; g0 += P) {
@@ -671,13 +719,14 @@ struct GemvStream {
         const int g = g0 + p;
         {
           uint32_t w[NMAT][32];
-          float s[NMAT], cf[NMAT];
+          float s[NMAT], bb[NMAT], cf[NMAT];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) {
-            unpack16_q4(L, c0[p][m], w[m]);
-            unpack16_q4(L, c1[p][m], w[m] + 16);
+            unpack16_q4s(L, c0[p][m], w[m]);
+            unpack16_q4s(L, c1[p][m], w[m] + 16);
             s[m] = f16f(sb[p][m] & 0xffffu);
-            cf[m] = fmaf(-1024.f, s[m], f16f(sb[p][m] >> 16));
+            bb[m] = f16f(sb[p][m] >> 16);
+            cf[m] = -1024.f * s[m];
           }
           load(p, min(g + P, gend - 1));
           if (g < gend) {
@@ -703,9 +752,10 @@ struct GemvStream {
                   }
                 }
               }
-              const float xsv = xsl[t * G + g];
+              const float2 xsv = xsl[t * G + g];
 #pragma unroll
-              for (int m = 0; m < NMAT; ++m) acc[m][t] += fmaf(s[m], d[m], cf[m] * xsv);
+              for (int m = 0; m < NMAT; ++m)
+                acc[m][t] += fmaf(s[m], d[m], fmaf(bb[m], xsv.y, cf[m] * xsv.x));
             }
           }
           }
@@ -751,7 +801,9 @@ struct Four {
 // batch costs one memory round trip.
 // src_row(t) must be a value-capturing callable (no arrays captured by
 // reference: they would live in scratch memory).
-template <typename SrcRow>
+// With ODD16, the odd columns (dwords 1 and 3 of each 4-dword chunk in the
+// paired order) are divided by 16 on the way (fp16, rounded once).
+template <bool ODD16, typename SrcRow>
 __device__ __forceinline__ void stage_rows(uint32_t* dst, int dst_row_dw, int nt, int row_u4,
                                            const SrcRow& src_row) {
   // (a native vector type: an array of HIP's uint4 is not split into
@@ -777,6 +829,14 @@ __device__ __forceinline__ void stage_rows(uint32_t* dst, int dst_row_dw, int nt
     for (int j = 0; j < NB; ++j) {
       const int i = min(base + tid + j * kGemvThreads, tot - 1);
       const int t = i / row_u4;
+      if (ODD16) {
+        // (elements copied to scalars first: __builtin_bit_cast of a vector
+        // element expression reads the vector's first element)
+        const f16x2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const uint32_t ey = v[j].y, ew = v[j].w;
+        v[j].y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ey) * k16);
+        v[j].w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ew) * k16);
+      }
       reinterpret_cast<u32x4*>(dst + t * dst_row_dw)[i - t * row_u4] = v[j];
     }
   };
@@ -789,7 +849,7 @@ __device__ __forceinline__ void stage_rows(uint32_t* dst, int dst_row_dw, int nt
 // (fp16 in the paired order) and their group sums are staged in LDS.  The
 // item and its slots are scalar loads; the weight prefetch is issued before
 // the token rows are staged.
-template <bool LO>
+template <bool LO, bool SPLIT>
 __global__ __launch_bounds__(kGemvThreads) void gemv_up_kernel(
     const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
     int H, int E, int k, int I, int Is, int T, const uint32_t* __restrict__ x16,
@@ -797,7 +857,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_up_kernel(
     const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
     uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nrb, int mt) {
   extern __shared__ uint32_t dyn[];
-  __shared__ float red[kGemvWaves][2][kGemvTokV2][64];
+  __shared__ float red[SPLIT ? 1 : 2][kGemvWaves][kGemvTokV2][64];
   int item_i, rb;
   if (!gemv_work(misc, nsh, nrb, item_i, rb)) return;
   const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
@@ -809,14 +869,20 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_up_kernel(
   const int G = H >> 6, Tk = T * k;
   const int xrow = LO ? H : H >> 1;               // dwords per staged row (hi [+ lo])
   uint32_t* xl = dyn;                              // [mt][xrow]
-  float* xsl = reinterpret_cast<float*>(dyn + mt * xrow);   // [mt][G]
+  float2* xsl = reinterpret_cast<float2*>(dyn + mt * xrow);   // [mt][G] (S1, S2)
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
   const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
-  GemvStream<2, kGemvP> st;
-  st.mat[0] = rec + kHeaderBytes + (size_t)rb * G * kQ4TileBytes;
-  st.mat[1] = st.mat[0] + sec;
-  st.gbeg = (G * wave) / kGemvWaves;
-  st.gend = (G * (wave + 1)) / kGemvWaves;
+  // SPLIT: the first half of the waves streams the gate matrix, the second
+  // half the up matrix (fewer registers per wave, more workgroups per CU);
+  // else every wave streams both.  The waves of a matrix split the groups.
+  constexpr int NM = SPLIT ? 1 : 2;
+  constexpr int WPM = SPLIT ? kGemvWaves / 2 : kGemvWaves;
+  const int mat = SPLIT ? wave / WPM : 0, wq = wave - mat * WPM;
+  GemvStream<NM, kGemvP> st;
+  st.mat[0] = rec + kHeaderBytes + (size_t)mat * sec + (size_t)rb * G * kQ4TileBytes;
+  if (!SPLIT) st.mat[NM - 1] = st.mat[0] + sec;
+  st.gbeg = (G * wq) / WPM;
+  st.gend = (G * (wq + 1)) / WPM;
   st.lane = lane;
   const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
 
@@ -837,80 +903,96 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_up_kernel(
     // group sums: the first kGemvThreads entries are loaded with the rows
     const int nxs = nt * G;
     const int i0 = min(tid, nxs - 1);
-    const float xs0 = xs[(size_t)tok[i0 / G] * G + (i0 % G)];
+    const float2* xs2 = reinterpret_cast<const float2*>(xs);
+    const float2 xs0 = xs2[(size_t)tok[i0 / G] * G + (i0 % G)];
     const int hdw = H >> 1;
-    stage_rows(xl, xrow, nt, H >> 3, [=](int t) {
+    stage_rows<true>(xl, xrow, nt, H >> 3, [=](int t) {
       return reinterpret_cast<const uint4*>(x16 + (size_t)tok[t] * hdw);
     });
     if (LO)
-      stage_rows(xl + hdw, xrow, nt, H >> 3, [=](int t) {
+      stage_rows<true>(xl + hdw, xrow, nt, H >> 3, [=](int t) {
         return reinterpret_cast<const uint4*>(x16lo + (size_t)tok[t] * hdw);
       });
     xsl[i0] = xs0;
     for (int i = tid + kGemvThreads; i < nxs; i += kGemvThreads)
-      xsl[i] = xs[(size_t)tok[i / G] * G + (i % G)];
+      xsl[i] = xs2[(size_t)tok[i / G] * G + (i % G)];
     __syncthreads();
-    float acc[2][kGemvTokV2];
-#pragma unroll
-    for (int t = 0; t < kGemvTokV2; ++t) acc[0][t] = acc[1][t] = 0.f;
-    if (busy) st.run<kGemvTokV2, LO>(xl, xrow, H >> 1, xsl, G, nt, acc);
+    float acc[NM][kGemvTokV2];
 #pragma unroll
     for (int t = 0; t < kGemvTokV2; ++t)
-      if (t < nt) {
-        red[wave][0][t][lane] = acc[0][t];
-        red[wave][1][t][lane] = acc[1][t];
-      }
+#pragma unroll
+      for (int q = 0; q < NM; ++q) acc[q][t] = 0.f;
+    if (busy) st.template run<kGemvTokV2, LO>(xl, xrow, H >> 1, xsl, G, nt, acc);
+#pragma unroll
+    for (int t = 0; t < kGemvTokV2; ++t)
+      if (t < nt)
+#pragma unroll
+        for (int q = 0; q < NM; ++q) red[q][wave][t][lane] = acc[q][t];
     __syncthreads();
     for (int t = wave; t < nt; t += kGemvWaves) {
       float gs = 0.f, us = 0.f;
 #pragma unroll
-      for (int w = 0; w < kGemvWaves; ++w) {
-        gs += red[w][0][t][lane];
-        us += red[w][1][t][lane];
+      for (int w = 0; w < WPM; ++w) {
+        gs += red[0][w][t][lane];
+        us += SPLIT ? red[0][WPM + w][t][lane] : red[NM - 1][w][t][lane];
       }
       const float hv = gs / (1.f + expf(-gs)) * us;
+      // h in fp16, odd columns stored divided by 16 (the streaming down
+      // pass stages them as they are); S1 sums what is stored, S2 the h
+      // those values stand for
       const _Float16 h16 = (_Float16)hv;
+      const bool odd = lane & 1;
+      const _Float16 hst = odd ? (_Float16)((float)h16 * 0.0625f) : h16;
       const int sv = slot[t];
       const int col = rb * 64 + lane;
-      hbuf[h_off(sv, Tk, I, Is) + pair_pos4(col)] = f16bits(h16);
-      const float hsum = wave_sum((float)h16);
-      if (lane == 0) hs[hs_off(sv, Tk, I, Is) + rb] = hsum;
+      hbuf[h_off(sv, Tk, I, Is) + pair_pos4(col)] = f16bits(hst);
+      const float s1 = wave_sum((float)hst);
+      const float s2 = wave_sum(odd ? 16.f * (float)hst : (float)hst);
+      if (lane == 0) reinterpret_cast<float2*>(hs)[hs_off(sv, Tk, I, Is) + rb] = make_float2(s1, s2);
     }
   }
 }
 
-// Streaming down: workgroup = (work item, 64-row block of H); its waves split
-// the inter/64 groups; the slots' h rows (fp16, paired order) and their group
-// sums are staged in LDS.  Writes one fp32 row per slot.
+// Streaming down: a workgroup owns one work item and rpw 64-row blocks of H
+// (the shared expert, whose K is the longest, one block; a routed expert rpu
+// blocks).  The waves of a row block split its inter/64 groups; the slots'
+// h rows (fp16, paired order) and their group sums are staged in LDS once per
+// workgroup.  Writes one fp32 row per slot.
 __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(
     const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
     int H, int E, int k, int I, int Is, int T, const int4* __restrict__ items,
     const int* __restrict__ misc, const int* __restrict__ slots,
     const uint32_t* __restrict__ hbuf32, const float* __restrict__ hs,
-    float* __restrict__ yslot, int nsh, int nrb, int mt) {
+    float* __restrict__ yslot, int nsh, int rpu, int mt) {
   extern __shared__ uint32_t dyn[];
   __shared__ float red[kGemvWaves][kGemvTokV2][64];
-  int item_i, rb;
-  if (!gemv_work(misc, nsh, nrb, item_i, rb)) return;
+  const int nrb = H >> 6;
+  const int nunits = (nrb + rpu - 1) / rpu;
+  int item_i, u;
+  if (!gemv_work(misc, nsh, nunits, item_i, u)) return;
   const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
   const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
   const bool sh = e == E;
   const int inter = sh ? Is : I;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rpw = sh ? 1 : rpu;                 // row blocks of this workgroup
+  const int wpr = kGemvWaves / rpw;             // waves per row block
+  const int rb0 = sh ? u : u * rpu;
+  const int rb = rb0 + wave / wpr, wq = wave - (wave / wpr) * wpr;
   const int G = H >> 6, G2 = inter >> 6, Tk = T * k;
   const int hrow = inter >> 1;
   uint32_t* hl = dyn;                                        // [mt][hrow]
-  float* hsl = reinterpret_cast<float*>(dyn + mt * hrow);    // [mt][G2]
+  float2* hsl = reinterpret_cast<float2*>(dyn + mt * hrow);    // [mt][G2] (S1, S2)
   const size_t sec = (size_t)G2 * G * kQ4TileBytes;
   const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
   GemvStream<1, kGemvP> st;
-  st.mat[0] = rec + kHeaderBytes + 2 * sec + (size_t)rb * G2 * kQ4TileBytes;
-  st.gbeg = (G2 * wave) / kGemvWaves;
-  st.gend = (G2 * (wave + 1)) / kGemvWaves;
+  st.mat[0] = rec + kHeaderBytes + 2 * sec + (size_t)min(rb, nrb - 1) * G2 * kQ4TileBytes;
+  st.gbeg = (G2 * wq) / wpr;
+  st.gend = (G2 * (wq + 1)) / wpr;
   st.lane = lane;
   const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
 
-  const bool busy = st.gbeg < st.gend;
+  const bool busy = st.gbeg < st.gend && rb < nrb;
   for (int p0 = 0; p0 < m; p0 += mt) {
     const int nt = min(mt, m - p0);
     if (p0 > 0) __syncthreads();
@@ -922,13 +1004,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(
     slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
     const int nhs = nt * G2;
     const int i0 = min(tid, nhs - 1);
-    const float hs0 = hs[hs_off(slot[i0 / G2], Tk, I, Is) + (i0 % G2)];
-    stage_rows(hl, hrow, nt, inter >> 3, [=](int t) {
+    const float2* hs2 = reinterpret_cast<const float2*>(hs);
+    const float2 hs0 = hs2[hs_off(slot[i0 / G2], Tk, I, Is) + (i0 % G2)];
+    stage_rows<false>(hl, hrow, nt, inter >> 3, [=](int t) {
       return reinterpret_cast<const uint4*>(hbuf32 + (h_off(slot[t], Tk, I, Is) >> 1));
     });
     hsl[i0] = hs0;
     for (int i = tid + kGemvThreads; i < nhs; i += kGemvThreads)
-      hsl[i] = hs[hs_off(slot[i / G2], Tk, I, Is) + (i % G2)];
+      hsl[i] = hs2[hs_off(slot[i / G2], Tk, I, Is) + (i % G2)];
     __syncthreads();
     float acc[1][kGemvTokV2];
 #pragma unroll
@@ -938,11 +1021,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(
     for (int t = 0; t < kGemvTokV2; ++t)
       if (t < nt) red[wave][t][lane] = acc[0][t];
     __syncthreads();
-    for (int t = wave; t < nt; t += kGemvWaves) {
+    // (row block, token) pairs over the waves; fixed-order sum over a block's waves
+    for (int pr = wave; pr < rpw * nt; pr += kGemvWaves) {
+      const int r = pr / nt, t = pr - r * nt;
       float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kGemvWaves; ++w) v += red[w][t][lane];
-      yslot[(size_t)slot[t] * H + rb * 64 + lane] = v;
+      for (int q = 0; q < wpr; ++q) v += red[r * wpr + q][t][lane];
+      if (rb0 + r < nrb) yslot[(size_t)slot[t] * H + (rb0 + r) * 64 + lane] = v;
     }
   }
 }
@@ -1503,7 +1587,8 @@ struct ExpertPtrs {
 // few enough that the staged rows fit 64 KB of LDS.
 static int gemv_tokens_per_pass(const LayerDev& d, int T) {
   const int imax = d.Is > d.I ? d.Is : d.I;
-  const int row_bytes = (d.H > imax ? d.H : imax) * 4;   // fp32 input: hi + lo halves
+  const int wmax = d.H > imax ? d.H : imax;
+  const int row_bytes = wmax * 4 + (wmax / 64) * 8;   // fp32 input: hi + lo halves, group sums
   int mt = kGemvTokV2;
   while (mt > 1 && mt * row_bytes > 56 * 1024) --mt;
   return T < mt ? T : mt;
@@ -1536,17 +1621,17 @@ static int routed_stream_items(const LayerDev& d, int T) {
 hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
-  const size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + d.H / 64) * 4;
+  const size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + 2 * (d.H / 64)) * 4;
   const int nsh = shared_streams(d, T) ? d.Is / 64 : 0, nrb = d.I / 64;
-  const dim3 grid(nsh + routed_stream_items(d, T) * nrb);
-  if (x_f32)
-    hipLaunchKernelGGL((gemv_up_kernel<true>), grid, dim3(kGemvThreads), lds, s, d.bank,
-                       d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs,
-                       p.items, p.misc, p.slots, p.hbuf, p.hs, nsh, nrb, mt);
-  else
-    hipLaunchKernelGGL((gemv_up_kernel<false>), grid, dim3(kGemvThreads), lds, s, d.bank,
-                       d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs,
-                       p.items, p.misc, p.slots, p.hbuf, p.hs, nsh, nrb, mt);
+  const int units = nsh + routed_stream_items(d, T) * nrb;
+  // many workgroups: one matrix per wave (more resident workgroups to hide
+  // each one's staging); few: both matrices per wave (shorter per-wave chain)
+  const bool split = units >= 1024;
+  auto* kern = x_f32 ? (split ? gemv_up_kernel<true, true> : gemv_up_kernel<true, false>)
+                     : (split ? gemv_up_kernel<false, true> : gemv_up_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3(units), dim3(kGemvThreads), lds, s, d.bank, d.stride, d.shared,
+                     d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs, p.items, p.misc, p.slots,
+                     p.hbuf, p.hs, nsh, nrb, mt);
   return hipGetLastError();
 }
 
@@ -1554,12 +1639,16 @@ hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
   const int imax = d.Is > d.I ? d.Is : d.I;
-  const size_t lds = (size_t)mt * (imax / 2 + imax / 64) * 4;
+  const size_t lds = (size_t)mt * (imax / 2 + 2 * (imax / 64)) * 4;
+  // routed experts: several row blocks per workgroup, one or two waves per
+  // block, so a workgroup's fixed costs cover more weights
   const int nrb = d.H / 64, nsh = shared_streams(d, T) ? nrb : 0;
-  const dim3 grid(nsh + routed_stream_items(d, T) * nrb);
+  const int G2 = d.I / 64;
+  const int rpu = G2 <= 24 ? kGemvWaves / 2 : 1;
+  const dim3 grid(nsh + routed_stream_items(d, T) * ((nrb + rpu - 1) / rpu));
   hipLaunchKernelGGL(gemv_down_kernel, grid, dim3(kGemvThreads), lds, s, d.bank, d.stride,
                      d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.items, p.misc, p.slots,
-                     reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, nsh, nrb, mt);
+                     reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, nsh, rpu, mt);
   return hipGetLastError();
 }
 
