@@ -38,6 +38,27 @@ def record_bytes(h, i):
     return 3 * h * i * 9 // 16
 
 
+def measured_traffic():
+    """HBM bytes per launch of the streaming gate/up kernel at this workload,
+    from the committed rocprofv3 FETCH_SIZE + WRITE_SIZE passes (calibrated
+    against a plain copy); None once the kernel sources differ from the ones
+    the counters were taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_up_decode_T16_hbm_traffic.md")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                      if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+        h = hashlib.sha256()
+        for f in ("moe_kernels.hip", "moe_internal.h"):
+            with open(os.path.join(ROOT, "quantized_routed_expert_bit_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != fields["source_sha256"].strip():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def build_layers(wl_index, n_copies, max_tokens, dev):
     import synth
     from quantized_routed_expert_bit_amd import MoELayer
@@ -256,7 +277,8 @@ def main():
                    "tokens_per_step": T, "layer_copies": args.copies, "launch": "hip_graph"},
         "roofline": {"bound": "hbm", "kernel": "gemv_up", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": int(up_bytes),
+                     "traffic": measured_traffic() if T == 16 else None,
+                     "bytes_per_launch": int(up_bytes),
                      "avg_launch_us": round(up_ms * 1e3, 3)},
         "layer_hbm": {"alg_bytes_per_step": int(layer_bytes),
                       "GB_s": round(layer_bytes / (res["ms_per_step"] * 1e-3) / 1e9, 1),
