@@ -1,24 +1,26 @@
 // HIP kernels (gfx950) of the routed-expert MoE layer.
 //
-// Layer definition and sources: include/moe.h.  Summary of the kernels:
-//   router_kernel   8-bit router GEMV -> fp32 partial logits per k-split; the
-//                   last workgroup of each token block sums them, adds the
-//                   logit bias and selects top-k with wave64 shuffles, then the
-//                   last token block buckets the (token, rank) slots by expert
-//                   and writes the work lists (one launch, no spinning).
-//   gemv_up_kernel  streaming expert path, gate and up: one lane per weight
-//                   row, 16-byte coalesced tile loads, nibbles unpacked in
-//                   registers, x read through the scalar cache; writes
-//                   h = SiLU(g) * u in fp16 and its per-64 group sums.
-//   gemv_down_kernel  the same for the down matrix; writes one fp32 row per
-//                   (token, expert) slot.
-//   combine_kernel  y[t] = sum_j p[t,j] y_slot[t,j] + y_shared[t] in fixed order.
+// Layer definition and record format: include/moe.h.  Kernels, in forward order:
+//   rmsnorm_kernel        optional per-token RMS normalization (stacked layers).
+//   router_gemv_kernel    8-bit router GEMV -> fp32 partial logits per k-split;
+//                         also writes x as fp16 (hi [+ lo]) and per-64 group sums.
+//   router_topk_kernel    sums the partials in fixed order, adds the logit bias,
+//                         top-k by (logit desc, index asc) with DPP reductions,
+//                         softmax over the k; buckets the slots when one
+//                         workgroup covers the batch (else bucket_kernel).
+//   gemv_up/down_kernel   streaming expert path (experts with few rows): one
+//                         lane per weight row, 16-byte tile loads, nibbles
+//                         lifted in registers, token rows staged in LDS.
+//   mfma_narrow_kernel    matrix-core path, 32-row tiles (a few tens of rows).
+//   mfma_wide_kernel      matrix-core path, 128-row tiles, LDS-DMA ring.
+//   combine_kernel        y[t] = [r +] sum_j p[t,j] y_slot[t,j] + y_shared[t].
 //
-// Dot products use v_dot2_f32_f16 on codes lifted to fp16 with the exponent
-// trick: (q | 0x6400) is the fp16 value 1024 + q exactly (q < 1024), so
+// The streaming dot products use v_dot2_f32_f16 on codes lifted to fp16 with
+// the exponent trick: (q | 0x6400) is the fp16 value 1024 + q exactly, so
 //     sum_k x_k (s q_k + b) = s * sum_k x_k (1024 + q_k) + (b - 1024 s) * sum_k x_k
-// with fp32 accumulation; the group sums sum_k x_k come from the same fp16
-// values that enter the dot products.
+// with fp32 accumulation (the 4-bit path folds this with two group sums, see
+// GemvStream).  The matrix-core paths dequantize to fp16 s*q + b (one rounding).
+
 #include "moe_internal.h"
 
 #include <math.h>
@@ -1033,20 +1035,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(
 
 // ------------------------------------------------------- matrix-core path --
 //
-// One workgroup = one 128-row tile of one expert's slot list x one column
-// block (gate/up: 128 intermediate columns; down: 256 output columns).  Each
-// of the 4 waves owns 32 gate+up columns (or 64 down columns), dequantizes its
-// weight rows to fp16 in registers (fp16(s*q + b), one rounding) and runs
-// v_mfma_f32_32x32x16_f16 against the gathered token rows, which the workgroup
-// stages once per 64-wide group in double-buffered LDS.  Within a group the
-// 64 k-values are taken in the paired order the fp16 activations are stored
-// in, so the MFMA slots of A and B line up without any shuffling: step ks of
-// lane half hi covers the codes of dword ks of 16-byte half hi of the row.
+// Weight rows are dequantized to fp16 in registers (fp16(s*q + b), one
+// rounding) and multiplied with the gathered token rows by
+// v_mfma_f32_32x32x16_f16.  Within a 64-wide group the k-values are taken in
+// the paired order the fp16 activations are stored in, so the MFMA slots of A
+// and B line up without any shuffling: step ks of lane half hi covers the
+// codes of dword ks of 16-byte half hi of the row.
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kALdsRow = 72;   // halfs per staged row: 64 + 8 of padding
 
 struct MfmaArgs {
   const uint8_t* bank;
@@ -1079,10 +1076,50 @@ __device__ __forceinline__ f16x8 dequant8(const Lift& L, uint32_t dw, f16x2 s2, 
   return r;
 }
 
+// ---- LDS DMA (global -> LDS without registers) ----
+// Each lane's 16 (or 4) bytes land at lds_base + lane * 16 (or 4): one wave
+// instruction fills a contiguous 1 KiB (256 B) block.  Issued through inline
+// assembly so the compiler neither waits for these loads on its own (the
+// kernel waits with explicit vmcnt counts) nor reorders LDS accesses across
+// them ("memory" clobber).
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"((uint32_t)(uintptr_t)lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"((uint32_t)(uintptr_t)lds_base) : "memory", "m0");
+}
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited on), N < 64
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+// workgroup barrier that orders LDS accesses in program order but adds no
+// memory-model wait of its own (the DMA waits above are explicit)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wide matrix-core kernel, for experts with >= wide_min_rows rows: one
+// workgroup = one 128-row tile x 128 gate+up columns (or 256 down columns);
+// wave w owns 32 (64) of the columns for all 128 rows (4 x 2 accumulators of
+// 32x32).  Per 64-wide K group, the token rows (A, fp16) and each wave's
+// weight codes and scales (B) are copied into a 3-stage LDS ring by LDS DMA
+// two groups ahead, so the only wait in the loop is one barrier per group.
+// A is stored unpadded with the 16-byte segments of row r XOR-swizzled by
+// (r & 7), so the MFMA operand reads (8 consecutive rows per 8 lanes) are
+// bank-conflict free.  B is dequantized in registers (fp16 s*q + b, one
+// rounding) one k-step at a time.
+constexpr int kWideA = kMfmaBM * 64;          // halfs per A plane per stage (16 KiB)
+constexpr int kWideB = kMfmaWaves * 2 * 512;  // halfs of B codes per stage (8 KiB)
+constexpr int kWideS = kMfmaWaves * 128;      // halfs of B scale/bias per stage (1 KiB)
+
 template <bool UP, bool LO>
-__global__ __launch_bounds__(256) void mfma_expert_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(256, 2) void mfma_wide_kernel(MfmaArgs a) {
   constexpr int NA = LO ? 2 : 1;
-  __shared__ __align__(16) uint16_t As[2][NA][kMfmaBM * kALdsRow];
+  constexpr int NST = 3;
+  constexpr int STAGE = NA * kWideA + kWideB + kWideS;    // halfs
+  __shared__ __align__(16) uint16_t ring[NST * STAGE];
   __shared__ int s_src[kMfmaBM];    // element offset of each row's A source
   __shared__ int s_slot[kMfmaBM];
   const int tile_i = blockIdx.y;
@@ -1110,28 +1147,46 @@ __global__ __launch_bounds__(256) void mfma_expert_kernel(MfmaArgs a) {
   }
   const uint8_t* rec = sh ? a.shared : a.bank + (size_t)e * a.stride;
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
-  const uint8_t* bb[2];
-  int brow[2];
+  // B sources of this lane: codes of (nb, hi, row) and, for the scale DMA,
+  // lanes 0-31 carry block 0's rows and lanes 32-63 block 1's
+  const uint8_t* bcode[2];
+  const uint8_t* bscale;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     // a wave past the last column still issues (unused) loads: point them at row 0
     const int r = won ? (UP ? n0 : n0 + nb * 32) : 0;
     const uint8_t* mat = rec + kHeaderBytes + (UP ? (nb ? sec : 0) : 2 * sec);
-    bb[nb] = mat + (size_t)(r >> 6) * Kg * kQ4TileBytes;
-    brow[nb] = (r & 63) + l32;
+    const uint8_t* blk = mat + (size_t)(r >> 6) * Kg * kQ4TileBytes;
+    bcode[nb] = blk + hi * 1024 + ((r & 63) + l32) * 16;
+    if (nb == hi) bscale = blk + kQ4CodeBytes + ((r & 63) + l32) * 4;
   }
   const uint16_t* asrc = UP ? a.x16 : a.hsrc;
   __syncthreads();
-
-  // A staging: 128 rows x 8 sixteen-byte segments per group = 4 per thread.
-  size_t a_off[4];
-  int a_lds[4];
+  // A sources: DMA instruction j of this wave fills rows (wave*4 + j)*8 ..
+  // +7; lane l writes row +l/8, physical segment l%8, which holds logical
+  // segment (l%8) ^ (row & 7)
+  const uint16_t* asj[4];
+  const uint16_t* asj_lo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int i = tid + 256 * j, r = i >> 3, sgm = i & 7;
-    a_off[j] = (size_t)s_src[r] + sgm * 8;
-    a_lds[j] = r * kALdsRow + sgm * 8;
+    const int row = (wave * 4 + j) * 8 + (lane >> 3);
+    const int lseg = (lane & 7) ^ (row & 7);
+    asj[j] = asrc + s_src[row] + lseg * 8;
+    asj_lo[j] = a.x16lo + s_src[row] + lseg * 8;
   }
+  auto issue = [&](int g, int stage) {
+    uint16_t* st = ring + stage * STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lds_dma16(asj[j] + g * 64, st + (wave * 4 + j) * 512);
+      if (LO) lds_dma16(asj_lo[j] + g * 64, st + kWideA + (wave * 4 + j) * 512);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      lds_dma16(bcode[nb] + (size_t)g * kQ4TileBytes, st + NA * kWideA + (wave * 2 + nb) * 512);
+    lds_dma4(bscale + (size_t)g * kQ4TileBytes, st + NA * kWideA + kWideB + wave * 128);
+  };
+  constexpr int kOps = 4 * NA + 3;   // DMA instructions per wave per group
   const Lift L;
   f32x16 acc[4][2];
 #pragma unroll
@@ -1142,96 +1197,58 @@ __global__ __launch_bounds__(256) void mfma_expert_kernel(MfmaArgs a) {
       for (int j = 0; j < 16; ++j) acc[mb][nb][j] = 0.f;
   const int nmb = (mrows + 31) >> 5;
 
-  // Weight fragments: a ring of PB groups loaded ahead.  Loads are never
-  // behind a branch (indexes past the end are clamped), so the compiler waits
-  // only for the ring entry it consumes; the group loop is padded to a
-  // multiple of PB and the padding iterations skip the math.
-  constexpr int PB = 4;
-  uint4 bc[PB][2];
-  uint32_t bs[PB][2];
+  issue(0, 0);
+  issue(min(1, Kg - 1), 1);
+  // the main loop, specialized on the number of 32-row blocks in the tile
+  auto run = [&](auto nmb_c) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    int cs = 0, ns = 2;                     // stage of group g, of group g + 2
+    for (int g = 0; g < Kg; ++g) {
+      wait_vmcnt<kOps>();                   // this wave's group-g copies are in LDS
+      lds_barrier();                        // ... and every wave's; group g-1 is consumed
+      issue(min(g + 2, Kg - 1), ns);
+      if (won) {
+        const uint16_t* st = ring + cs * STAGE;
+        const uint4* bq = reinterpret_cast<const uint4*>(st + NA * kWideA + wave * 1024);
+        const uint4 bc0 = bq[lane], bc1 = bq[64 + lane];
+        const uint32_t* sq = reinterpret_cast<const uint32_t*>(st + NA * kWideA + kWideB + wave * 128);
+        const uint32_t sb0 = sq[l32], sb1 = sq[32 + l32];
+        const uint32_t sv0 = sb0 & 0xffffu, bv0 = sb0 >> 16, sv1 = sb1 & 0xffffu, bv1 = sb1 >> 16;
+        const f16x2 s20 = __builtin_bit_cast(f16x2, sv0 | (sv0 << 16));
+        const f16x2 b20 = __builtin_bit_cast(f16x2, bv0 | (bv0 << 16));
+        const f16x2 s21 = __builtin_bit_cast(f16x2, sv1 | (sv1 << 16));
+        const f16x2 b21 = __builtin_bit_cast(f16x2, bv1 | (bv1 << 16));
+        const uint32_t c0[4] = {bc0.x, bc0.y, bc0.z, bc0.w};
+        const uint32_t c1[4] = {bc1.x, bc1.y, bc1.z, bc1.w};
+        const uint16_t* arow = st + l32 * 64;
 #pragma unroll
-  for (int q = 0; q < PB; ++q) {
-    const int gq = min(q, Kg - 1);
+        for (int ks = 0; ks < 4; ++ks) {
+          const f16x8 bf0 = dequant8(L, c0[ks], s20, b20);
+          const f16x8 bf1 = dequant8(L, c1[ks], s21, b21);
+          const int phys = (hi * 4 + ks) ^ (l32 & 7);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const uint8_t* t = bb[nb] + (size_t)gq * kQ4TileBytes;
-      bc[q][nb] = ld16(t + hi * 1024 + brow[nb] * 16);
-      bs[q][nb] = ld4(t + kQ4CodeBytes + brow[nb] * 4);
-    }
-  }
-  uint4 ar[4], al[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ar[j] = *reinterpret_cast<const uint4*>(asrc + a_off[j]);
-    if (LO) al[j] = *reinterpret_cast<const uint4*>(a.x16lo + a_off[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<uint4*>(&As[0][0][a_lds[j]]) = ar[j];
-    if (LO) *reinterpret_cast<uint4*>(&As[0][NA - 1][a_lds[j]]) = al[j];
-  }
-  __syncthreads();
-  const int Kp = (Kg + PB - 1) / PB * PB;
-  for (int g0 = 0; g0 < Kp; g0 += PB) {
-#pragma unroll
-    for (int q = 0; q < PB; ++q) {
-      const int g = g0 + q;
-      const int cur = q & 1;             // g0 is even, so this is g & 1
-      const int gn = min(g + 1, Kg - 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ar[j] = *reinterpret_cast<const uint4*>(asrc + a_off[j] + gn * 64);
-        if (LO) al[j] = *reinterpret_cast<const uint4*>(a.x16lo + a_off[j] + gn * 64);
-      }
-      if (won && g < Kg) {
-        f16x8 bf[2][4];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const uint32_t sv = bs[q][nb] & 0xffffu, bv = bs[q][nb] >> 16;
-          const f16x2 s2 = __builtin_bit_cast(f16x2, sv | (sv << 16));
-          const f16x2 b2 = __builtin_bit_cast(f16x2, bv | (bv << 16));
-          bf[nb][0] = dequant8(L, bc[q][nb].x, s2, b2);
-          bf[nb][1] = dequant8(L, bc[q][nb].y, s2, b2);
-          bf[nb][2] = dequant8(L, bc[q][nb].z, s2, b2);
-          bf[nb][3] = dequant8(L, bc[q][nb].w, s2, b2);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          if (mb < nmb) {
+          for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
             for (int qa = 0; qa < NA; ++qa) {
-              const uint16_t* arow = &As[cur][qa][(mb * 32 + l32) * kALdsRow + hi * 32];
-#pragma unroll
-              for (int ks = 0; ks < 4; ++ks) {
-                const f16x8 af = *reinterpret_cast<const f16x8*>(arow + ks * 8);
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                  acc[mb][nb] =
-                      __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nb][ks], acc[mb][nb], 0, 0, 0);
-              }
+              const f16x8 af =
+                  *reinterpret_cast<const f16x8*>(arow + qa * kWideA + mb * 32 * 64 + phys * 8);
+              acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf0, acc[mb][0], 0, 0, 0);
+              acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf1, acc[mb][1], 0, 0, 0);
             }
           }
         }
       }
-      {
-        const int gr = min(g + PB, Kg - 1);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const uint8_t* t = bb[nb] + (size_t)gr * kQ4TileBytes;
-          bc[q][nb] = ld16(t + hi * 1024 + brow[nb] * 16);
-          bs[q][nb] = ld4(t + kQ4CodeBytes + brow[nb] * 4);
-        }
-      }
-      if (g + 1 < Kg) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          *reinterpret_cast<uint4*>(&As[cur ^ 1][0][a_lds[j]]) = ar[j];
-          if (LO) *reinterpret_cast<uint4*>(&As[cur ^ 1][NA - 1][a_lds[j]]) = al[j];
-        }
-      }
-      __syncthreads();
+      cs = cs == NST - 1 ? 0 : cs + 1;
+      ns = ns == NST - 1 ? 0 : ns + 1;
     }
+  };
+  switch (nmb) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    default: run(std::integral_constant<int, 4>{}); break;
   }
+  wait_vmcnt<0>();                          // no copy may still target LDS at exit
   if (!won) return;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -1726,9 +1743,9 @@ hipError_t launch_mfma_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const MfmaArgs m = mfma_args(d, T);
   const dim3 grid((imax + 127) / 128, nt);
   if (x_f32)
-    hipLaunchKernelGGL((mfma_expert_kernel<true, true>), grid, dim3(256), 0, s, m);
+    hipLaunchKernelGGL((mfma_wide_kernel<true, true>), grid, dim3(256), 0, s, m);
   else
-    hipLaunchKernelGGL((mfma_expert_kernel<true, false>), grid, dim3(256), 0, s, m);
+    hipLaunchKernelGGL((mfma_wide_kernel<true, false>), grid, dim3(256), 0, s, m);
   return hipGetLastError();
 }
 
@@ -1736,7 +1753,7 @@ hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s) {
   const int nt = mfma_tiles_max(d, T);
   if (nt == 0) return hipSuccess;
   const MfmaArgs m = mfma_args(d, T);
-  hipLaunchKernelGGL((mfma_expert_kernel<false, false>), dim3((d.H + 255) / 256, nt), dim3(256), 0,
+  hipLaunchKernelGGL((mfma_wide_kernel<false, false>), dim3((d.H + 255) / 256, nt), dim3(256), 0,
                      s, m);
   return hipGetLastError();
 }
