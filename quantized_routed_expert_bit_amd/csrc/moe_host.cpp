@@ -161,7 +161,7 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
   d.rmsnorm = (cfg->flags & MOE_F_RMSNORM) ? 1 : 0;
   d.max_tokens = cfg->max_tokens;
   d.mfma_min_rows = 4;
-  d.wide_min_rows = 64;
+  d.wide_min_rows = 32;
   d.L = ws_layout(*cfg);
   if (hipSetDevice(cfg->device) != hipSuccess ||
       hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
