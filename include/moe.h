@@ -71,7 +71,8 @@
  * written or freed.  All device work of a call is ordered on the caller's
  * hipStream_t (passed as void*, NULL = the null stream): it starts after work
  * already enqueued there and finishes before work enqueued later.  Inside a
- * forward, the matrix-core kernels run on a stream the context owns, forked
+ * forward, the 128-row matrix-core kernels (batches with experts of 32+ rows)
+ * run on a stream the context owns, forked
  * from and joined back into the caller's stream with events (so a forward can
  * be captured into a HIP graph).  moe_forward performs no host synchronisation
  * and no allocation.  A context is not thread-safe and
@@ -186,14 +187,14 @@ int moe_set_path_rows(moe_ctx *ctx, int32_t mfma_min_rows, int32_t wide_min_rows
 /* Kernel timing (measurement aid).  moe_profile_start creates event pairs for
  * up to max_calls forwards; each later moe_forward on a stream that is not
  * being captured into a graph records one pair around each kernel it launches,
- * on the forward's stream.  moe_profile_read waits for the
+ * on the stream it runs on.  moe_profile_read waits for the
  * recorded events, writes the average milliseconds per launch of each kernel
  * slot into avg_ms[0 .. n_slots-1] (0 for a slot never launched) and the number
  * of profiled forwards into *n_calls, then stops profiling.  Slots:
- * 0 router+top-k+bucketing, 1 streaming gate/up, 2 streaming down,
+ * 0 router+top-k+bucketing, 1 gate/up launch of the streaming path (which
+ * also carries the 32-row matrix-core tiles), 2 down launch of the same,
  * 3 matrix-core gate/up (128-row tiles), 4 matrix-core down (128-row tiles),
- * 5 combine, 6 matrix-core gate/up (32-row tiles), 7 matrix-core down
- * (32-row tiles).
+ * 5 combine, 6 and 7 reserved (always 0).
  * Errors: MOE_EINVAL, MOE_EHIP. */
 #define MOE_PROFILE_SLOTS 8
 int moe_profile_start(moe_ctx *ctx, int32_t max_calls);

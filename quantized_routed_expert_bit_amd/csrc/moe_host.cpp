@@ -280,41 +280,25 @@ int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, 
   e = launch_router(d, xin, f32, n_tokens, 0, nullptr, ids_out, p_out, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "router launch");
   mark(0, 1, s);
-  // Matrix-core work (experts with many rows, and the shared expert at T >= 4)
-  // and streaming work touch disjoint slots: run them concurrently.
-  const bool mf = mfma_needed(d, n_tokens), nf = narrow_needed(d, n_tokens);
+  // Wide matrix-core work (experts with many rows) runs on the context's side
+  // stream, concurrently with the streaming launches, which also carry the
+  // narrow matrix-core tiles; the two touch disjoint slots.  Decode-sized
+  // batches need no wide work and so no fork or join.
+  const bool mf = mfma_needed(d, n_tokens);
   hipStream_t ms = s;
-  if (mf || nf) {
+  if (mf) {
     ms = ctx->side;
     if ((e = hipEventRecord(ctx->fork, s)) != hipSuccess ||
         (e = hipStreamWaitEvent(ms, ctx->fork, 0)) != hipSuccess)
       return hip_fail(ctx, e, "forking the matrix-core stream");
-  }
-  if (mf) {
     mark(3, 0, ms);
     e = launch_mfma_up(d, f32, n_tokens, ms);
     if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core gate/up launch");
     mark(3, 1, ms);
-  }
-  if (nf) {
-    mark(6, 0, ms);
-    e = launch_narrow_up(d, f32, n_tokens, ms);
-    if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core gate/up launch");
-    mark(6, 1, ms);
-  }
-  if (mf) {
     mark(4, 0, ms);
     e = launch_mfma_down(d, n_tokens, ms);
     if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core down launch");
     mark(4, 1, ms);
-  }
-  if (nf) {
-    mark(7, 0, ms);
-    e = launch_narrow_down(d, n_tokens, ms);
-    if (e != hipSuccess) return hip_fail(ctx, e, "narrow matrix-core down launch");
-    mark(7, 1, ms);
-  }
-  if (mf || nf) {
     if ((e = hipEventRecord(ctx->join, ms)) != hipSuccess)
       return hip_fail(ctx, e, "joining the matrix-core stream");
   }
@@ -331,7 +315,7 @@ int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, 
     e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
   }
-  if (mf || nf) {
+  if (mf) {
     if ((e = hipStreamWaitEvent(s, ctx->join, 0)) != hipSuccess)
       return hip_fail(ctx, e, "joining the matrix-core stream");
   }

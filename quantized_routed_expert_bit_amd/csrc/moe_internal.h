@@ -82,14 +82,12 @@ struct LayerDev {
 hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int mode,
                          float* logits_out, int32_t* ids_out, float* p_out,
                          hipStream_t s);
+// The streaming launches also run the narrow (32-row) matrix-core tiles.
 hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
 hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s);
 bool mfma_needed(const LayerDev& d, int T);
 hipError_t launch_mfma_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
 hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s);
-bool narrow_needed(const LayerDev& d, int T);
-hipError_t launch_narrow_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
-hipError_t launch_narrow_down(const LayerDev& d, int T, hipStream_t s);
 hipError_t launch_combine(const LayerDev& d, int T, const float* p, const float* residual, float* y,
                           hipStream_t s);
 hipError_t launch_ws_init(const LayerDev& d, hipStream_t s);

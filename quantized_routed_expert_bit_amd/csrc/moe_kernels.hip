@@ -789,269 +789,6 @@ struct GemvStream {
 
 constexpr int kGemvP = 2;   // groups in flight per wave
 
-// Which (work item, row block) a streaming workgroup owns.  The grid is flat:
-// the first nsh workgroups are the row blocks of the shared expert (the last
-// streaming item when it streams), started first because it is the largest;
-// then nrb row blocks per routed item.  Returns false for a workgroup past
-// the routed items of this forward.
-__device__ __forceinline__ bool gemv_work(const int* misc, int nsh, int nrb, int& item_i, int& rb) {
-  const int n_items = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNGemv];
-  const int b = blockIdx.x;
-  if (b < nsh) {
-    item_i = n_items - 1;
-    rb = b;
-    return item_i >= 0;
-  }
-  item_i = (b - nsh) / nrb;
-  rb = (b - nsh) - item_i * nrb;
-  return item_i < n_items - (nsh > 0 ? 1 : 0);
-}
-
-// Four wave-uniform values (one per token row of a streaming pass) selected
-// by a runtime row index without indexing a register array.
-static_assert(kGemvTokV2 == 4, "streaming passes hold four token rows");
-struct Four {
-  int v0, v1, v2, v3;
-  __device__ __forceinline__ int operator[](int i) const {
-    return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3;
-  }
-};
-
-// Stage nt rows of `row_u4` uint4 each into LDS (row t at dst + t * dst_row_dw
-// dwords) from src_row(t).  Each batch issues all its loads before the first
-// LDS write (every load unconditional, index clamped into the last row), so a
-// batch costs one memory round trip.
-// src_row(t) must be a value-capturing callable (no arrays captured by
-// reference: they would live in scratch memory).
-// With ODD16, the odd columns (dwords 1 and 3 of each 4-dword chunk in the
-// paired order) are divided by 16 on the way (fp16, rounded once).
-template <bool ODD16, typename SrcRow>
-__device__ __forceinline__ void stage_rows(uint32_t* dst, int dst_row_dw, int nt, int row_u4,
-                                           const SrcRow& src_row) {
-  // (a native vector type: an array of HIP's uint4 is not split into
-  // registers and would live in scratch memory)
-  // The first batch is straight-line code: inside a loop the compiler's
-  // waits for the registers the previous iteration loaded also wait for the
-  // weight loads issued before the staging.
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  constexpr int NB = 8;
-  const int tid = threadIdx.x, tot = nt * row_u4;
-  auto batch = [&](int base) {
-    u32x4 v[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int i = min(base + tid + j * kGemvThreads, tot - 1);
-      const int t = i / row_u4;
-      v[j] = reinterpret_cast<const u32x4*>(src_row(t))[i - t * row_u4];
-    }
-    // stores clamped like the loads (a clamped lane rewrites the last
-    // element with the value it holds), so every load is consumed on every
-    // path and no wait for it is left pending at a loop back edge
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int i = min(base + tid + j * kGemvThreads, tot - 1);
-      const int t = i / row_u4;
-      if (ODD16) {
-        // (elements copied to scalars first: __builtin_bit_cast of a vector
-        // element expression reads the vector's first element)
-        const f16x2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-        const uint32_t ey = v[j].y, ew = v[j].w;
-        v[j].y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ey) * k16);
-        v[j].w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ew) * k16);
-      }
-      reinterpret_cast<u32x4*>(dst + t * dst_row_dw)[i - t * row_u4] = v[j];
-    }
-  };
-  batch(0);
-  for (int base = NB * kGemvThreads; base < tot; base += NB * kGemvThreads) batch(base);
-}
-
-// Streaming gate/up: workgroup = (work item, 64-row block of the expert's
-// intermediate dimension); its waves split the H/64 groups; token rows of x
-// (fp16 in the paired order) and their group sums are staged in LDS.  The
-// item and its slots are scalar loads; the weight prefetch is issued before
-// the token rows are staged.
-template <bool LO, bool SPLIT>
-__global__ __launch_bounds__(kGemvThreads) void gemv_up_kernel(
-    const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
-    int H, int E, int k, int I, int Is, int T, const uint32_t* __restrict__ x16,
-    const uint32_t* __restrict__ x16lo, const float* __restrict__ xs,
-    const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
-    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nrb, int mt) {
-  extern __shared__ uint32_t dyn[];
-  __shared__ float red[SPLIT ? 1 : 2][kGemvWaves][kGemvTokV2][64];
-  int item_i, rb;
-  if (!gemv_work(misc, nsh, nrb, item_i, rb)) return;
-  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
-  const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
-  const bool sh = e == E;
-  const int inter = sh ? Is : I;
-  if (rb * 64 >= inter) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = H >> 6, Tk = T * k;
-  const int xrow = LO ? H : H >> 1;               // dwords per staged row (hi [+ lo])
-  uint32_t* xl = dyn;                              // [mt][xrow]
-  float2* xsl = reinterpret_cast<float2*>(dyn + mt * xrow);   // [mt][G] (S1, S2)
-  const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
-  const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
-  // SPLIT: the first half of the waves streams the gate matrix, the second
-  // half the up matrix (fewer registers per wave, more workgroups per CU);
-  // else every wave streams both.  The waves of a matrix split the groups.
-  constexpr int NM = SPLIT ? 1 : 2;
-  constexpr int WPM = SPLIT ? kGemvWaves / 2 : kGemvWaves;
-  const int mat = SPLIT ? wave / WPM : 0, wq = wave - mat * WPM;
-  GemvStream<NM, kGemvP> st;
-  st.mat[0] = rec + kHeaderBytes + (size_t)mat * sec + (size_t)rb * G * kQ4TileBytes;
-  if (!SPLIT) st.mat[NM - 1] = st.mat[0] + sec;
-  st.gbeg = (G * wq) / WPM;
-  st.gend = (G * (wq + 1)) / WPM;
-  st.lane = lane;
-  const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
-
-  const bool busy = st.gbeg < st.gend;
-  for (int p0 = 0; p0 < m; p0 += mt) {
-    const int nt = min(mt, m - p0);
-    if (p0 > 0) __syncthreads();
-    if (busy) st.prefetch();
-    Four slot, tok;
-    slot.v0 = (int)sl[loff + p0];
-    slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
-    slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
-    slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
-    tok.v0 = slot.v0 < Tk ? slot.v0 / k : slot.v0 - Tk;
-    tok.v1 = slot.v1 < Tk ? slot.v1 / k : slot.v1 - Tk;
-    tok.v2 = slot.v2 < Tk ? slot.v2 / k : slot.v2 - Tk;
-    tok.v3 = slot.v3 < Tk ? slot.v3 / k : slot.v3 - Tk;
-    // group sums: the first kGemvThreads entries are loaded with the rows
-    const int nxs = nt * G;
-    const int i0 = min(tid, nxs - 1);
-    const float2* xs2 = reinterpret_cast<const float2*>(xs);
-    const float2 xs0 = xs2[(size_t)tok[i0 / G] * G + (i0 % G)];
-    const int hdw = H >> 1;
-    stage_rows<true>(xl, xrow, nt, H >> 3, [=](int t) {
-      return reinterpret_cast<const uint4*>(x16 + (size_t)tok[t] * hdw);
-    });
-    if (LO)
-      stage_rows<true>(xl + hdw, xrow, nt, H >> 3, [=](int t) {
-        return reinterpret_cast<const uint4*>(x16lo + (size_t)tok[t] * hdw);
-      });
-    xsl[i0] = xs0;
-    for (int i = tid + kGemvThreads; i < nxs; i += kGemvThreads)
-      xsl[i] = xs2[(size_t)tok[i / G] * G + (i % G)];
-    __syncthreads();
-    float acc[NM][kGemvTokV2];
-#pragma unroll
-    for (int t = 0; t < kGemvTokV2; ++t)
-#pragma unroll
-      for (int q = 0; q < NM; ++q) acc[q][t] = 0.f;
-    if (busy) st.template run<kGemvTokV2, LO>(xl, xrow, H >> 1, xsl, G, nt, acc);
-#pragma unroll
-    for (int t = 0; t < kGemvTokV2; ++t)
-      if (t < nt)
-#pragma unroll
-        for (int q = 0; q < NM; ++q) red[q][wave][t][lane] = acc[q][t];
-    __syncthreads();
-    for (int t = wave; t < nt; t += kGemvWaves) {
-      float gs = 0.f, us = 0.f;
-#pragma unroll
-      for (int w = 0; w < WPM; ++w) {
-        gs += red[0][w][t][lane];
-        us += SPLIT ? red[0][WPM + w][t][lane] : red[NM - 1][w][t][lane];
-      }
-      const float hv = gs / (1.f + expf(-gs)) * us;
-      // h in fp16, odd columns stored divided by 16 (the streaming down
-      // pass stages them as they are); S1 sums what is stored, S2 the h
-      // those values stand for
-      const _Float16 h16 = (_Float16)hv;
-      const bool odd = lane & 1;
-      const _Float16 hst = odd ? (_Float16)((float)h16 * 0.0625f) : h16;
-      const int sv = slot[t];
-      const int col = rb * 64 + lane;
-      hbuf[h_off(sv, Tk, I, Is) + pair_pos4(col)] = f16bits(hst);
-      const float s1 = wave_sum((float)hst);
-      const float s2 = wave_sum(odd ? 16.f * (float)hst : (float)hst);
-      if (lane == 0) reinterpret_cast<float2*>(hs)[hs_off(sv, Tk, I, Is) + rb] = make_float2(s1, s2);
-    }
-  }
-}
-
-// Streaming down: a workgroup owns one work item and rpw 64-row blocks of H
-// (the shared expert, whose K is the longest, one block; a routed expert rpu
-// blocks).  The waves of a row block split its inter/64 groups; the slots'
-// h rows (fp16, paired order) and their group sums are staged in LDS once per
-// workgroup.  Writes one fp32 row per slot.
-__global__ __launch_bounds__(kGemvThreads) void gemv_down_kernel(
-    const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
-    int H, int E, int k, int I, int Is, int T, const int4* __restrict__ items,
-    const int* __restrict__ misc, const int* __restrict__ slots,
-    const uint32_t* __restrict__ hbuf32, const float* __restrict__ hs,
-    float* __restrict__ yslot, int nsh, int rpu, int mt) {
-  extern __shared__ uint32_t dyn[];
-  __shared__ float red[kGemvWaves][kGemvTokV2][64];
-  const int nrb = H >> 6;
-  const int nunits = (nrb + rpu - 1) / rpu;
-  int item_i, u;
-  if (!gemv_work(misc, nsh, nunits, item_i, u)) return;
-  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
-  const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
-  const bool sh = e == E;
-  const int inter = sh ? Is : I;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rpw = sh ? 1 : rpu;                 // row blocks of this workgroup
-  const int wpr = kGemvWaves / rpw;             // waves per row block
-  const int rb0 = sh ? u : u * rpu;
-  const int rb = rb0 + wave / wpr, wq = wave - (wave / wpr) * wpr;
-  const int G = H >> 6, G2 = inter >> 6, Tk = T * k;
-  const int hrow = inter >> 1;
-  uint32_t* hl = dyn;                                        // [mt][hrow]
-  float2* hsl = reinterpret_cast<float2*>(dyn + mt * hrow);    // [mt][G2] (S1, S2)
-  const size_t sec = (size_t)G2 * G * kQ4TileBytes;
-  const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
-  GemvStream<1, kGemvP> st;
-  st.mat[0] = rec + kHeaderBytes + 2 * sec + (size_t)min(rb, nrb - 1) * G2 * kQ4TileBytes;
-  st.gbeg = (G2 * wq) / wpr;
-  st.gend = (G2 * (wq + 1)) / wpr;
-  st.lane = lane;
-  const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
-
-  const bool busy = st.gbeg < st.gend && rb < nrb;
-  for (int p0 = 0; p0 < m; p0 += mt) {
-    const int nt = min(mt, m - p0);
-    if (p0 > 0) __syncthreads();
-    if (busy) st.prefetch();
-    Four slot;
-    slot.v0 = (int)sl[loff + p0];
-    slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
-    slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
-    slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
-    const int nhs = nt * G2;
-    const int i0 = min(tid, nhs - 1);
-    const float2* hs2 = reinterpret_cast<const float2*>(hs);
-    const float2 hs0 = hs2[hs_off(slot[i0 / G2], Tk, I, Is) + (i0 % G2)];
-    stage_rows<false>(hl, hrow, nt, inter >> 3, [=](int t) {
-      return reinterpret_cast<const uint4*>(hbuf32 + (h_off(slot[t], Tk, I, Is) >> 1));
-    });
-    hsl[i0] = hs0;
-    for (int i = tid + kGemvThreads; i < nhs; i += kGemvThreads)
-      hsl[i] = hs2[hs_off(slot[i / G2], Tk, I, Is) + (i % G2)];
-    __syncthreads();
-    float acc[1][kGemvTokV2];
-#pragma unroll
-    for (int t = 0; t < kGemvTokV2; ++t) acc[0][t] = 0.f;
-    if (busy) st.run<kGemvTokV2, false>(hl, hrow, 0, hsl, G2, nt, acc);
-#pragma unroll
-    for (int t = 0; t < kGemvTokV2; ++t)
-      if (t < nt) red[wave][t][lane] = acc[0][t];
-    __syncthreads();
-    // (row block, token) pairs over the waves; fixed-order sum over a block's waves
-    for (int pr = wave; pr < rpw * nt; pr += kGemvWaves) {
-      const int r = pr / nt, t = pr - r * nt;
-      float v = 0.f;
-      for (int q = 0; q < wpr; ++q) v += red[r * wpr + q][t][lane];
-      if (rb0 + r < nrb) yslot[(size_t)slot[t] * H + (rb0 + r) * 64 + lane] = v;
-    }
-  }
-}
 
 // ------------------------------------------------------- matrix-core path --
 //
@@ -1312,13 +1049,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
 // with a PN-deep register ring for both operands (A straight from global, no
 // LDS, no barriers in the loop) and the partial accumulators are summed across
 // waves in fixed order at the end.
+// The body works on tile tile_i, column block cblk, with red (32 KiB) and
+// s_slot (32 ints) in LDS; it is the narrow kernel below, and the first
+// workgroups of the streaming kernels run it too (one launch for both paths).
+typedef float NarrowRed[2][16][64];
 template <bool UP, bool LO>
-__global__ __launch_bounds__(256) void mfma_narrow_kernel(MfmaArgs a) {
-  constexpr int PN = 4;
+__device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int cblk,
+                                            NarrowRed* red, int* s_slot) {
+  constexpr int PN = 2;
   constexpr int NA = LO ? 2 : 1;
-  __shared__ float red[kMfmaWaves][2][16][64];
-  __shared__ int s_slot[32];
-  const int tile_i = blockIdx.y;
   if (tile_i >= a.misc[kNNarrow]) return;
   const int2 tl = a.ntiles[tile_i];
   const int4 it = a.mitems[tl.x];
@@ -1330,7 +1069,7 @@ __global__ __launch_bounds__(256) void mfma_narrow_kernel(MfmaArgs a) {
   const int Kg = UP ? G : inter >> 6;
   constexpr int CB = UP ? 32 : 64;
   const int ncols = UP ? inter : a.H;
-  const int n0 = blockIdx.x * CB;
+  const int n0 = cblk * CB;
   if (n0 >= ncols) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5, l32 = lane & 31;
@@ -1383,32 +1122,32 @@ __global__ __launch_bounds__(256) void mfma_narrow_kernel(MfmaArgs a) {
 #pragma unroll
       for (int q = 0; q < PN; ++q) {
         const int g = g0 + q;
-        f16x8 bf[2][4];
+        // dequantize one k-step at a time, consuming ring slot q in place;
+        // the slot is refilled after its math (few registers: this body
+        // also runs inside the streaming launches)
+        f16x2 s2[2], b2[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const uint32_t sv = rs[q][nb] & 0xffffu, bv = rs[q][nb] >> 16;
-          const f16x2 s2 = __builtin_bit_cast(f16x2, sv | (sv << 16));
-          const f16x2 b2 = __builtin_bit_cast(f16x2, bv | (bv << 16));
-          bf[nb][0] = dequant8(L, rb[q][nb].x, s2, b2);
-          bf[nb][1] = dequant8(L, rb[q][nb].y, s2, b2);
-          bf[nb][2] = dequant8(L, rb[q][nb].z, s2, b2);
-          bf[nb][3] = dequant8(L, rb[q][nb].w, s2, b2);
+          s2[nb] = __builtin_bit_cast(f16x2, sv | (sv << 16));
+          b2[nb] = __builtin_bit_cast(f16x2, bv | (bv << 16));
         }
-        f16x8 af[NA][4];
-#pragma unroll
-        for (int qa = 0; qa < NA; ++qa)
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) af[qa][ks] = __builtin_bit_cast(f16x8, ra[q][qa][ks]);
-        QREB_NARROW_LOAD(q, min(g + PN, gend - 1));
         if (g < gend) {
 #pragma unroll
-          for (int qa = 0; qa < NA; ++qa)
+          for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t c0 = ks == 0 ? rb[q][0].x : ks == 1 ? rb[q][0].y : ks == 2 ? rb[q][0].z : rb[q][0].w;
+            const uint32_t c1 = ks == 0 ? rb[q][1].x : ks == 1 ? rb[q][1].y : ks == 2 ? rb[q][1].z : rb[q][1].w;
+            const f16x8 bf0 = dequant8(L, c0, s2[0], b2[0]);
+            const f16x8 bf1 = dequant8(L, c1, s2[1], b2[1]);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-              for (int nb = 0; nb < 2; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[qa][ks], bf[nb][ks], acc[nb], 0, 0, 0);
+            for (int qa = 0; qa < NA; ++qa) {
+              const f16x8 af = __builtin_bit_cast(f16x8, ra[q][qa][ks]);
+              acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf0, acc[0], 0, 0, 0);
+              acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf1, acc[1], 0, 0, 0);
+            }
+          }
         }
+        QREB_NARROW_LOAD(q, min(g + PN, gend - 1));
       }
     }
 #undef QREB_NARROW_LOAD
@@ -1439,6 +1178,289 @@ __global__ __launch_bounds__(256) void mfma_narrow_kernel(MfmaArgs a) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) a.yslot[(size_t)sl * a.H + n0 + nb * 32 + l32] = v[nb];
       }
+    }
+  }
+}
+
+
+// --------------------------------------------- streaming path kernels --
+
+// Which (work item, row block) a streaming workgroup owns.  The grid is flat:
+// the first nsh workgroups are the row blocks of the shared expert (the last
+// streaming item when it streams), started first because it is the largest;
+// then nrb row blocks per routed item.  Returns false for a workgroup past
+// the routed items of this forward.
+__device__ __forceinline__ bool gemv_work(const int* misc, int b, int nsh, int nrb, int& item_i,
+                                          int& rb) {
+  const int n_items = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNGemv];
+  if (b < nsh) {
+    item_i = n_items - 1;
+    rb = b;
+    return item_i >= 0;
+  }
+  item_i = (b - nsh) / nrb;
+  rb = (b - nsh) - item_i * nrb;
+  return item_i < n_items - (nsh > 0 ? 1 : 0);
+}
+
+// Four wave-uniform values (one per token row of a streaming pass) selected
+// by a runtime row index without indexing a register array.
+static_assert(kGemvTokV2 == 4, "streaming passes hold four token rows");
+struct Four {
+  int v0, v1, v2, v3;
+  __device__ __forceinline__ int operator[](int i) const {
+    return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3;
+  }
+};
+
+// Stage nt rows of `row_u4` uint4 each into LDS (row t at dst + t * dst_row_dw
+// dwords) from src_row(t).  Each batch issues all its loads before the first
+// LDS write (every load unconditional, index clamped into the last row), so a
+// batch costs one memory round trip.
+// src_row(t) must be a value-capturing callable (no arrays captured by
+// reference: they would live in scratch memory).
+// With ODD16, the odd columns (dwords 1 and 3 of each 4-dword chunk in the
+// paired order) are divided by 16 on the way (fp16, rounded once).
+template <bool ODD16, typename SrcRow>
+__device__ __forceinline__ void stage_rows(uint32_t* dst, int dst_row_dw, int nt, int row_u4,
+                                           const SrcRow& src_row) {
+  // (a native vector type: an array of HIP's uint4 is not split into
+  // registers and would live in scratch memory)
+  // The first batch is straight-line code: inside a loop the compiler's
+  // waits for the registers the previous iteration loaded also wait for the
+  // weight loads issued before the staging.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int NB = 8;
+  const int tid = threadIdx.x, tot = nt * row_u4;
+  auto batch = [&](int base) {
+    u32x4 v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = min(base + tid + j * kGemvThreads, tot - 1);
+      const int t = i / row_u4;
+      v[j] = reinterpret_cast<const u32x4*>(src_row(t))[i - t * row_u4];
+    }
+    // stores clamped like the loads (a clamped lane rewrites the last
+    // element with the value it holds), so every load is consumed on every
+    // path and no wait for it is left pending at a loop back edge
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = min(base + tid + j * kGemvThreads, tot - 1);
+      const int t = i / row_u4;
+      if (ODD16) {
+        // (elements copied to scalars first: __builtin_bit_cast of a vector
+        // element expression reads the vector's first element)
+        const f16x2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const uint32_t ey = v[j].y, ew = v[j].w;
+        v[j].y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ey) * k16);
+        v[j].w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ew) * k16);
+      }
+      reinterpret_cast<u32x4*>(dst + t * dst_row_dw)[i - t * row_u4] = v[j];
+    }
+  };
+  batch(0);
+  for (int base = NB * kGemvThreads; base < tot; base += NB * kGemvThreads) batch(base);
+}
+
+// Streaming gate/up: workgroup = (work item, 64-row block of the expert's
+// intermediate dimension); its waves split the H/64 groups; token rows of x
+// (fp16 in the paired order) and their group sums are staged in LDS.  The
+// item and its slots are scalar loads; the weight prefetch is issued before
+// the token rows are staged.
+template <bool LO, bool SPLIT>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(SPLIT && !LO ? 4 : 1)))
+void gemv_up_kernel(
+    const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
+    int H, int E, int k, int I, int Is, int T, const uint32_t* __restrict__ x16,
+    const uint32_t* __restrict__ x16lo, const float* __restrict__ xs,
+    const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
+    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nrb, int mt, MfmaArgs ma,
+    int nn, int ncb) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ float red[SPLIT ? 1 : 2][kGemvWaves][kGemvTokV2][64];
+  // the first nn workgroups run the narrow matrix-core tiles (ncb column
+  // blocks per tile), so both expert paths share one launch
+  if ((int)blockIdx.x < nn) {
+    narrow_tile<true, LO>(ma, blockIdx.x / ncb, blockIdx.x % ncb, reinterpret_cast<NarrowRed*>(dyn),
+                          reinterpret_cast<int*>(dyn) + kMfmaWaves * 2 * 16 * 64);
+    return;
+  }
+  int item_i, rb;
+  if (!gemv_work(misc, (int)blockIdx.x - nn, nsh, nrb, item_i, rb)) return;
+  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
+  const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
+  const bool sh = e == E;
+  const int inter = sh ? Is : I;
+  if (rb * 64 >= inter) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = H >> 6, Tk = T * k;
+  const int xrow = LO ? H : H >> 1;               // dwords per staged row (hi [+ lo])
+  uint32_t* xl = dyn;                              // [mt][xrow]
+  float2* xsl = reinterpret_cast<float2*>(dyn + mt * xrow);   // [mt][G] (S1, S2)
+  const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
+  const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
+  // SPLIT: the first half of the waves streams the gate matrix, the second
+  // half the up matrix (fewer registers per wave, more workgroups per CU);
+  // else every wave streams both.  The waves of a matrix split the groups.
+  constexpr int NM = SPLIT ? 1 : 2;
+  constexpr int WPM = SPLIT ? kGemvWaves / 2 : kGemvWaves;
+  const int mat = SPLIT ? wave / WPM : 0, wq = wave - mat * WPM;
+  GemvStream<NM, kGemvP> st;
+  st.mat[0] = rec + kHeaderBytes + (size_t)mat * sec + (size_t)rb * G * kQ4TileBytes;
+  if (!SPLIT) st.mat[NM - 1] = st.mat[0] + sec;
+  st.gbeg = (G * wq) / WPM;
+  st.gend = (G * (wq + 1)) / WPM;
+  st.lane = lane;
+  const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
+
+  const bool busy = st.gbeg < st.gend;
+  for (int p0 = 0; p0 < m; p0 += mt) {
+    const int nt = min(mt, m - p0);
+    if (p0 > 0) __syncthreads();
+    if (busy) st.prefetch();
+    Four slot, tok;
+    slot.v0 = (int)sl[loff + p0];
+    slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
+    slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
+    slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
+    tok.v0 = slot.v0 < Tk ? slot.v0 / k : slot.v0 - Tk;
+    tok.v1 = slot.v1 < Tk ? slot.v1 / k : slot.v1 - Tk;
+    tok.v2 = slot.v2 < Tk ? slot.v2 / k : slot.v2 - Tk;
+    tok.v3 = slot.v3 < Tk ? slot.v3 / k : slot.v3 - Tk;
+    // group sums: the first kGemvThreads entries are loaded with the rows
+    const int nxs = nt * G;
+    const int i0 = min(tid, nxs - 1);
+    const float2* xs2 = reinterpret_cast<const float2*>(xs);
+    const float2 xs0 = xs2[(size_t)tok[i0 / G] * G + (i0 % G)];
+    const int hdw = H >> 1;
+    stage_rows<true>(xl, xrow, nt, H >> 3, [=](int t) {
+      return reinterpret_cast<const uint4*>(x16 + (size_t)tok[t] * hdw);
+    });
+    if (LO)
+      stage_rows<true>(xl + hdw, xrow, nt, H >> 3, [=](int t) {
+        return reinterpret_cast<const uint4*>(x16lo + (size_t)tok[t] * hdw);
+      });
+    xsl[i0] = xs0;
+    for (int i = tid + kGemvThreads; i < nxs; i += kGemvThreads)
+      xsl[i] = xs2[(size_t)tok[i / G] * G + (i % G)];
+    __syncthreads();
+    float acc[NM][kGemvTokV2];
+#pragma unroll
+    for (int t = 0; t < kGemvTokV2; ++t)
+#pragma unroll
+      for (int q = 0; q < NM; ++q) acc[q][t] = 0.f;
+    if (busy) st.template run<kGemvTokV2, LO>(xl, xrow, H >> 1, xsl, G, nt, acc);
+#pragma unroll
+    for (int t = 0; t < kGemvTokV2; ++t)
+      if (t < nt)
+#pragma unroll
+        for (int q = 0; q < NM; ++q) red[q][wave][t][lane] = acc[q][t];
+    __syncthreads();
+    for (int t = wave; t < nt; t += kGemvWaves) {
+      float gs = 0.f, us = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPM; ++w) {
+        gs += red[0][w][t][lane];
+        us += SPLIT ? red[0][WPM + w][t][lane] : red[NM - 1][w][t][lane];
+      }
+      const float hv = gs / (1.f + expf(-gs)) * us;
+      // h in fp16, odd columns stored divided by 16 (the streaming down
+      // pass stages them as they are); S1 sums what is stored, S2 the h
+      // those values stand for
+      const _Float16 h16 = (_Float16)hv;
+      const bool odd = lane & 1;
+      const _Float16 hst = odd ? (_Float16)((float)h16 * 0.0625f) : h16;
+      const int sv = slot[t];
+      const int col = rb * 64 + lane;
+      hbuf[h_off(sv, Tk, I, Is) + pair_pos4(col)] = f16bits(hst);
+      const float s1 = wave_sum((float)hst);
+      const float s2 = wave_sum(odd ? 16.f * (float)hst : (float)hst);
+      if (lane == 0) reinterpret_cast<float2*>(hs)[hs_off(sv, Tk, I, Is) + rb] = make_float2(s1, s2);
+    }
+  }
+}
+
+// Streaming down: a workgroup owns one work item and rpw 64-row blocks of H
+// (the shared expert, whose K is the longest, one block; a routed expert rpu
+// blocks).  The waves of a row block split its inter/64 groups; the slots'
+// h rows (fp16, paired order) and their group sums are staged in LDS once per
+// workgroup.  Writes one fp32 row per slot.
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_down_kernel(
+    const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
+    int H, int E, int k, int I, int Is, int T, const int4* __restrict__ items,
+    const int* __restrict__ misc, const int* __restrict__ slots,
+    const uint32_t* __restrict__ hbuf32, const float* __restrict__ hs,
+    float* __restrict__ yslot, int nsh, int rpu, int mt, MfmaArgs ma, int nn, int ncb) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ float red[kGemvWaves][kGemvTokV2][64];
+  if ((int)blockIdx.x < nn) {     // narrow matrix-core tiles first (see gemv_up_kernel)
+    narrow_tile<false, false>(ma, blockIdx.x / ncb, blockIdx.x % ncb,
+                              reinterpret_cast<NarrowRed*>(dyn),
+                              reinterpret_cast<int*>(dyn) + kMfmaWaves * 2 * 16 * 64);
+    return;
+  }
+  const int nrb = H >> 6;
+  const int nunits = (nrb + rpu - 1) / rpu;
+  int item_i, u;
+  if (!gemv_work(misc, (int)blockIdx.x - nn, nsh, nunits, item_i, u)) return;
+  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
+  const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
+  const bool sh = e == E;
+  const int inter = sh ? Is : I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rpw = sh ? 1 : rpu;                 // row blocks of this workgroup
+  const int wpr = kGemvWaves / rpw;             // waves per row block
+  const int rb0 = sh ? u : u * rpu;
+  const int rb = rb0 + wave / wpr, wq = wave - (wave / wpr) * wpr;
+  const int G = H >> 6, G2 = inter >> 6, Tk = T * k;
+  const int hrow = inter >> 1;
+  uint32_t* hl = dyn;                                        // [mt][hrow]
+  float2* hsl = reinterpret_cast<float2*>(dyn + mt * hrow);    // [mt][G2] (S1, S2)
+  const size_t sec = (size_t)G2 * G * kQ4TileBytes;
+  const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
+  GemvStream<1, kGemvP> st;
+  st.mat[0] = rec + kHeaderBytes + 2 * sec + (size_t)min(rb, nrb - 1) * G2 * kQ4TileBytes;
+  st.gbeg = (G2 * wq) / wpr;
+  st.gend = (G2 * (wq + 1)) / wpr;
+  st.lane = lane;
+  const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
+
+  const bool busy = st.gbeg < st.gend && rb < nrb;
+  for (int p0 = 0; p0 < m; p0 += mt) {
+    const int nt = min(mt, m - p0);
+    if (p0 > 0) __syncthreads();
+    if (busy) st.prefetch();
+    Four slot;
+    slot.v0 = (int)sl[loff + p0];
+    slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
+    slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
+    slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
+    const int nhs = nt * G2;
+    const int i0 = min(tid, nhs - 1);
+    const float2* hs2 = reinterpret_cast<const float2*>(hs);
+    const float2 hs0 = hs2[hs_off(slot[i0 / G2], Tk, I, Is) + (i0 % G2)];
+    stage_rows<false>(hl, hrow, nt, inter >> 3, [=](int t) {
+      return reinterpret_cast<const uint4*>(hbuf32 + (h_off(slot[t], Tk, I, Is) >> 1));
+    });
+    hsl[i0] = hs0;
+    for (int i = tid + kGemvThreads; i < nhs; i += kGemvThreads)
+      hsl[i] = hs2[hs_off(slot[i / G2], Tk, I, Is) + (i % G2)];
+    __syncthreads();
+    float acc[1][kGemvTokV2];
+#pragma unroll
+    for (int t = 0; t < kGemvTokV2; ++t) acc[0][t] = 0.f;
+    if (busy) st.run<kGemvTokV2, false>(hl, hrow, 0, hsl, G2, nt, acc);
+#pragma unroll
+    for (int t = 0; t < kGemvTokV2; ++t)
+      if (t < nt) red[wave][t][lane] = acc[0][t];
+    __syncthreads();
+    // (row block, token) pairs over the waves; fixed-order sum over a block's waves
+    for (int pr = wave; pr < rpw * nt; pr += kGemvWaves) {
+      const int r = pr / nt, t = pr - r * nt;
+      float v = 0.f;
+      for (int q = 0; q < wpr; ++q) v += red[r * wpr + q][t][lane];
+      if (rb0 + r < nrb) yslot[(size_t)slot[t] * H + (rb0 + r) * 64 + lane] = v;
     }
   }
 }
@@ -1667,20 +1689,31 @@ static int routed_stream_items(const LayerDev& d, int T) {
   return Tk < d.E ? Tk : d.E;
 }
 
+static int narrow_tiles_max(const LayerDev& d, int T);
+static MfmaArgs mfma_args(const LayerDev& d, int T);
+
+// LDS bytes of a narrow matrix-core tile run inside a streaming launch
+constexpr size_t kNarrowLds = sizeof(NarrowRed) * kMfmaWaves + 32 * sizeof(int);
+
 hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
-  const size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + 2 * (d.H / 64)) * 4;
+  size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + 2 * (d.H / 64)) * 4;
   const int nsh = shared_streams(d, T) ? d.Is / 64 : 0, nrb = d.I / 64;
   const int units = nsh + routed_stream_items(d, T) * nrb;
+  // narrow matrix-core tiles (experts with a few tens of rows) in the same
+  // launch: 32 columns per workgroup
+  const int imax = d.Is > d.I ? d.Is : d.I;
+  const int ncb = imax / 32, nn = ncb * narrow_tiles_max(d, T);
+  if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
   // many workgroups: one matrix per wave (more resident workgroups to hide
   // each one's staging); few: both matrices per wave (shorter per-wave chain)
   const bool split = units >= 1024;
   auto* kern = x_f32 ? (split ? gemv_up_kernel<true, true> : gemv_up_kernel<true, false>)
                      : (split ? gemv_up_kernel<false, true> : gemv_up_kernel<false, false>);
-  hipLaunchKernelGGL(kern, dim3(units), dim3(kGemvThreads), lds, s, d.bank, d.stride, d.shared,
-                     d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs, p.items, p.misc, p.slots,
-                     p.hbuf, p.hs, nsh, nrb, mt);
+  hipLaunchKernelGGL(kern, dim3(nn + units), dim3(kGemvThreads), lds, s, d.bank, d.stride,
+                     d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs, p.items, p.misc,
+                     p.slots, p.hbuf, p.hs, nsh, nrb, mt, mfma_args(d, T), nn, ncb);
   return hipGetLastError();
 }
 
@@ -1694,23 +1727,32 @@ hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
   const int nrb = d.H / 64, nsh = shared_streams(d, T) ? nrb : 0;
   const int G2 = d.I / 64;
   const int rpu = G2 <= 24 ? kGemvWaves / 2 : 1;
-  const dim3 grid(nsh + routed_stream_items(d, T) * ((nrb + rpu - 1) / rpu));
-  hipLaunchKernelGGL(gemv_down_kernel, grid, dim3(kGemvThreads), lds, s, d.bank, d.stride,
-                     d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.items, p.misc, p.slots,
-                     reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, nsh, rpu, mt);
+  const int units = nsh + routed_stream_items(d, T) * ((nrb + rpu - 1) / rpu);
+  const int ncb = d.H / 64, nn = ncb * narrow_tiles_max(d, T);   // narrow down tiles, 64 columns
+  size_t ldsn = lds;
+  if (nn > 0 && ldsn < kNarrowLds) ldsn = kNarrowLds;
+  hipLaunchKernelGGL(gemv_down_kernel, dim3(nn + units), dim3(kGemvThreads), ldsn, s, d.bank,
+                     d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.items, p.misc, p.slots,
+                     reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, nsh, rpu, mt,
+                     mfma_args(d, T), nn, ncb);
   return hipGetLastError();
 }
 
 // Upper bounds of matrix-core row tiles in one forward (the exact counts are
 // in misc[kNTiles] / misc[kNNarrow]): an item with r rows adds ceil(r / BM).
+// An item with r rows in [lo, hi) adds ceil(r / bm) tiles (hi = 0: no upper
+// bound); at most min(E, Tk / lo) routed items reach lo rows.
 static int tiles_max(const LayerDev& d, int T, int lo, int hi, int bm) {
   const int Tk = T * d.k;
   if (T < lo) return 0;                     // no expert (nor the shared one) reaches lo rows
   int items = Tk / lo;
   if (items > d.E) items = d.E;
   int n = (Tk + bm - 1) / bm + items;
-  if (d.has_shared) n += (T + bm - 1) / bm + 1;
-  (void)hi;
+  if (hi > 0) {                             // each item adds at most ceil((hi - 1) / bm)
+    const int per = (hi - 1 + bm - 1) / bm;
+    if (items * per < n) n = items * per;
+  }
+  if (d.has_shared && (hi == 0 || T < hi)) n += (T + bm - 1) / bm;
   return n;
 }
 static int mfma_tiles_max(const LayerDev& d, int T) {
@@ -1745,28 +1787,8 @@ static MfmaArgs mfma_args(const LayerDev& d, int T) {
 }
 
 bool mfma_needed(const LayerDev& d, int T) { return mfma_tiles_max(d, T) > 0; }
-bool narrow_needed(const LayerDev& d, int T) { return narrow_tiles_max(d, T) > 0; }
 
-hipError_t launch_narrow_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
-  const int nt = narrow_tiles_max(d, T);
-  if (nt == 0) return hipSuccess;
-  const int imax = d.Is > d.I ? d.Is : d.I;
-  const MfmaArgs m = mfma_args(d, T);
-  const dim3 grid(imax / 32, nt);
-  if (x_f32)
-    hipLaunchKernelGGL((mfma_narrow_kernel<true, true>), grid, dim3(256), 0, s, m);
-  else
-    hipLaunchKernelGGL((mfma_narrow_kernel<true, false>), grid, dim3(256), 0, s, m);
-  return hipGetLastError();
-}
 
-hipError_t launch_narrow_down(const LayerDev& d, int T, hipStream_t s) {
-  const int nt = narrow_tiles_max(d, T);
-  if (nt == 0) return hipSuccess;
-  const MfmaArgs m = mfma_args(d, T);
-  hipLaunchKernelGGL((mfma_narrow_kernel<false, false>), dim3(d.H / 64, nt), dim3(256), 0, s, m);
-  return hipGetLastError();
-}
 
 hipError_t launch_mfma_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const int nt = mfma_tiles_max(d, T);
