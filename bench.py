@@ -90,12 +90,13 @@ def run_case(layers, sh, T, steps, warmup, tag=0):
     ys = [torch.empty((T, sh.hidden), dtype=torch.float32, device=dev) for _ in range(n)]
     # routing per copy (deterministic): distinct experts and rows
     distinct, streamed = [], []
-    rmin = layers[0].mfma_min_rows
+    rwide = layers[0].wide_min_rows
     for l in range(n):
         _, ids, _ = layers[l].forward(xs[l], return_selection=True)
         cnt = np.bincount(ids.cpu().numpy().reshape(-1), minlength=sh.n_experts)
         distinct.append(int((cnt > 0).sum()))
-        streamed.append(int(((cnt > 0) & (cnt < rmin)).sum()))   # experts on the streaming path
+        # experts in the streaming launches: streamed, or in 32-row matrix-core tiles
+        streamed.append(int(((cnt > 0) & (cnt < rwide)).sum()))
     for i in range(warmup):
         layers[i % n].forward(xs[i % n], y=ys[i % n])
     torch.cuda.synchronize()
@@ -245,11 +246,11 @@ def main():
     res = run_case(layers, sh, T, args.steps, args.warmup)
     log(f"T={T}: {res['ms_per_step']*1e3:.1f} us/step, kernels {res['kern_ms']}")
 
-    # dominant kernel: streaming gate/up.  Algorithmic bytes per launch =
-    # (routed experts on the streaming path, i.e. with fewer than mfma_min_rows
-    # rows, + the shared expert when it streams) * 2*H*I*4.5/8.
-    rmin = layers[0].mfma_min_rows
-    shared_streams = sh.has_shared and T < rmin
+    # dominant kernel: the gate/up launch of the streaming path, which also
+    # carries the 32-row matrix-core tiles.  Algorithmic bytes per launch =
+    # (routed experts with fewer than wide_min_rows rows, + the shared expert
+    # when the batch is below that) * 2*H*I*4.5/8.
+    shared_streams = sh.has_shared and T < layers[0].wide_min_rows
     up_bytes = res["streamed"] * 2 * sh.hidden * sh.inter * 9 / 16 + \
         (2 * sh.hidden * sh.shared_inter * 9 / 16 if shared_streams else 0)
     up_ms = res["kern_ms"]["gemv_up"]
@@ -293,7 +294,8 @@ def main():
         for Tx in (1, 4):
             r = run_case(layers, sh, Tx, args.steps, args.warmup, tag=Tx)
             ub = r["streamed"] * 2 * sh.hidden * sh.inter * 9 / 16 + \
-                (2 * sh.hidden * sh.shared_inter * 9 / 16 if sh.has_shared and Tx < rmin else 0)
+                (2 * sh.hidden * sh.shared_inter * 9 / 16
+                 if sh.has_shared and Tx < layers[0].wide_min_rows else 0)
             extra[f"T{Tx}"] = {"tokens_s": round(r["tok_s"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2),
                                "gemv_up_GB_s": round(ub / (r["kern_ms"]["gemv_up"] * 1e-3) / 1e9, 1),
                                "kernel_us": {k: round(v * 1e3, 3) for k, v in r["kern_ms"].items()},

@@ -86,7 +86,7 @@ WsLayout ws_layout(const moe_config& c) {
   o = al(o);
   L.offs = take((E + 1) * 4);
   L.slots = take((Tk + T) * 4);
-  L.items = take((E + 1) * 16);
+  L.items = take((E + 1) * 32);   // (expert, rows, offset, 0) + first 4 slots
   L.mitems = take((E + 1) * 16);
   L.mtiles = take(((Tk + kMfmaBM - 1) / kMfmaBM + E + (T + kMfmaBM - 1) / kMfmaBM + 1) * 8);
   L.ntiles = take(((Tk + kNarrowBM - 1) / kNarrowBM + E + (T + kNarrowBM - 1) / kNarrowBM + 1) * 8);

@@ -213,7 +213,7 @@ struct RouterArgs {
   int mfma_min_rows, wide_min_rows, has_shared;
 };
 
-constexpr int kBucketSmem = 5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + kMaxExperts;
+constexpr int kBucketSmem = 5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + 16 * kMaxExperts + kMaxExperts;
 
 // Bucketing, by one 256-thread workgroup once every token's top-k is known:
 // LDS histogram of the T*k selections -> exclusive scan -> slot lists grouped
@@ -228,7 +228,8 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   int* s_scan = s_cur + kMaxExperts + 2;                     // [256]
   int* s_tot = s_scan + 256;                                 // [4]
   int* s_mrows = s_tot + 4;                                  // [E + 1] rows per matrix-core item
-  unsigned char* s_pred = reinterpret_cast<unsigned char*>(s_mrows + kMaxExperts + 2);   // [E]
+  int* s_first = s_mrows + kMaxExperts + 2;                  // [E][4] first slots per expert
+  unsigned char* s_pred = reinterpret_cast<unsigned char*>(s_first + 4 * kMaxExperts);   // [E]
   const int tid = threadIdx.x;
   const int E = a.E, Tk = a.T * a.k;
   const int R = a.mfma_min_rows;
@@ -272,7 +273,11 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
     for (int j = 0; j < 8; ++j) v[j] = ids[min(s0 + 256 * j, Tk - 1)];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (s0 + 256 * j < Tk) a.slots[atomicAdd(&s_cur[v[j]], 1)] = s0 + 256 * j;
+      if (s0 + 256 * j < Tk) {
+        const int pos = atomicAdd(&s_cur[v[j]], 1), r = pos - s_off[v[j]];
+        a.slots[pos] = s0 + 256 * j;
+        if (r < 4) s_first[v[j] * 4 + r] = s0 + 256 * j;
+      }
   }
   if (a.has_shared)
     for (int t = tid; t < a.T; t += 256) a.slots[Tk + t] = Tk + t;
@@ -296,8 +301,15 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
     for (int e = tid; e < E; e += 256)
       if (s_flag[e]) {
         const int pos = s_flag[e] == 1 ? (s_cur[e] & 0xffff) : n_first + (s_cur[e] >> 16);
-        (path == 0 ? a.items : a.mitems)[pos] = make_int4(e, s_cnt[e], s_off[e], 0);
-        if (path == 1) s_mrows[pos] = s_cnt[e];
+        if (path == 0) {   // streaming item: (expert, rows, offset) + its first 4 slots
+          const int c = s_cnt[e];
+          const int* f = s_first + e * 4;
+          a.items[2 * pos] = make_int4(e, c, s_off[e], 0);
+          a.items[2 * pos + 1] = make_int4(f[0], f[min(1, c - 1)], f[min(2, c - 1)], f[min(3, c - 1)]);
+        } else {
+          a.mitems[pos] = make_int4(e, s_cnt[e], s_off[e], 0);
+          s_mrows[pos] = s_cnt[e];
+        }
       }
     if (tid == 0) s_tot[path] = n_first + (tot >> 16);
     __syncthreads();
@@ -311,7 +323,11 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
       }
       ++n_mfma;
     } else {
-      if (tid == 0) a.items[n_gemv] = make_int4(E, a.T, Tk, 0);
+      if (tid == 0) {
+        a.items[2 * n_gemv] = make_int4(E, a.T, Tk, 0);
+        a.items[2 * n_gemv + 1] = make_int4(Tk, Tk + min(1, a.T - 1), Tk + min(2, a.T - 1),
+                                            Tk + min(3, a.T - 1));
+      }
       ++n_gemv;
     }
   }
@@ -1274,8 +1290,8 @@ void gemv_up_kernel(
     int H, int E, int k, int I, int Is, int T, const uint32_t* __restrict__ x16,
     const uint32_t* __restrict__ x16lo, const float* __restrict__ xs,
     const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
-    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nrb, int mt, MfmaArgs ma,
-    int nn, int ncb) {
+    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nunits, int rpw, int mt,
+    MfmaArgs ma, int nn, int ncb) {
   extern __shared__ uint32_t dyn[];
   __shared__ float red[SPLIT ? 1 : 2][kGemvWaves][kGemvTokV2][64];
   // the first nn workgroups run the narrow matrix-core tiles (ncb column
@@ -1285,13 +1301,15 @@ void gemv_up_kernel(
                           reinterpret_cast<int*>(dyn) + kMfmaWaves * 2 * 16 * 64);
     return;
   }
-  int item_i, rb;
-  if (!gemv_work(misc, (int)blockIdx.x - nn, nsh, nrb, item_i, rb)) return;
-  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
+  // a unit is rpw consecutive 64-row blocks of one item (rpw = 2 only with SPLIT)
+  int item_i, u;
+  if (!gemv_work(misc, (int)blockIdx.x - nn, nsh, nunits, item_i, u)) return;
+  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + 2 * item_i));
   const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
   const bool sh = e == E;
   const int inter = sh ? Is : I;
-  if (rb * 64 >= inter) return;
+  const int rb0 = u * rpw, nrb_i = inter >> 6;
+  if (rb0 >= nrb_i) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H >> 6, Tk = T * k;
   const int xrow = LO ? H : H >> 1;               // dwords per staged row (hi [+ lo])
@@ -1299,30 +1317,41 @@ void gemv_up_kernel(
   float2* xsl = reinterpret_cast<float2*>(dyn + mt * xrow);   // [mt][G] (S1, S2)
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
   const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
-  // SPLIT: the first half of the waves streams the gate matrix, the second
-  // half the up matrix (fewer registers per wave, more workgroups per CU);
-  // else every wave streams both.  The waves of a matrix split the groups.
+  // SPLIT: each row block's waves are half gate, half up (fewer registers
+  // per wave, more workgroups per CU); with rpw = 2 that is one wave per
+  // (row block, matrix) streaming all groups.  Else every wave streams both
+  // matrices.  The waves of a (row block, matrix) split the groups.
   constexpr int NM = SPLIT ? 1 : 2;
-  constexpr int WPM = SPLIT ? kGemvWaves / 2 : kGemvWaves;
-  const int mat = SPLIT ? wave / WPM : 0, wq = wave - mat * WPM;
+  const int wpr = kGemvWaves / rpw;                    // waves per row block
+  const int wpm = SPLIT ? wpr / 2 : wpr;               // waves per matrix
+  const int r = wave / wpr, wq = wave - r * wpr;
+  const int mat = SPLIT ? wq / wpm : 0, wk = wq - mat * wpm;
+  const int rb = rb0 + r;
   GemvStream<NM, kGemvP> st;
-  st.mat[0] = rec + kHeaderBytes + (size_t)mat * sec + (size_t)rb * G * kQ4TileBytes;
+  st.mat[0] = rec + kHeaderBytes + (size_t)mat * sec + (size_t)min(rb, nrb_i - 1) * G * kQ4TileBytes;
   if (!SPLIT) st.mat[NM - 1] = st.mat[0] + sec;
-  st.gbeg = (G * wq) / WPM;
-  st.gend = (G * (wq + 1)) / WPM;
+  st.gbeg = (G * wk) / wpm;
+  st.gend = (G * (wk + 1)) / wpm;
   st.lane = lane;
   const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
 
-  const bool busy = st.gbeg < st.gend;
+  const bool busy = st.gbeg < st.gend && rb < nrb_i;
   for (int p0 = 0; p0 < m; p0 += mt) {
     const int nt = min(mt, m - p0);
     if (p0 > 0) __syncthreads();
     if (busy) st.prefetch();
     Four slot, tok;
-    slot.v0 = (int)sl[loff + p0];
-    slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
-    slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
-    slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
+    if (p0 == 0) {   // the item record carries its first 4 slots (one load level less)
+      slot.v0 = (int)itp[4];
+      slot.v1 = (int)itp[5];
+      slot.v2 = (int)itp[6];
+      slot.v3 = (int)itp[7];
+    } else {
+      slot.v0 = (int)sl[loff + p0];
+      slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
+      slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
+      slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
+    }
     tok.v0 = slot.v0 < Tk ? slot.v0 / k : slot.v0 - Tk;
     tok.v1 = slot.v1 < Tk ? slot.v1 / k : slot.v1 - Tk;
     tok.v2 = slot.v2 < Tk ? slot.v2 / k : slot.v2 - Tk;
@@ -1356,12 +1385,16 @@ void gemv_up_kernel(
 #pragma unroll
         for (int q = 0; q < NM; ++q) red[q][wave][t][lane] = acc[q][t];
     __syncthreads();
-    for (int t = wave; t < nt; t += kGemvWaves) {
+    // (row block, token) pairs over the waves; fixed-order sums over the
+    // waves of each matrix
+    for (int pr = wave; pr < rpw * nt; pr += kGemvWaves) {
+      const int rr = pr / nt, t = pr - rr * nt;
+      const int rbr = rb0 + rr;
+      if (rbr >= nrb_i) continue;
       float gs = 0.f, us = 0.f;
-#pragma unroll
-      for (int w = 0; w < WPM; ++w) {
-        gs += red[0][w][t][lane];
-        us += SPLIT ? red[0][WPM + w][t][lane] : red[NM - 1][w][t][lane];
+      for (int j = 0; j < wpm; ++j) {
+        gs += red[0][rr * wpr + j][t][lane];
+        us += SPLIT ? red[0][rr * wpr + wpm + j][t][lane] : red[NM - 1][rr * wpr + j][t][lane];
       }
       const float hv = gs / (1.f + expf(-gs)) * us;
       // h in fp16, odd columns stored divided by 16 (the streaming down
@@ -1371,11 +1404,11 @@ void gemv_up_kernel(
       const bool odd = lane & 1;
       const _Float16 hst = odd ? (_Float16)((float)h16 * 0.0625f) : h16;
       const int sv = slot[t];
-      const int col = rb * 64 + lane;
+      const int col = rbr * 64 + lane;
       hbuf[h_off(sv, Tk, I, Is) + pair_pos4(col)] = f16bits(hst);
       const float s1 = wave_sum((float)hst);
       const float s2 = wave_sum(odd ? 16.f * (float)hst : (float)hst);
-      if (lane == 0) reinterpret_cast<float2*>(hs)[hs_off(sv, Tk, I, Is) + rb] = make_float2(s1, s2);
+      if (lane == 0) reinterpret_cast<float2*>(hs)[hs_off(sv, Tk, I, Is) + rbr] = make_float2(s1, s2);
     }
   }
 }
@@ -1404,7 +1437,7 @@ void gemv_down_kernel(
   const int nunits = (nrb + rpu - 1) / rpu;
   int item_i, u;
   if (!gemv_work(misc, (int)blockIdx.x - nn, nsh, nunits, item_i, u)) return;
-  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + item_i));
+  const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + 2 * item_i));
   const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
   const bool sh = e == E;
   const int inter = sh ? Is : I;
@@ -1432,10 +1465,17 @@ void gemv_down_kernel(
     if (p0 > 0) __syncthreads();
     if (busy) st.prefetch();
     Four slot;
-    slot.v0 = (int)sl[loff + p0];
-    slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
-    slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
-    slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
+    if (p0 == 0) {   // the item record carries its first 4 slots (one load level less)
+      slot.v0 = (int)itp[4];
+      slot.v1 = (int)itp[5];
+      slot.v2 = (int)itp[6];
+      slot.v3 = (int)itp[7];
+    } else {
+      slot.v0 = (int)sl[loff + p0];
+      slot.v1 = (int)sl[loff + p0 + min(1, nt - 1)];
+      slot.v2 = (int)sl[loff + p0 + min(2, nt - 1)];
+      slot.v3 = (int)sl[loff + p0 + min(3, nt - 1)];
+    }
     const int nhs = nt * G2;
     const int i0 = min(tid, nhs - 1);
     const float2* hs2 = reinterpret_cast<const float2*>(hs);
@@ -1699,21 +1739,27 @@ hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
   size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + 2 * (d.H / 64)) * 4;
-  const int nsh = shared_streams(d, T) ? d.Is / 64 : 0, nrb = d.I / 64;
-  const int units = nsh + routed_stream_items(d, T) * nrb;
+  const int nsh1 = shared_streams(d, T) ? d.Is / 64 : 0, nrb = d.I / 64;
+  const int units1 = nsh1 + routed_stream_items(d, T) * nrb;   // one row block per unit
   // narrow matrix-core tiles (experts with a few tens of rows) in the same
   // launch: 32 columns per workgroup
   const int imax = d.Is > d.I ? d.Is : d.I;
   const int ncb = imax / 32, nn = ncb * narrow_tiles_max(d, T);
   if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
   // many workgroups: one matrix per wave (more resident workgroups to hide
-  // each one's staging); few: both matrices per wave (shorter per-wave chain)
-  const bool split = units >= 1024;
+  // each one's staging); few: both matrices per wave (shorter per-wave
+  // chain).  One row block per unit: two (one wave per row block and matrix)
+  // measured 1.3x slower at 16 tokens.
+  const bool split = units1 >= 1024;
+  const int rpw = 1;
+  const int nunits = (nrb + rpw - 1) / rpw;
+  const int nsh = nsh1 ? (nsh1 + rpw - 1) / rpw : 0;
+  const int units = nsh + routed_stream_items(d, T) * nunits;
   auto* kern = x_f32 ? (split ? gemv_up_kernel<true, true> : gemv_up_kernel<true, false>)
                      : (split ? gemv_up_kernel<false, true> : gemv_up_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3(nn + units), dim3(kGemvThreads), lds, s, d.bank, d.stride,
                      d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs, p.items, p.misc,
-                     p.slots, p.hbuf, p.hs, nsh, nrb, mt, mfma_args(d, T), nn, ncb);
+                     p.slots, p.hbuf, p.hs, nsh, nunits, rpw, mt, mfma_args(d, T), nn, ncb);
   return hipGetLastError();
 }
 
