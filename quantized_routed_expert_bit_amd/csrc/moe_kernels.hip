@@ -1065,10 +1065,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
 // with a PN-deep register ring for both operands (A straight from global, no
 // LDS, no barriers in the loop) and the partial accumulators are summed across
 // waves in fixed order at the end.
-// The body works on tile tile_i, column block cblk, with red (32 KiB) and
-// s_slot (32 ints) in LDS; it is the narrow kernel below, and the first
-// workgroups of the streaming kernels run it too (one launch for both paths).
-typedef float NarrowRed[2][16][64];
+// The body works on tile tile_i, column block cblk, with red (16 KiB, one
+// [16][64] plane per wave) and s_slot (32 ints) in LDS; the first workgroups
+// of the streaming kernels run it (one launch for both expert paths).
+typedef float NarrowRed[16][64];
 template <bool UP, bool LO>
 __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int cblk,
                                             NarrowRed* red, int* s_slot) {
@@ -1168,31 +1168,35 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
     }
 #undef QREB_NARROW_LOAD
   }
+  // wave w finishes rows j in {4w .. 4w+3} of each lane's 16 (fixed-order
+  // sum over the waves), one 32-column block at a time through the same LDS
+  float v[2][4];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < 2; ++nb) {
+    if (nb) __syncthreads();   // every wave has read block 0 before it is overwritten
 #pragma unroll
-    for (int j = 0; j < 16; ++j) red[wave][nb][j][lane] = acc[nb][j];
-  __syncthreads();
-  // wave w finishes rows j in {4w .. 4w+3} of each lane's 16 (fixed-order sum over waves)
+    for (int j = 0; j < 16; ++j) red[wave][j][lane] = acc[nb][j];
+    __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kMfmaWaves; ++w) sum += red[w][wave * 4 + jj][lane];
+      v[nb][jj] = sum;
+    }
+  }
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int j = wave * 4 + jj;
     const int row = 8 * (j >> 2) + 4 * hi + (j & 3);
-    float v[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      v[nb] = 0.f;
-#pragma unroll
-      for (int w = 0; w < kMfmaWaves; ++w) v[nb] += red[w][nb][j][lane];
-    }
     if (row < mrows) {
       const int sl = s_slot[row];
       if (UP) {
-        const float hv = v[0] / (1.f + expf(-v[0])) * v[1];
+        const float hv = v[0][jj] / (1.f + expf(-v[0][jj])) * v[1][jj];
         a.hdst[h_off(sl, Tk, a.I, a.Is) + pair_pos4(n0 + l32)] = f16bits((_Float16)hv);
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) a.yslot[(size_t)sl * a.H + n0 + nb * 32 + l32] = v[nb];
+        for (int nb = 0; nb < 2; ++nb) a.yslot[(size_t)sl * a.H + n0 + nb * 32 + l32] = v[nb][jj];
       }
     }
   }
@@ -1200,6 +1204,33 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
 
 
 // --------------------------------------------- streaming path kernels --
+
+// Which narrow matrix-core tile a workgroup of a streaming launch runs.  The
+// tiles of this forward (misc[kNNarrow] of them, the shared expert's nsht
+// tiles last in the list) take the first workgroups of the grid, compacted:
+// the shared expert's tiles (ncbs column blocks each) first, as the largest,
+// then the routed ones (ncbr each).  Returns true with (tile, cblk) set for a
+// narrow workgroup; else rebases b onto the streaming units, so the
+// workgroups past this forward's work all sit at the end of the grid.
+__device__ __forceinline__ bool narrow_work(const int* misc, int nsht, int ncbs, int ncbr, int& b,
+                                            int& tile, int& cblk) {
+  const int nreal = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNNarrow];
+  const int nrt = max(nreal - nsht, 0);
+  const int nsw = nsht * ncbs;
+  if (b < nsw) {
+    tile = nrt + b / ncbs;
+    cblk = b - (b / ncbs) * ncbs;
+    return true;
+  }
+  b -= nsw;
+  if (b < nrt * ncbr) {
+    tile = b / ncbr;
+    cblk = b - tile * ncbr;
+    return true;
+  }
+  b -= nrt * ncbr;
+  return false;
+}
 
 // Which (work item, row block) a streaming workgroup owns.  The grid is flat:
 // the first nsh workgroups are the row blocks of the shared expert (the last
@@ -1291,19 +1322,22 @@ void gemv_up_kernel(
     const uint32_t* __restrict__ x16lo, const float* __restrict__ xs,
     const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
     uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nunits, int rpw, int mt,
-    MfmaArgs ma, int nn, int ncb) {
+    MfmaArgs ma, int nsht, int ncbs, int ncbr) {
   extern __shared__ uint32_t dyn[];
-  __shared__ float red[SPLIT ? 1 : 2][kGemvWaves][kGemvTokV2][64];
-  // the first nn workgroups run the narrow matrix-core tiles (ncb column
-  // blocks per tile), so both expert paths share one launch
-  if ((int)blockIdx.x < nn) {
-    narrow_tile<true, LO>(ma, blockIdx.x / ncb, blockIdx.x % ncb, reinterpret_cast<NarrowRed*>(dyn),
-                          reinterpret_cast<int*>(dyn) + kMfmaWaves * 2 * 16 * 64);
+  // the narrow matrix-core tiles run in the first workgroups, so both
+  // expert paths share one launch
+  int b = (int)blockIdx.x, tile, cblk;
+  if (narrow_work(misc, nsht, ncbs, ncbr, b, tile, cblk)) {
+    narrow_tile<true, LO>(ma, tile, cblk, reinterpret_cast<NarrowRed*>(dyn),
+                          reinterpret_cast<int*>(dyn) + kMfmaWaves * 16 * 64);
     return;
   }
+  // per-wave partial sums, in LDS over the staged rows once they are consumed
+  float (*red)[kGemvWaves][kGemvTokV2][64] =
+      reinterpret_cast<float (*)[kGemvWaves][kGemvTokV2][64]>(dyn);
   // a unit is rpw consecutive 64-row blocks of one item (rpw = 2 only with SPLIT)
   int item_i, u;
-  if (!gemv_work(misc, (int)blockIdx.x - nn, nsh, nunits, item_i, u)) return;
+  if (!gemv_work(misc, b, nsh, nunits, item_i, u)) return;
   const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + 2 * item_i));
   const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
   const bool sh = e == E;
@@ -1379,6 +1413,7 @@ void gemv_up_kernel(
 #pragma unroll
       for (int q = 0; q < NM; ++q) acc[q][t] = 0.f;
     if (busy) st.template run<kGemvTokV2, LO>(xl, xrow, H >> 1, xsl, G, nt, acc);
+    __syncthreads();   // the staged rows are consumed: red overlays them
 #pragma unroll
     for (int t = 0; t < kGemvTokV2; ++t)
       if (t < nt)
@@ -1424,19 +1459,19 @@ void gemv_down_kernel(
     int H, int E, int k, int I, int Is, int T, const int4* __restrict__ items,
     const int* __restrict__ misc, const int* __restrict__ slots,
     const uint32_t* __restrict__ hbuf32, const float* __restrict__ hs,
-    float* __restrict__ yslot, int nsh, int rpu, int mt, MfmaArgs ma, int nn, int ncb) {
+    float* __restrict__ yslot, int nsh, int rpu, int mt, MfmaArgs ma, int nsht, int ncb) {
   extern __shared__ uint32_t dyn[];
-  __shared__ float red[kGemvWaves][kGemvTokV2][64];
-  if ((int)blockIdx.x < nn) {     // narrow matrix-core tiles first (see gemv_up_kernel)
-    narrow_tile<false, false>(ma, blockIdx.x / ncb, blockIdx.x % ncb,
-                              reinterpret_cast<NarrowRed*>(dyn),
-                              reinterpret_cast<int*>(dyn) + kMfmaWaves * 2 * 16 * 64);
+  int b = (int)blockIdx.x, tile, cblk;
+  if (narrow_work(misc, nsht, ncb, ncb, b, tile, cblk)) {   // as in gemv_up_kernel
+    narrow_tile<false, false>(ma, tile, cblk, reinterpret_cast<NarrowRed*>(dyn),
+                              reinterpret_cast<int*>(dyn) + kMfmaWaves * 16 * 64);
     return;
   }
+  float (*red)[kGemvTokV2][64] = reinterpret_cast<float (*)[kGemvTokV2][64]>(dyn);   // over the rows
   const int nrb = H >> 6;
   const int nunits = (nrb + rpu - 1) / rpu;
   int item_i, u;
-  if (!gemv_work(misc, (int)blockIdx.x - nn, nsh, nunits, item_i, u)) return;
+  if (!gemv_work(misc, b, nsh, nunits, item_i, u)) return;
   const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + 2 * item_i));
   const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
   const bool sh = e == E;
@@ -1491,6 +1526,7 @@ void gemv_down_kernel(
 #pragma unroll
     for (int t = 0; t < kGemvTokV2; ++t) acc[0][t] = 0.f;
     if (busy) st.run<kGemvTokV2, false>(hl, hrow, 0, hsl, G2, nt, acc);
+    __syncthreads();   // the staged rows are consumed: red overlays them
 #pragma unroll
     for (int t = 0; t < kGemvTokV2; ++t)
       if (t < nt) red[wave][t][lane] = acc[0][t];
@@ -1694,15 +1730,19 @@ struct ExpertPtrs {
   int ni;
 };
 
-// Token rows per streaming pass: at most kGemvTokV2, never more than T, and
-// few enough that the staged rows fit 64 KB of LDS.
+// Token rows per streaming pass: at most kGemvTokV2, never more than T nor
+// than the rows a streaming item can have (mfma_min_rows - 1), and few
+// enough that the staged rows fit 56 KB of LDS.  (The LDS a workgroup asks
+// for is sized by it, and decides how many workgroups a CU holds.)
 static int gemv_tokens_per_pass(const LayerDev& d, int T) {
   const int imax = d.Is > d.I ? d.Is : d.I;
   const int wmax = d.H > imax ? d.H : imax;
   const int row_bytes = wmax * 4 + (wmax / 64) * 8;   // fp32 input: hi + lo halves, group sums
   int mt = kGemvTokV2;
   while (mt > 1 && mt * row_bytes > 56 * 1024) --mt;
-  return T < mt ? T : mt;
+  if (mt > T) mt = T;
+  if (mt > d.mfma_min_rows - 1) mt = d.mfma_min_rows - 1;
+  return mt < 1 ? 1 : mt;
 }
 
 static ExpertPtrs expert_ptrs(const LayerDev& d, int T) {
@@ -1735,6 +1775,13 @@ static MfmaArgs mfma_args(const LayerDev& d, int T);
 // LDS bytes of a narrow matrix-core tile run inside a streaming launch
 constexpr size_t kNarrowLds = sizeof(NarrowRed) * kMfmaWaves + 32 * sizeof(int);
 
+// The shared expert's 32-row tiles, when it takes that path (the bucketing
+// pass lists them last).
+static int narrow_shared_tiles(const LayerDev& d, int T) {
+  const bool narrow = d.has_shared && T >= d.mfma_min_rows && T < d.wide_min_rows;
+  return narrow ? (T + kNarrowBM - 1) / kNarrowBM : 0;
+}
+
 hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
@@ -1742,15 +1789,17 @@ hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const int nsh1 = shared_streams(d, T) ? d.Is / 64 : 0, nrb = d.I / 64;
   const int units1 = nsh1 + routed_stream_items(d, T) * nrb;   // one row block per unit
   // narrow matrix-core tiles (experts with a few tens of rows) in the same
-  // launch: 32 columns per workgroup
-  const int imax = d.Is > d.I ? d.Is : d.I;
-  const int ncb = imax / 32, nn = ncb * narrow_tiles_max(d, T);
+  // launch: 32 gate+up columns per workgroup
+  const int nsht = narrow_shared_tiles(d, T), ncbs = d.Is / 32, ncbr = d.I / 32;
+  const int nn = nsht * ncbs + (narrow_tiles_max(d, T) - nsht) * ncbr;
   if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
   // many workgroups: one matrix per wave (more resident workgroups to hide
   // each one's staging); few: both matrices per wave (shorter per-wave
   // chain).  One row block per unit: two (one wave per row block and matrix)
   // measured 1.3x slower at 16 tokens.
   const bool split = units1 >= 1024;
+  const size_t red_bytes = (size_t)(split ? 1 : 2) * kGemvWaves * kGemvTokV2 * 64 * 4;
+  if (lds < red_bytes) lds = red_bytes;
   const int rpw = 1;
   const int nunits = (nrb + rpw - 1) / rpw;
   const int nsh = nsh1 ? (nsh1 + rpw - 1) / rpw : 0;
@@ -1759,15 +1808,18 @@ hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
                      : (split ? gemv_up_kernel<false, true> : gemv_up_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3(nn + units), dim3(kGemvThreads), lds, s, d.bank, d.stride,
                      d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs, p.items, p.misc,
-                     p.slots, p.hbuf, p.hs, nsh, nunits, rpw, mt, mfma_args(d, T), nn, ncb);
+                     p.slots, p.hbuf, p.hs, nsh, nunits, rpw, mt, mfma_args(d, T), nsht, ncbs,
+                     ncbr);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
-  const int imax = d.Is > d.I ? d.Is : d.I;
-  const size_t lds = (size_t)mt * (imax / 2 + 2 * (imax / 64)) * 4;
+  const int imax = shared_streams(d, T) && d.Is > d.I ? d.Is : d.I;   // longest streamed K
+  size_t lds = (size_t)mt * (imax / 2 + 2 * (imax / 64)) * 4;
+  const size_t red_bytes = (size_t)kGemvWaves * kGemvTokV2 * 64 * 4;
+  if (lds < red_bytes) lds = red_bytes;
   // routed experts: several row blocks per workgroup, one or two waves per
   // block, so a workgroup's fixed costs cover more weights
   const int nrb = d.H / 64, nsh = shared_streams(d, T) ? nrb : 0;
@@ -1775,12 +1827,11 @@ hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
   const int rpu = G2 <= 24 ? kGemvWaves / 2 : 1;
   const int units = nsh + routed_stream_items(d, T) * ((nrb + rpu - 1) / rpu);
   const int ncb = d.H / 64, nn = ncb * narrow_tiles_max(d, T);   // narrow down tiles, 64 columns
-  size_t ldsn = lds;
-  if (nn > 0 && ldsn < kNarrowLds) ldsn = kNarrowLds;
-  hipLaunchKernelGGL(gemv_down_kernel, dim3(nn + units), dim3(kGemvThreads), ldsn, s, d.bank,
+  if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
+  hipLaunchKernelGGL(gemv_down_kernel, dim3(nn + units), dim3(kGemvThreads), lds, s, d.bank,
                      d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.items, p.misc, p.slots,
                      reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, nsh, rpu, mt,
-                     mfma_args(d, T), nn, ncb);
+                     mfma_args(d, T), narrow_shared_tiles(d, T), ncb);
   return hipGetLastError();
 }
 
