@@ -92,7 +92,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.ntiles = take(((Tk + kNarrowBM - 1) / kNarrowBM + E + (T + kNarrowBM - 1) / kNarrowBM + 1) * 8);
   L.pred = take(Tk * 4);
   L.hbuf = take((Tk * I + Ts * Is) * 2);
-  L.hs = take((Tk * (I / 64) + Ts * (Is / 64)) * 8);
+  L.hs = take((Tk * (I / 32) + Ts * (Is / 32)) * 8);   // (S1, S2) per 32-column half
   L.yslot = take((Tk + Ts) * H * 4);
   L.xn = take((c.flags & MOE_F_RMSNORM) ? T * H * 4 : 0);
   L.total = o;
@@ -170,6 +170,13 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
     moe_close(c);
     return MOE_EHIP;
   }
+  int n_cu = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, cfg->device) != hipSuccess ||
+      n_cu <= 0) {
+    moe_close(c);
+    return MOE_EHIP;
+  }
+  d.n_cu = n_cu;
   *out = c;
   return MOE_OK;
 }

@@ -72,6 +72,7 @@ struct LayerDev {
   int H, E, Epad, k, I, Is, has_shared, rmsnorm, max_tokens;
   int mfma_min_rows;   // rows at which an expert leaves the streaming path
   int wide_min_rows;   // rows at which it uses 128-row instead of 32-row tiles
+  int n_cu;            // compute units of the device
   // workspace
   uint8_t* ws;
   WsLayout L;

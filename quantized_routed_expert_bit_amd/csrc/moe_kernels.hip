@@ -712,21 +712,33 @@ __device__ __forceinline__ size_t h_off(int slot, int Tk, int I, int Is) {
 __device__ __forceinline__ size_t hs_off(int slot, int Tk, int I, int Is) {
   return slot < Tk ? (size_t)slot * (I >> 6) : (size_t)Tk * (I >> 6) + (size_t)(slot - Tk) * (Is >> 6);
 }
+// (S1, S2) of 64-column group o of the h rows: the gate/up pass writes one
+// pair per 32-column half (float2 entries 2o and 2o + 1), summed here in
+// that order
+__device__ __forceinline__ float2 hs_group(const float2* hs2, size_t o) {
+  const float2 a = hs2[2 * o], b = hs2[2 * o + 1];
+  return make_float2(a.x + b.x, a.y + b.y);
+}
 
 // One wave's share of a row-per-lane streaming GEMV: NMAT matrices (gate and
 // up, or down) over the groups [gbeg, gend) of one 64-row block, for nt <= MT
 // token rows held in LDS.  Weight tiles are loaded P groups ahead, so P*NMAT
-// 2.3 KB tiles per wave are in flight while earlier ones are consumed.
+// tiles per wave are in flight while earlier ones are consumed.
 // The staged activations x~ hold the odd columns divided by 16 and the lifted
 // codes of those columns are 1024 + 16q, so dot(x~, lifted) = 1024 S1 + sum(q x)
 // with S1 = sum(x~) and S2 = sum(x) (both per group, in xsl):
 // acc[m][t] += sum over the groups of (s * dot - 1024 s * S1 + b * S2).
+// HALF: the wave covers 32 rows of the tile, lane l taking row `row` and the
+// 32-column half hh = l / 32 of each group; both halves of a row are summed
+// after the loop, and only the hh = 0 lane adds the b and S1 terms.
 // With LO, each staged row holds fp16 hi halves then lo halves (fp32 input);
 // both enter the same dot product, and the sums cover hi + lo.
-template <int NMAT, int P>
+template <int NMAT, int P, bool HALF = false>
 struct GemvStream {
   const uint8_t* mat[NMAT];
   int gbeg, gend, lane;
+  int gstr = 1;   // group stride: the wave takes gbeg, gbeg + gstr, ... below gend
+  int row = 0, hh = 0;   // HALF: the lane's row of the tile and column half
   uint4 c0[P][NMAT], c1[P][NMAT];
   uint32_t sb[P][NMAT];
 
@@ -734,39 +746,48 @@ struct GemvStream {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       const uint8_t* t = mat[m] + (size_t)g * kQ4TileBytes;
-      c0[p][m] = ld16(t + lane * 16);
-      c1[p][m] = ld16(t + 1024 + lane * 16);
-      sb[p][m] = ld4(t + kQ4CodeBytes + lane * 4);
+      if (HALF) {
+        c0[p][m] = ld16(t + hh * 1024 + row * 16);
+        sb[p][m] = ld4(t + kQ4CodeBytes + row * 4);
+      } else {
+        c0[p][m] = ld16(t + lane * 16);
+        c1[p][m] = ld16(t + 1024 + lane * 16);
+        sb[p][m] = ld4(t + kQ4CodeBytes + lane * 4);
+      }
     }
   }
   // Issue the first P groups' loads.  Every load is unconditional (a group
   // index past the end is clamped to the last group) so the number of loads
   // in flight is static and the compiler waits only for the buffer it reads.
   // Requires gbeg < gend.
+  __device__ __forceinline__ int glast() const { return gbeg + ((gend - 1 - gbeg) / gstr) * gstr; }
   __device__ __forceinline__ void prefetch() {
 #pragma unroll
-    for (int p = 0; p < P; ++p) load(p, min(gbeg + p, gend - 1));
+    for (int p = 0; p < P; ++p) load(p, min(gbeg + p * gstr, glast()));
   }
   template <int MT, bool LO>
   __device__ __forceinline__ void run(const uint32_t* xl, int xrow_dw, int lo_dw, const float2* xsl,
                                       int G, int nt, float (&acc)[NMAT][MT]) {
     const Lift L;
-    for (int g0 = gbeg; g0 < gend; g0 += P) {
+    constexpr int NW = HALF ? 16 : 32;   // lifted dwords per lane per group
+    const int gl = glast();
+    const bool fold = !HALF || hh == 0;
+    for (int g0 = gbeg; g0 < gend; g0 += P * gstr) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        const int g = g0 + p;
+        const int g = g0 + p * gstr;
         {
-          uint32_t w[NMAT][32];
+          uint32_t w[NMAT][NW];
           float s[NMAT], bb[NMAT], cf[NMAT];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) {
             unpack16_q4s(L, c0[p][m], w[m]);
-            unpack16_q4s(L, c1[p][m], w[m] + 16);
+            if (!HALF) unpack16_q4s(L, c1[p][m], w[m] + 16);
             s[m] = f16f(sb[p][m] & 0xffffu);
-            bb[m] = f16f(sb[p][m] >> 16);
-            cf[m] = -1024.f * s[m];
+            bb[m] = fold ? f16f(sb[p][m] >> 16) : 0.f;
+            cf[m] = fold ? -1024.f * s[m] : 0.f;
           }
-          load(p, min(g + P, gend - 1));
+          load(p, min(g + P * gstr, gl));
           if (g < gend) {
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
@@ -777,9 +798,10 @@ struct GemvStream {
 #pragma unroll
               for (int half = 0; half < (LO ? 2 : 1); ++half) {
                 const uint4* xp =
-                    reinterpret_cast<const uint4*>(xl + t * xrow_dw + half * lo_dw + g * 32);
+                    reinterpret_cast<const uint4*>(xl + t * xrow_dw + half * lo_dw + g * 32) +
+                    (HALF ? hh * 4 : 0);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < NW / 4; ++i) {
                   const uint4 xv = xp[i];
 #pragma unroll
                   for (int m = 0; m < NMAT; ++m) {
@@ -1310,18 +1332,20 @@ __device__ __forceinline__ void stage_rows(uint32_t* dst, int dst_row_dw, int nt
 }
 
 // Streaming gate/up: workgroup = (work item, 64-row block of the expert's
-// intermediate dimension); its waves split the H/64 groups; token rows of x
-// (fp16 in the paired order) and their group sums are staged in LDS.  The
-// item and its slots are scalar loads; the weight prefetch is issued before
-// the token rows are staged.
-template <bool LO, bool SPLIT>
+// intermediate dimension, or with HALF a 32-row half of one); its waves split
+// the H/64 groups; token rows of x (fp16 in the paired order) and their group
+// sums are staged in LDS.  The item and its slots are scalar loads; the
+// weight prefetch is issued before the token rows are staged.  HALF units
+// (each lane one row and one 32-column half of every group) double the
+// workgroups when the 64-row units would leave CUs idle.
+template <bool LO, bool SPLIT, bool HALF>
 __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(SPLIT && !LO ? 4 : 1)))
 void gemv_up_kernel(
     const uint8_t* __restrict__ bank, uint64_t stride, const uint8_t* __restrict__ shared,
     int H, int E, int k, int I, int Is, int T, const uint32_t* __restrict__ x16,
     const uint32_t* __restrict__ x16lo, const float* __restrict__ xs,
     const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
-    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nunits, int rpw, int mt,
+    uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nunits, int mt,
     MfmaArgs ma, int nsht, int ncbs, int ncbr) {
   extern __shared__ uint32_t dyn[];
   // the narrow matrix-core tiles run in the first workgroups, so both
@@ -1335,15 +1359,14 @@ void gemv_up_kernel(
   // per-wave partial sums, in LDS over the staged rows once they are consumed
   float (*red)[kGemvWaves][kGemvTokV2][64] =
       reinterpret_cast<float (*)[kGemvWaves][kGemvTokV2][64]>(dyn);
-  // a unit is rpw consecutive 64-row blocks of one item (rpw = 2 only with SPLIT)
   int item_i, u;
   if (!gemv_work(misc, b, nsh, nunits, item_i, u)) return;
   const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + 2 * item_i));
   const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
   const bool sh = e == E;
   const int inter = sh ? Is : I;
-  const int rb0 = u * rpw, nrb_i = inter >> 6;
-  if (rb0 >= nrb_i) return;
+  const int rb = HALF ? u >> 1 : u, rh = HALF ? u & 1 : 0, nrb_i = inter >> 6;
+  if (rb >= nrb_i) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = H >> 6, Tk = T * k;
   const int xrow = LO ? H : H >> 1;               // dwords per staged row (hi [+ lo])
@@ -1351,25 +1374,23 @@ void gemv_up_kernel(
   float2* xsl = reinterpret_cast<float2*>(dyn + mt * xrow);   // [mt][G] (S1, S2)
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
   const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
-  // SPLIT: each row block's waves are half gate, half up (fewer registers
-  // per wave, more workgroups per CU); with rpw = 2 that is one wave per
-  // (row block, matrix) streaming all groups.  Else every wave streams both
-  // matrices.  The waves of a (row block, matrix) split the groups.
+  // SPLIT: half the waves stream gate, half up (fewer registers per wave,
+  // more workgroups per CU).  Else every wave streams both matrices.  The
+  // waves of a matrix split the groups.
   constexpr int NM = SPLIT ? 1 : 2;
-  const int wpr = kGemvWaves / rpw;                    // waves per row block
-  const int wpm = SPLIT ? wpr / 2 : wpr;               // waves per matrix
-  const int r = wave / wpr, wq = wave - r * wpr;
-  const int mat = SPLIT ? wq / wpm : 0, wk = wq - mat * wpm;
-  const int rb = rb0 + r;
-  GemvStream<NM, kGemvP> st;
-  st.mat[0] = rec + kHeaderBytes + (size_t)mat * sec + (size_t)min(rb, nrb_i - 1) * G * kQ4TileBytes;
+  constexpr int wpm = SPLIT ? kGemvWaves / 2 : kGemvWaves;   // waves per matrix
+  const int mat = SPLIT ? wave / wpm : 0, wk = wave - mat * wpm;
+  GemvStream<NM, kGemvP, HALF> st;
+  st.mat[0] = rec + kHeaderBytes + (size_t)mat * sec + (size_t)rb * G * kQ4TileBytes;
   if (!SPLIT) st.mat[NM - 1] = st.mat[0] + sec;
   st.gbeg = (G * wk) / wpm;
   st.gend = (G * (wk + 1)) / wpm;
   st.lane = lane;
+  st.row = rh * 32 + (lane & 31);
+  st.hh = lane >> 5;
   const cu32p sl = as_const(reinterpret_cast<const uint32_t*>(slots));
 
-  const bool busy = st.gbeg < st.gend && rb < nrb_i;
+  const bool busy = st.gbeg < st.gend;
   for (int p0 = 0; p0 < m; p0 += mt) {
     const int nt = min(mt, m - p0);
     if (p0 > 0) __syncthreads();
@@ -1420,30 +1441,46 @@ void gemv_up_kernel(
 #pragma unroll
         for (int q = 0; q < NM; ++q) red[q][wave][t][lane] = acc[q][t];
     __syncthreads();
-    // (row block, token) pairs over the waves; fixed-order sums over the
-    // waves of each matrix
-    for (int pr = wave; pr < rpw * nt; pr += kGemvWaves) {
-      const int rr = pr / nt, t = pr - rr * nt;
-      const int rbr = rb0 + rr;
-      if (rbr >= nrb_i) continue;
+    // one token per wave; fixed-order sums over the waves of each matrix
+    // (HALF: lane l < 32 adds row l's two column halves)
+    for (int t = wave; t < nt; t += kGemvWaves) {
+      const int l = HALF ? lane & 31 : lane;
       float gs = 0.f, us = 0.f;
+#pragma unroll
       for (int j = 0; j < wpm; ++j) {
-        gs += red[0][rr * wpr + j][t][lane];
-        us += SPLIT ? red[0][rr * wpr + wpm + j][t][lane] : red[NM - 1][rr * wpr + j][t][lane];
+        gs += red[0][j][t][l];
+        us += SPLIT ? red[0][wpm + j][t][l] : red[NM - 1][j][t][l];
+        if (HALF) {
+          gs += red[0][j][t][l + 32];
+          us += SPLIT ? red[0][wpm + j][t][l + 32] : red[NM - 1][j][t][l + 32];
+        }
       }
       const float hv = gs / (1.f + expf(-gs)) * us;
       // h in fp16, odd columns stored divided by 16 (the streaming down
       // pass stages them as they are); S1 sums what is stored, S2 the h
-      // those values stand for
+      // those values stand for, per 32-column half (the down pass adds the
+      // two halves of a group)
       const _Float16 h16 = (_Float16)hv;
-      const bool odd = lane & 1;
+      const bool odd = lane & 1, mine = !HALF || lane < 32;
       const _Float16 hst = odd ? (_Float16)((float)h16 * 0.0625f) : h16;
+      const float v1 = mine ? (float)hst : 0.f;
+      const float v2 = mine ? (odd ? 16.f * (float)hst : (float)hst) : 0.f;
       const int sv = slot[t];
-      const int col = rbr * 64 + lane;
-      hbuf[h_off(sv, Tk, I, Is) + pair_pos4(col)] = f16bits(hst);
-      const float s1 = wave_sum((float)hst);
-      const float s2 = wave_sum(odd ? 16.f * (float)hst : (float)hst);
-      if (lane == 0) reinterpret_cast<float2*>(hs)[hs_off(sv, Tk, I, Is) + rbr] = make_float2(s1, s2);
+      const int col = rb * 64 + rh * 32 + l;
+      if (mine) hbuf[h_off(sv, Tk, I, Is) + pair_pos4(col)] = f16bits(hst);
+      float2* hso = reinterpret_cast<float2*>(hs) + 2 * hs_off(sv, Tk, I, Is) + 2 * rb;
+      if (HALF) {
+        const float s1 = wave_sum(v1), s2 = wave_sum(v2);
+        if (lane == 0) hso[rh] = make_float2(s1, s2);
+      } else {
+        const bool lo32 = lane < 32;
+        const float s1a = wave_sum(lo32 ? v1 : 0.f), s2a = wave_sum(lo32 ? v2 : 0.f);
+        const float s1b = wave_sum(lo32 ? 0.f : v1), s2b = wave_sum(lo32 ? 0.f : v2);
+        if (lane == 0) {
+          hso[0] = make_float2(s1a, s2a);
+          hso[1] = make_float2(s1b, s2b);
+        }
+      }
     }
   }
 }
@@ -1514,13 +1551,13 @@ void gemv_down_kernel(
     const int nhs = nt * G2;
     const int i0 = min(tid, nhs - 1);
     const float2* hs2 = reinterpret_cast<const float2*>(hs);
-    const float2 hs0 = hs2[hs_off(slot[i0 / G2], Tk, I, Is) + (i0 % G2)];
+    const float2 hs0 = hs_group(hs2, hs_off(slot[i0 / G2], Tk, I, Is) + (i0 % G2));
     stage_rows<false>(hl, hrow, nt, inter >> 3, [=](int t) {
       return reinterpret_cast<const uint4*>(hbuf32 + (h_off(slot[t], Tk, I, Is) >> 1));
     });
     hsl[i0] = hs0;
     for (int i = tid + kGemvThreads; i < nhs; i += kGemvThreads)
-      hsl[i] = hs2[hs_off(slot[i / G2], Tk, I, Is) + (i % G2)];
+      hsl[i] = hs_group(hs2, hs_off(slot[i / G2], Tk, I, Is) + (i % G2));
     __syncthreads();
     float acc[1][kGemvTokV2];
 #pragma unroll
@@ -1786,8 +1823,13 @@ hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
   size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + 2 * (d.H / 64)) * 4;
-  const int nsh1 = shared_streams(d, T) ? d.Is / 64 : 0, nrb = d.I / 64;
-  const int units1 = nsh1 + routed_stream_items(d, T) * nrb;   // one row block per unit
+  // units: 64-row blocks, or their 32-row halves while the 64-row units
+  // would not give every CU two workgroups
+  const int units64 = (shared_streams(d, T) ? d.Is / 64 : 0) + routed_stream_items(d, T) * (d.I / 64);
+  const bool half = units64 < 2 * d.n_cu;
+  const int rpu = half ? 32 : 64;
+  const int nsh = shared_streams(d, T) ? d.Is / rpu : 0, nunits = d.I / rpu;
+  const int units = nsh + routed_stream_items(d, T) * nunits;
   // narrow matrix-core tiles (experts with a few tens of rows) in the same
   // launch: 32 gate+up columns per workgroup
   const int nsht = narrow_shared_tiles(d, T), ncbs = d.Is / 32, ncbr = d.I / 32;
@@ -1795,21 +1837,18 @@ hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
   // many workgroups: one matrix per wave (more resident workgroups to hide
   // each one's staging); few: both matrices per wave (shorter per-wave
-  // chain).  One row block per unit: two (one wave per row block and matrix)
-  // measured 1.3x slower at 16 tokens.
-  const bool split = units1 >= 1024;
+  // chain)
+  const bool split = units64 >= 1024;
   const size_t red_bytes = (size_t)(split ? 1 : 2) * kGemvWaves * kGemvTokV2 * 64 * 4;
   if (lds < red_bytes) lds = red_bytes;
-  const int rpw = 1;
-  const int nunits = (nrb + rpw - 1) / rpw;
-  const int nsh = nsh1 ? (nsh1 + rpw - 1) / rpw : 0;
-  const int units = nsh + routed_stream_items(d, T) * nunits;
-  auto* kern = x_f32 ? (split ? gemv_up_kernel<true, true> : gemv_up_kernel<true, false>)
-                     : (split ? gemv_up_kernel<false, true> : gemv_up_kernel<false, false>);
+  // (split implies 64-row units: 1024 of them exceed the 32-row threshold)
+  auto* kern = x_f32 ? (split ? gemv_up_kernel<true, true, false>
+                              : half ? gemv_up_kernel<true, false, true> : gemv_up_kernel<true, false, false>)
+                     : (split ? gemv_up_kernel<false, true, false>
+                              : half ? gemv_up_kernel<false, false, true> : gemv_up_kernel<false, false, false>);
   hipLaunchKernelGGL(kern, dim3(nn + units), dim3(kGemvThreads), lds, s, d.bank, d.stride,
                      d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs, p.items, p.misc,
-                     p.slots, p.hbuf, p.hs, nsh, nunits, rpw, mt, mfma_args(d, T), nsht, ncbs,
-                     ncbr);
+                     p.slots, p.hbuf, p.hs, nsh, nunits, mt, mfma_args(d, T), nsht, ncbs, ncbr);
   return hipGetLastError();
 }
 
