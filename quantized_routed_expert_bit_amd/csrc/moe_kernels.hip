@@ -122,27 +122,6 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ int dpp_i(int old, int src) {
   return __builtin_amdgcn_update_dpp(old, src, CTRL, ROWS, 0xF, false);
 }
-template <int CTRL, int ROWS>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = __builtin_bit_cast(float, dpp_i<CTRL, ROWS>(__builtin_bit_cast(int, v),
-                                                               __builtin_bit_cast(int, v)));
-  const int oi = dpp_i<CTRL, ROWS>(i, i);
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
-}
-// (value desc, index asc) maximum over the wave; every lane gets the winner.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_step<0xB1, 0xF>(v, i);
-  argmax_step<0x4E, 0xF>(v, i);
-  argmax_step<0x141, 0xF>(v, i);
-  argmax_step<0x140, 0xF>(v, i);
-  argmax_step<0x142, 0xA>(v, i);
-  argmax_step<0x143, 0xC>(v, i);
-  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-  i = __builtin_amdgcn_readlane(i, 63);
-}
 // Inclusive prefix sum over the wave (lane order).
 __device__ __forceinline__ int wave_incl_scan(int x) {
   x += dpp_i<0x111, 0xF>(0, x);
@@ -363,6 +342,123 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   }
 }
 
+constexpr int kBucketWaveSmem = 7 * kMaxExperts * 4 + kMaxExperts;
+
+// Bucketing by one wave, for a batch of at most 512 slots (decode: the top-k
+// workgroup buckets its own batch).  It builds the same lists as
+// bucket_tokens: lane l owns the experts [l*ne, (l+1)*ne) and the slots l,
+// l + 64, ...; expert offsets and list positions are DPP scans of per-lane
+// counts, and the LDS operations of one wave complete in order, so there is
+// no barrier.  Matrix-core tiles are listed in expert order, the shared
+// expert's last.  `ids` may be in LDS (the caller synchronizes before).
+__device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) {
+  if (threadIdx.x >= 64) return;
+  int* s_cnt = reinterpret_cast<int*>(smem);   // [E]
+  int* s_off = s_cnt + kMaxExperts;             // [E]
+  int* s_cur = s_off + kMaxExperts;             // [E] placement cursors
+  int* s_first = s_cur + kMaxExperts;           // [E][4] first slots per expert
+  unsigned char* s_pred = reinterpret_cast<unsigned char*>(s_first + 4 * kMaxExperts);   // [E]
+  const int lane = threadIdx.x, E = a.E, Tk = a.T * a.k;
+  const int R = a.mfma_min_rows, W = a.wide_min_rows;
+  const int ne = (E + 63) >> 6, e0 = min(E, lane * ne), e1 = min(E, e0 + ne);
+  const int pv = a.misc[kPredValid];
+  for (int e = e0; e < e1; ++e) {
+    s_cnt[e] = 0;
+    s_pred[e] = pv ? 0 : 1;   // with a lookahead prediction, predicted experts first
+  }
+  for (int s0 = lane; s0 < pv; s0 += 64) {
+    const int v = a.pred[s0];
+    if (v >= 0 && v < E) s_pred[v] = 1;
+  }
+  for (int s0 = lane; s0 < Tk; s0 += 64) atomicAdd(&s_cnt[ids[s0]], 1);
+  // expert offsets: a run over the lane's experts above a wave scan of the
+  // lane totals
+  int tot = 0;
+  for (int e = e0; e < e1; ++e) tot += s_cnt[e];
+  int run = wave_incl_scan(tot) - tot;
+  for (int e = e0; e < e1; ++e) {
+    const int c = s_cnt[e];
+    a.offs[e] = run;
+    s_off[e] = run;
+    s_cur[e] = run;
+    run += c;
+  }
+  if (lane == 0) a.offs[E] = Tk;
+  for (int s0 = lane; s0 < Tk; s0 += 64) {
+    const int e = ids[s0];
+    const int pos = atomicAdd(&s_cur[e], 1), r = pos - s_off[e];
+    a.slots[pos] = s0;
+    if (r < 4) s_first[e * 4 + r] = s0;
+  }
+  if (a.has_shared)
+    for (int t = lane; t < a.T; t += 64) a.slots[Tk + t] = Tk + t;
+  // per-lane counts, packed: streaming and matrix-core items (predicted in
+  // the low 16 bits, the rest in the high 16), 128-row tiles (low) and
+  // 32-row tiles (high); every total is below 2^16
+  int ng = 0, nm = 0, ntl = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = s_cnt[e], inc = s_pred[e] ? 1 : 0x10000;
+    if (c > 0 && c < R) ng += inc;
+    if (c >= R) {
+      nm += inc;
+      ntl += c >= W ? (c + kMfmaBM - 1) / kMfmaBM : ((c + kNarrowBM - 1) / kNarrowBM) << 16;
+    }
+  }
+  const int ig = wave_incl_scan(ng), im = wave_incl_scan(nm), it = wave_incl_scan(ntl);
+  const int tg = __builtin_amdgcn_readlane(ig, 63), tm = __builtin_amdgcn_readlane(im, 63);
+  const int tt = __builtin_amdgcn_readlane(it, 63);
+  const int xg = ig - ng, xm = im - nm, xt = it - ntl;
+  int pg0 = xg & 0xffff, pg1 = (tg & 0xffff) + (xg >> 16);
+  int pm0 = xm & 0xffff, pm1 = (tm & 0xffff) + (xm >> 16);
+  int pw = xt & 0xffff, pn = xt >> 16;
+  for (int e = e0; e < e1; ++e) {
+    const int c = s_cnt[e];
+    if (c == 0) continue;
+    const bool first = s_pred[e] != 0;
+    if (c < R) {   // streaming item: (expert, rows, offset) + its first 4 slots
+      const int pos = first ? pg0++ : pg1++;
+      const int* f = s_first + e * 4;
+      a.items[2 * pos] = make_int4(e, c, s_off[e], 0);
+      a.items[2 * pos + 1] = make_int4(f[0], f[min(1, c - 1)], f[min(2, c - 1)], f[min(3, c - 1)]);
+    } else {
+      const int pos = first ? pm0++ : pm1++;
+      a.mitems[pos] = make_int4(e, c, s_off[e], 0);
+      if (c >= W)
+        for (int j = 0; j * kMfmaBM < c; ++j) a.mtiles[pw++] = make_int2(pos, j * kMfmaBM);
+      else
+        for (int j = 0; j * kNarrowBM < c; ++j) a.ntiles[pn++] = make_int2(pos, j * kNarrowBM);
+    }
+  }
+  int n_gemv = (tg & 0xffff) + (tg >> 16), n_mfma = (tm & 0xffff) + (tm >> 16);
+  int n_tiles = tt & 0xffff, n_narrow = tt >> 16;
+  if (a.has_shared) {   // the shared expert: last item of its path, its tiles last
+    const int T = a.T;
+    if (T >= R) {
+      const bool wide = T >= W;
+      const int bm = wide ? kMfmaBM : kNarrowBM, nt = (T + bm - 1) / bm;
+      int2* out = wide ? a.mtiles + n_tiles : a.ntiles + n_narrow;
+      if (lane == 0) a.mitems[n_mfma] = make_int4(E, T, Tk, 0);
+      for (int j = lane; j < nt; j += 64) out[j] = make_int2(n_mfma, j * bm);
+      ++n_mfma;
+      if (wide) n_tiles += nt; else n_narrow += nt;
+    } else {
+      if (lane == 0) {
+        a.items[2 * n_gemv] = make_int4(E, T, Tk, 0);
+        a.items[2 * n_gemv + 1] = make_int4(Tk, Tk + min(1, T - 1), Tk + min(2, T - 1), Tk + min(3, T - 1));
+      }
+      ++n_gemv;
+    }
+  }
+  if (lane == 0) {
+    a.misc[kNGemv] = n_gemv;
+    a.misc[kNMfma] = n_mfma;
+    a.misc[kNTiles] = n_tiles;
+    a.misc[kNNarrow] = n_narrow;
+    a.misc[kPredValid] = 0;
+    a.misc[kCntAll] = 0;
+  }
+}
+
 // Router GEMV: workgroup = (64-expert row block, k-split of kRouterGPW groups,
 // token block of up to kRouterTokMax tokens).  Writes one fp32 partial logit
 // per (k-split, token, expert); the rb == 0 workgroups also publish x in fp16
@@ -543,92 +639,124 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouterArgs a) {
   }
 }
 
-// Top-k: workgroup = TPW tokens (TPW * Epad <= 512).  Sums the k-split
-// partials in fixed order (all loads of a thread issued together), adds the
-// logit bias, then one wave per token selects k experts by (logit desc,
-// index asc) with wave64 shuffles and takes the softmax over them.
-// Selection key of expert e with logit v: the float's order-preserving bit
-// pattern above ~e, so that the largest key is the largest logit and, among
-// equal logits, the lowest index.  0 is below every real key.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+// Maximum / minimum over each group of LPT lanes (16: one DPP row; 64: the
+// wave); every lane of the group gets it.
+template <int LPT>
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+#define QREB_GROUP_STEP(OP, C, R) v = OP(v, (uint32_t)dpp_i<C, R>((int)v, (int)v))
+  QREB_GROUP_STEP(max, 0xB1, 0xF);
+  QREB_GROUP_STEP(max, 0x4E, 0xF);
+  QREB_GROUP_STEP(max, 0x141, 0xF);
+  QREB_GROUP_STEP(max, 0x140, 0xF);
+  if constexpr (LPT == 64) {
+    QREB_GROUP_STEP(max, 0x142, 0xA);
+    QREB_GROUP_STEP(max, 0x143, 0xC);
+    v = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  }
+  return v;
 }
-__device__ __forceinline__ float topk_key_value(uint64_t key) {
-  const uint32_t o = (uint32_t)(key >> 32);
+template <int LPT>
+__device__ __forceinline__ uint32_t group_umin(uint32_t v) {
+  QREB_GROUP_STEP(min, 0xB1, 0xF);
+  QREB_GROUP_STEP(min, 0x4E, 0xF);
+  QREB_GROUP_STEP(min, 0x141, 0xF);
+  QREB_GROUP_STEP(min, 0x140, 0xF);
+  if constexpr (LPT == 64) {
+    QREB_GROUP_STEP(min, 0x142, 0xA);
+    QREB_GROUP_STEP(min, 0x143, 0xC);
+    v = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  }
+#undef QREB_GROUP_STEP
+  return v;
+}
+// Order-preserving unsigned image of a float (larger float, larger key;
+// -0 is never stored) and back.
+__device__ __forceinline__ uint32_t f2key(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t o) {
   return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-__device__ __forceinline__ int topk_key_index(uint64_t key) {
-  return (int)(0xFFFFFFFFu - (uint32_t)key);
-}
-template <int CTRL, int ROWS>
-__device__ __forceinline__ void key_max_step(uint64_t& key) {
-  const uint32_t lo = (uint32_t)dpp_i<CTRL, ROWS>((int)(uint32_t)key, (int)(uint32_t)key);
-  const uint32_t hi = (uint32_t)dpp_i<CTRL, ROWS>((int)(uint32_t)(key >> 32), (int)(uint32_t)(key >> 32));
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  key = o > key ? o : key;
-}
-// Maximum key over each group of LPT lanes (16: one DPP row; 64: the wave);
-// every lane of the group gets it.
-template <int LPT>
-__device__ __forceinline__ uint64_t group_key_max(uint64_t key) {
-  key_max_step<0xB1, 0xF>(key);
-  key_max_step<0x4E, 0xF>(key);
-  key_max_step<0x141, 0xF>(key);
-  key_max_step<0x140, 0xF>(key);
-  if constexpr (LPT == 64) {
-    key_max_step<0x142, 0xA>(key);
-    key_max_step<0x143, 0xC>(key);
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)key, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
-    key = ((uint64_t)hi << 32) | lo;
-  }
-  return key;
+// a where m is all ones, else b (one v_bfi_b32)
+__device__ __forceinline__ uint32_t pick(uint32_t m, uint32_t a, uint32_t b) {
+  return (a & m) | (b & ~m);
 }
 
-// Top-k of the logits of nt tokens held in LDS (s_lg[t * Epad + e]).  A group
-// of LPT lanes owns one token, lane l holding experts l + LPT*i (i < NV); the
-// k winners come out one at a time as group maxima of the per-lane best key.
-// The softmax over the selected logits is summed in selection order.
+// Top-k of the logits of nt tokens held in LDS (s_lg[t * Epad + e]; padding
+// experts hold -inf, a NaN logit was stored as -inf, -0 as +0).  A group of
+// LPT lanes owns one token, lane l holding experts l + LPT*i (i < NV), first
+// sorted by logit, descending, within the lane (a stable sort, so equal
+// logits stay in index order).  Each of the k rounds takes the group maximum
+// of the lanes' heads, the lowest expert index among the heads equal to it
+// (ties go to the lowest index), and shifts the winning lane's list by one.
+// The softmax over the selected logits is summed in selection order; the
+// token's LDS row is reused for the exponentials.
 template <int LPT, int NV>
-__device__ void topk_select(const RouterArgs& a, const float* s_lg, int* s_ids, int nt, int t0) {
-  constexpr int NG = 256 / LPT;          // token groups per workgroup
+__device__ void topk_select(const RouterArgs& a, float* s_lg, int* s_ids, int nt, int t0) {
+  constexpr int NG = 256 / LPT;             // token groups per workgroup
+  constexpr uint32_t kNone = 0xFFFFFFFFu;   // index of an exhausted list entry
   const int tid = threadIdx.x, l = tid % LPT;
   for (int t = tid / LPT; t < nt; t += NG) {
-    uint64_t key[NV];
+    uint32_t v[NV], id[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e = l + LPT * i;
-      key[i] = e < a.E ? topk_key(s_lg[t * a.Epad + e], e) : 0ull;
+      id[i] = (uint32_t)(l + LPT * i);
+      v[i] = f2key((int)id[i] < a.Epad ? s_lg[t * a.Epad + id[i]] : -INFINITY);
     }
-    uint64_t mine = 0, first = 0;
-    float sum = 0.f;
+    // odd-even transposition sort (adjacent swaps on strictly larger keys:
+    // stable)
+#pragma unroll
+    for (int r = 0; r < NV; ++r)
+#pragma unroll
+      for (int i = r & 1; i + 1 < NV; i += 2) {
+        const uint32_t m = v[i + 1] > v[i] ? kNone : 0u;
+        const uint32_t va = v[i], vb = v[i + 1], ia = id[i], ib = id[i + 1];
+        v[i] = pick(m, vb, va);
+        v[i + 1] = pick(m, va, vb);
+        id[i] = pick(m, ib, ia);
+        id[i + 1] = pick(m, ia, ib);
+      }
+    uint32_t first = 0, mine = 0, mine_id = 0;
     for (int j = 0; j < a.k; ++j) {
-      uint64_t best = key[0];
+      const uint32_t gm = group_umax<LPT>(v[0]);
+      const uint32_t cand = v[0] == gm ? id[0] : kNone;
+      const uint32_t win = group_umin<LPT>(cand);
+      if (j == 0) first = gm;
+      if (l == j) {
+        mine = gm;
+        mine_id = win;
+      }
+      const uint32_t m = cand == win ? kNone : 0u;
 #pragma unroll
-      for (int i = 1; i < NV; ++i) best = key[i] > best ? key[i] : best;
-      best = group_key_max<LPT>(best);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) key[i] = key[i] == best ? 0ull : key[i];
-      if (j == 0) first = best;
-      if (l == j) mine = best;
-      sum += expf(topk_key_value(best) - topk_key_value(first));
+      for (int i = 0; i + 1 < NV; ++i) {
+        v[i] = pick(m, v[i + 1], v[i]);
+        id[i] = pick(m, id[i + 1], id[i]);
+      }
+      v[NV - 1] = pick(m, 0u, v[NV - 1]);   // key 0 sits below -inf
+      id[NV - 1] = pick(m, kNone, id[NV - 1]);
     }
+    // softmax: lane l < k holds the l-th selected logit; the exponentials go
+    // through the token's LDS row (one wave: in order) and are summed in
+    // selection order
+    float* ex = s_lg + t * a.Epad;
+    const float el = expf(key2f(mine) - key2f(first));
+    if (l < a.k) ex[l] = el;
+    float sum = 0.f;
+    for (int j = 0; j < a.k; ++j) sum += ex[j];
     if (l < a.k) {
       const int tok = t0 + t;
-      int id = topk_key_index(mine);
-      id = id >= 0 && id < a.E ? id : 0;   // always an expert index, whatever the inputs
+      const int idx = (int)mine_id < a.E ? (int)mine_id : 0;   // always an expert index
       const size_t o = (size_t)tok * a.k + l;
       if (a.mode == 0) {
-        const float pr = expf(topk_key_value(mine) - topk_key_value(first)) / sum;
-        a.ids_ws[o] = id;
+        const float pr = el / sum;
+        a.ids_ws[o] = idx;
         a.p_ws[o] = pr;
-        s_ids[t * a.k + l] = id;
-        if (a.ids_out) a.ids_out[o] = id;
+        s_ids[t * a.k + l] = idx;
+        if (a.ids_out) a.ids_out[o] = idx;
         if (a.p_out) a.p_out[o] = pr;
       } else {
-        a.pred[o] = id;
+        a.pred[o] = idx;
       }
     }
   }
@@ -648,32 +776,35 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a, int tpw)
   const int nt = min(tpw, a.T - t0);
   const int npair = nt * a.Epad;
   // every load unconditional (indices clamped into the buffer), so a batch of
-  // 4 pairs x 8 splits is in flight at once
-  for (int p0 = 0; p0 < npair; p0 += 1024) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int pt[4], pe[4];
+  // 8 pairs x 8 splits is in flight at once (one batch for 16 tokens x 128
+  // experts)
+  constexpr int NP = 8;
+  for (int p0 = 0; p0 < npair; p0 += 256 * NP) {
+    float acc[NP];
+    int pt[NP], pe[NP];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NP; ++j) {
+      acc[j] = 0.f;
       const int i = min(p0 + tid + 256 * j, npair - 1);
       pt[j] = i / a.Epad;
       pe[j] = i - pt[j] * a.Epad;
     }
     for (int k0 = 0; k0 < a.KS; k0 += 8) {
-      float pv[4][8];
+      float pv[NP][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NP; ++j)
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int ks = min(k0 + q, a.KS - 1);
           pv[j][q] = a.part[((size_t)ks * a.T + t0 + pt[j]) * a.Epad + pe[j]];
         }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NP; ++j)
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[j] += k0 + q < a.KS ? pv[j][q] : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NP; ++j) {
       const int i = p0 + tid + 256 * j;
       if (i < npair) {
         const int t = pt[j], e = pe[j];
@@ -692,10 +823,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a, int tpw)
   __syncthreads();
   topk_select<LPT, NV>(a, s_lg, s_ids, nt, t0);
   if (a.mode == 2 && blockIdx.x == 0 && tid == 0) a.misc[kPredValid] = a.T * a.k;
-  if (a.mode == 0 && gridDim.x == 1) {
-    __shared__ __align__(16) uint8_t smem[kBucketSmem];
+  if (a.mode == 0 && gridDim.x == 1) {   // at most kRouterTokMax * kMaxTopK = 512 slots
+    __shared__ __align__(16) uint8_t smem[kBucketWaveSmem];
     __syncthreads();
-    bucket_tokens(a, s_ids, smem);
+    bucket_wave(a, s_ids, smem);
   }
 }
 
@@ -1860,10 +1991,14 @@ hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
   const size_t red_bytes = (size_t)kGemvWaves * kGemvTokV2 * 64 * 4;
   if (lds < red_bytes) lds = red_bytes;
   // routed experts: several row blocks per workgroup, one or two waves per
-  // block, so a workgroup's fixed costs cover more weights
+  // block, so a workgroup's fixed costs cover more weights; four blocks (one
+  // wave each) once two-block units would exceed what the CUs hold at once
+  // while most routed experts stream (fewer than 4 rows on average)
   const int nrb = d.H / 64, nsh = shared_streams(d, T) ? nrb : 0;
   const int G2 = d.I / 64;
-  const int rpu = G2 <= 24 ? kGemvWaves / 2 : 1;
+  const int two = routed_stream_items(d, T) * ((nrb + 1) / 2);
+  const bool many = two > 8 * d.n_cu && T * d.k < 4 * d.E;
+  const int rpu = G2 > 24 ? 1 : many ? kGemvWaves : kGemvWaves / 2;
   const int units = nsh + routed_stream_items(d, T) * ((nrb + rpu - 1) / rpu);
   const int ncb = d.H / 64, nn = ncb * narrow_tiles_max(d, T);   // narrow down tiles, 64 columns
   if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
