@@ -19,8 +19,9 @@ EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
             "moe_router_logits", "moe_set_path_rows", "moe_close", "moe_strerror",
             "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
             "moe_profile_start", "moe_profile_read")
+# kernel timing slots of moe_profile_read (the last two are reserved)
 PROFILE_SLOTS = ("router", "gemv_up", "gemv_down", "mfma_up", "mfma_down", "combine",
-                 "narrow_up", "narrow_down")
+                 "reserved6", "reserved7")
 
 
 class MoeConfig(ctypes.Structure):

@@ -103,7 +103,8 @@ class MoELayer:
         calls = ctypes.c_int32()
         self._check(self.lib.moe_profile_read(self.ctx, arr, ctypes.byref(calls), n),
                     "moe_profile_read")
-        return dict(zip(L.PROFILE_SLOTS, list(arr))), calls.value
+        return ({k: v for k, v in zip(L.PROFILE_SLOTS, list(arr)) if not k.startswith("reserved")},
+                calls.value)
 
     def set_path_rows(self, mfma_min_rows, wide_min_rows=None):
         if wide_min_rows is None:
