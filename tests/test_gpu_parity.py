@@ -82,6 +82,22 @@ def test_layer_parity_decode(torch_dev, cfg):
                         p.cpu().numpy(), f"cfg{cfg} T={T}")
 
 
+def test_streaming_unit_layouts(torch_dev):
+    """Decode batch sizes that select each streaming layout at the decode
+    shape: 32-row gate/up units (2 tokens), 64-row units with both matrices
+    per wave (8), one matrix per wave with four-row-block down units (12)."""
+    wl = synth.WORKLOADS[1]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, 12)
+    ol = P.oracle_layer(li)
+    for T in (2, 8, 12):
+        P.log(f"cfg1 streaming layout T={T}")
+        xb = synth.make_hidden(0, 1, T, wl.shape.hidden, tag=11)
+        y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+        P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                        p.cpu().numpy(), f"cfg1 layout T={T}")
+
+
 @pytest.mark.parametrize("shape", [
     dict(H=320, E=65, k=3, I=128, Is=0, T=7),        # ragged router split, padded experts
     dict(H=128, E=16, k=16, I=64, Is=192, T=5),      # k = E: dense softmax
