@@ -68,6 +68,21 @@ def test_router_logits(torch_dev, cfg):
     assert err < 2e-5
 
 
+@pytest.mark.parametrize("T", [128, 300])
+def test_router_logits_matrix_core(torch_dev, T):
+    """From 128 bf16 tokens the router GEMV runs on the matrix cores (128-token
+    tiles; 300 leaves a ragged last tile)."""
+    wl = synth.WORKLOADS[1]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, T)
+    ol = P.oracle_layer(li)
+    xb = synth.make_hidden(0, 1, T, wl.shape.hidden, tag=5)
+    lg = m.router_logits(P.bf16_tensor(xb, torch_dev)).cpu().numpy()
+    err = np.abs(lg - ol.logits(oracle.bf16_bits_to_f64(xb))).max()
+    P.log(f"router matrix-core T={T}: max |logit err| = {err:.3e}")
+    assert err < 2e-5
+
+
 @pytest.mark.parametrize("cfg", [0, 1])
 def test_layer_parity_decode(torch_dev, cfg):
     wl = synth.WORKLOADS[cfg]
