@@ -765,17 +765,18 @@ __device__ void topk_select(const RouterArgs& a, float* s_lg, int* s_ids, int nt
 }
 
 // Router GEMV on the matrix cores, for large bf16 batches.  Workgroup =
-// (64-expert row block, k-split of kRouterGPW groups, 128-token tile); wave w
-// owns tokens 64 (w & 1) .. +63 (two 32-row MFMA blocks) against experts
+// (64-expert row block, k-split of kRouterGPW groups, 64-token tile); wave w
+// owns tokens 32 (w & 1) .. +31 (one 32-row MFMA block) against experts
 // 32 (w >> 1) .. +31.  Per 64-wide group the token rows are converted to fp16
-// (the 8-bit pair order) into an LDS double buffer, the next group's rows
-// being loaded meanwhile; B is the lifted codes (1024 + q, exact in fp16),
-// and the group's products are folded into the logits as s * P + (b - 1024
-// s) * sum(x) in fp32, as in the VALU GEMV.  Writes the same k-split
-// partials; the eb == 0 workgroups also publish x for the expert kernels.
-constexpr int kRmTok = 128;   // tokens per matrix-core router tile
+// (the 8-bit pair order) into an LDS double buffer, the next groups' rows and
+// codes being loaded meanwhile; B is the lifted codes (1024 + q, exact in
+// fp16), and the group's products are folded into the logits as
+// s * P + (b - 1024 s) * sum(x) in fp32, as in the VALU GEMV.  Writes the
+// same k-split partials; the eb == 0 workgroups also publish x16 and the
+// streaming path's group sums.
+constexpr int kRmTok = 64;   // tokens per matrix-core router tile
 __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
-  __shared__ __align__(16) uint16_t xa[2][kRmTok * 64];   // fp16 x, 8-bit pair order
+  __shared__ __align__(16) uint16_t xa[2][kRmTok * 64];   // fp16 x, 8-bit pair order, swizzled
   __shared__ __align__(16) float xsum[2][kRmTok];          // per-token group sums
   const int eb = blockIdx.x, ks = blockIdx.y, tb = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -784,57 +785,58 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
   const int g0 = ks * kRouterGPW, ng = min(kRouterGPW, a.G - g0);
   const bool wx = a.write_x && eb == 0;
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  // x chunks of this thread: chunk c = tid + 256 j (j < 4) is token c / 8,
+  // x chunks of this thread: chunk c = tid + 256 j (j < 2) is token c / 8,
   // columns 8 (c % 8) .. +7 of the group; the 8 chunks of a token are 8
   // consecutive lanes.  Rows past the batch repeat its last token (their
-  // logits are not written).
-  uint4 raw[4];
+  // logits are not written).  The group loop is unrolled, so each group's
+  // chunks have registers of their own; they are loaded four groups ahead.
+  constexpr int NCH = kRmTok * 8 / 256;
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  u4v raw[kRouterGPW][NCH];
   auto load_x = [&](int gl) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NCH; ++j) {
       const int c = tid + 256 * j, t = min(c >> 3, nt - 1), r = c & 7;
-      raw[j] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * a.H + (size_t)(g0 + gl) * 64 + r * 8);
+      raw[gl][j] = *reinterpret_cast<const u4v*>(x + (size_t)(t0 + t) * a.H + (size_t)(g0 + gl) * 64 + r * 8);
     }
   };
+  // bf16 -> fp16 (exact for values in fp16's normal range) in the 8-bit pair
+  // order, and the group sum of the fp16 values the products use; the eb == 0
+  // workgroups also write x16 (4-bit pair order) and, for the streaming path,
+  // S1 over what it stages (odd columns divided by 16) and S2 over the values
+  // those stand for
   auto stage_x = [&](int gl, int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NCH; ++j) {
       const int c = tid + 256 * j, t = c >> 3, r = c & 7, c8 = r * 8;
-      const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      const uint32_t w0 = raw[gl][j].x, w1 = raw[gl][j].y, w2 = raw[gl][j].z, w3 = raw[gl][j].w;
+      const uint32_t w[4] = {w0, w1, w2, w3};
       uint16_t h8[8], h4[8];
-      // the router's group sum (hi + lo, as in the VALU GEMV), and for the
-      // streaming path S1 over what it stages (odd columns divided by 16) and
-      // S2 over the values those stand for
-      float sum = 0.f, s1 = 0.f, s2 = 0.f;
+      float sum = 0.f, s1 = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const uint32_t bits = (q & 1) ? (w[q >> 1] & 0xffff0000u) : (w[q >> 1] << 16);
-        const float v = __builtin_bit_cast(float, bits);
-        const _Float16 h = (_Float16)v;
-        const uint16_t hb = f16bits(h), lb = f16bits((_Float16)(v - (float)h));
+        const uint16_t hb = f16bits((_Float16)__builtin_bit_cast(float, bits));
         h8[pair_pos8(q)] = hb;
         h4[pair_pos4(q)] = hb;
-        const float vh = f16f(hb), vl = f16f(lb);
-        sum += vh + vl;
-        if (q & 1) {
-          const float sh = f16f(f16bits((_Float16)(vh * 0.0625f)));
-          s1 += sh;
-          s2 += 16.f * sh;
-        } else {
-          s1 += vh;
-          s2 += vh;
-        }
+        const float vh = f16f(hb);
+        sum += vh;
+        if (wx) s1 += (q & 1) ? f16f(f16bits((_Float16)(vh * 0.0625f))) : vh;
       }
       sum = sum8_lanes(sum);
-      s1 = sum8_lanes(s1);
-      s2 = sum8_lanes(s2);
-      *reinterpret_cast<uint4*>(&xa[buf][t * 64 + c8]) = *reinterpret_cast<const uint4*>(h8);
+      // 16-byte segment r of row t sits at r ^ ((t >> 1) & 7): the operand
+      // reads of 16 consecutive rows are then bank-conflict free
+      *reinterpret_cast<uint4*>(&xa[buf][t * 64 + (r ^ ((t >> 1) & 7)) * 8]) =
+          *reinterpret_cast<const uint4*>(h8);
       if (r == 0) xsum[buf][t] = sum;
-      if (wx && t < nt) {
-        const size_t dst = (size_t)(t0 + t) * a.H + (size_t)(g0 + gl) * 64 + c8;
-        *reinterpret_cast<uint4*>(a.x16 + dst) = *reinterpret_cast<const uint4*>(h4);
-        if (r == 0)
-          reinterpret_cast<float2*>(a.xs)[(size_t)(t0 + t) * a.G + g0 + gl] = make_float2(s1, s2);
+      if (wx) {
+        s1 = sum8_lanes(s1);
+        if (t < nt) {
+          const size_t dst = (size_t)(t0 + t) * a.H + (size_t)(g0 + gl) * 64 + c8;
+          *reinterpret_cast<uint4*>(a.x16 + dst) = *reinterpret_cast<const uint4*>(h4);
+          if (r == 0)
+            reinterpret_cast<float2*>(a.xs)[(size_t)(t0 + t) * a.G + g0 + gl] = make_float2(s1, sum);
+        }
       }
     }
   };
@@ -842,71 +844,78 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
   // 8-byte half hi of each 16-column chunk
   const int brow = 32 * (wave >> 1) + l32;
   const uint8_t* btile = a.router + ((size_t)eb * a.G + g0) * kQ8TileBytes;
-  const int mt = wave & 1;
+  const int m = 32 * (wave & 1) + l32;   // this lane's token row in the A operand
   const Lift L;
-  f32x16 lg[2];
+  f32x16 lg;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) lg[mb][j] = 0.f;
-  load_x(0);
-  stage_x(0, 0);
-  if (ng > 1) load_x(1);
-  __syncthreads();
-  for (int gl = 0; gl < ng; ++gl) {
-    const int buf = gl & 1;
+  for (int j = 0; j < 16; ++j) lg[j] = 0.f;
+  // the codes and scale/bias of each group, loaded four groups ahead
+  uint32_t cd[kRouterGPW][4][2], sbq[kRouterGPW];
+  auto load_b = [&](int gl) {
     const uint8_t* tile = btile + (size_t)gl * kQ8TileBytes;
-    uint32_t cd[4][2];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const uint2 v = *reinterpret_cast<const uint2*>(tile + kk * 1024 + brow * 16 + hi * 8);
-      cd[kk][0] = v.x;
-      cd[kk][1] = v.y;
+      cd[gl][kk][0] = v.x;
+      cd[gl][kk][1] = v.y;
     }
-    const uint32_t sb = ld4(tile + kQ8CodeBytes + brow * 4);
+    sbq[gl] = ld4(tile + kQ8CodeBytes + brow * 4);
+  };
+#pragma unroll
+  for (int gl = 0; gl < 3; ++gl)
+    if (gl < ng) {
+      load_b(gl);
+      load_x(gl);
+    }
+  stage_x(0, 0);
+  if (3 < ng) {
+    load_b(3);
+    load_x(3);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int gl = 0; gl < kRouterGPW; ++gl) {
+    if (gl >= ng) break;
+    const int buf = gl & 1;
+    const uint32_t sb = sbq[gl];
     const float s = f16f(sb & 0xffffu), cf = fmaf(-1024.f, s, f16f(sb >> 16));
-    f32x16 pr[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pr[mb][j] = 0.f;
+    f32x16 pr;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-      const u4v bw = {L.q8(cd[kk][0], 0), L.q8(cd[kk][0], 1), L.q8(cd[kk][1], 0), L.q8(cd[kk][1], 1)};
+      const u4v bw = {L.q8(cd[gl][kk][0], 0), L.q8(cd[gl][kk][0], 1), L.q8(cd[gl][kk][1], 0),
+                      L.q8(cd[gl][kk][1], 1)};
       const f16x8 bf = __builtin_bit_cast(f16x8, bw);
+      const int seg = (2 * kk + hi) ^ ((m >> 1) & 7);
+      const f16x8 af = *reinterpret_cast<const f16x8*>(&xa[buf][m * 64 + seg * 8]);
+      if (kk == 0) {
+        f32x16 z;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int m = 64 * mt + 32 * mb + l32;
-        const f16x8 af = *reinterpret_cast<const f16x8*>(&xa[buf][m * 64 + kk * 16 + hi * 8]);
-        pr[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, pr[mb], 0, 0, 0);
+        for (int j = 0; j < 16; ++j) z[j] = 0.f;
+        pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, z, 0, 0, 0);
+      } else {
+        pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, pr, 0, 0, 0);
       }
     }
     // fold: logit += s * P + (b - 1024 s) * sum(x) for each (token, expert)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xsum[buf][32 * (wave & 1) + 8 * j4 + 4 * hi]);
+      const float xq[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int m = 64 * mt + 32 * mb + 8 * j4 + 4 * hi;
-        const float4 xv = *reinterpret_cast<const float4*>(&xsum[buf][m]);
-        const float xq[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          lg[mb][4 * j4 + jj] += fmaf(s, pr[mb][4 * j4 + jj], cf * xq[jj]);
-      }
-    if (gl + 1 < ng) {
-      stage_x(gl + 1, buf ^ 1);
-      if (gl + 2 < ng) load_x(gl + 2);
+      for (int jj = 0; jj < 4; ++jj) lg[4 * j4 + jj] += fmaf(s, pr[4 * j4 + jj], cf * xq[jj]);
+    }
+    if (gl + 1 < ng) stage_x(gl + 1, buf ^ 1);
+    if (gl + 4 < ng) {
+      load_b(gl + 4);
+      load_x(gl + 4);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int m = 64 * mt + 32 * mb + 8 * (j >> 2) + 4 * hi + (j & 3);
-      if (m < nt) a.part[((size_t)ks * a.T + t0 + m) * a.Epad + eb * 64 + brow] = lg[mb][j];
-    }
+  for (int j = 0; j < 16; ++j) {
+    const int mo = 32 * (wave & 1) + 8 * (j >> 2) + 4 * hi + (j & 3);
+    if (mo < nt) a.part[((size_t)ks * a.T + t0 + mo) * a.Epad + eb * 64 + brow] = lg[j];
+  }
 }
 
 // Top-k: workgroup = tpw tokens (tpw * Epad <= 4096).  Sums the k-split
