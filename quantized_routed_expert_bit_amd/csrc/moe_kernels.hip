@@ -1206,17 +1206,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   __shared__ __align__(16) uint16_t ring[NST * STAGE];
   __shared__ int s_src[kMfmaBM];    // element offset of each row's A source
   __shared__ int s_slot[kMfmaBM];
-  // (tile, column block) units, column block fastest: consecutive
-  // workgroups share the tile's token rows.  (Giving each XCD a contiguous
-  // run of units, so that an expert's tiles share one L2, measured 1.7x
-  // slower.)  The grid is an upper bound; units past the forward's tile
-  // count exit.
+  // (tile, column block) units.  Workgroup b runs on XCD b % 8, and every
+  // column block of tile t on XCD t % 8, so the tile's token rows, which
+  // each column block reads in full, are fetched into one L2: b = ((t / 8) *
+  // nblk + cblk) * 8 + t % 8 (measured 2.5 % faster than column blocks in
+  // consecutive workgroups; giving each XCD a contiguous run of tiles was
+  // 1.7x slower).  The grid is an upper bound (tiles rounded up to a
+  // multiple of 8); units past the forward's tile count exit.
   constexpr int CB = NW * (UP ? 32 : 64);       // columns per workgroup
   const int nblk = ((UP ? (a.Is > a.I ? a.Is : a.I) : a.H) + CB - 1) / CB;
-  const int units = a.misc[kNTiles] * nblk;
-  const int u = (int)blockIdx.x;
-  if (u >= units) return;
-  const int tile_i = u / nblk, cblk = u - tile_i * nblk;
+  const int q8 = (int)blockIdx.x >> 3;
+  const int cblk = q8 % nblk, tile_i = (q8 / nblk) * 8 + ((int)blockIdx.x & 7);
+  if (tile_i >= a.misc[kNTiles]) return;
   const int2 tl = a.mtiles[tile_i];
   const int4 it = a.mitems[tl.x];
   const int e = it.x, m_tot = it.y, loff = it.z, m0 = tl.y;
@@ -2227,7 +2228,7 @@ hipError_t launch_mfma_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   // one-dimensional grid; the kernel maps it onto (tile, column block)
   // 4 waves (128 columns): measured faster than 8 waves (256 columns), which
   // halve the token-row reads but leave one workgroup per CU
-  const dim3 grid(((imax + 127) / 128) * nt);
+  const dim3 grid(((imax + 127) / 128) * ((nt + 7) / 8) * 8);
   if (x_f32)
     hipLaunchKernelGGL((mfma_wide_kernel<true, true, 4>), grid, dim3(256), 0, s, m);
   else
@@ -2239,7 +2240,7 @@ hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s) {
   const int nt = mfma_tiles_max(d, T);
   if (nt == 0) return hipSuccess;
   const MfmaArgs m = mfma_args(d, T);
-  hipLaunchKernelGGL((mfma_wide_kernel<false, false, 4>), dim3(((d.H + 255) / 256) * nt),
+  hipLaunchKernelGGL((mfma_wide_kernel<false, false, 4>), dim3(((d.H + 255) / 256) * ((nt + 7) / 8) * 8),
                      dim3(256), 0, s, m);
   return hipGetLastError();
 }
