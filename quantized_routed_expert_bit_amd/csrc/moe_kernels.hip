@@ -143,20 +143,24 @@ __device__ __forceinline__ float sum8_lanes(float v) {
   return v;
 }
 
-// Exclusive scan of n ints held in LDS (n <= 256 * 8), by a 256-thread block.
-// Returns the total.  All threads must call it.
-__device__ int block_excl_scan(int* data, int n, int* scratch256) {
+// Exclusive scan of n ints held in LDS, by a block of NT threads.  Returns
+// the total.  All threads must call it; scratch holds NT / 64 ints.
+template <int NT>
+__device__ int block_excl_scan(int* data, int n, int* scratch) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + 255) / 256;
+  const int per = (n + NT - 1) / NT;
   const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
   int s = 0;
   for (int i = b0; i < b1; ++i) s += data[i];
   const int incl = wave_incl_scan(s);
-  if (lane == 63) scratch256[wave] = incl;
+  if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += scratch256[w];
-  const int total = scratch256[0] + scratch256[1] + scratch256[2] + scratch256[3];
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    before += w < wave ? scratch[w] : 0;
+    total += scratch[w];
+  }
   int run = before + incl - s;  // exclusive prefix of this thread's chunk
   for (int i = b0; i < b1; ++i) {
     const int v = data[i];
@@ -196,17 +200,18 @@ struct RouterArgs {
 
 constexpr int kBucketSmem = 5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + 16 * kMaxExperts + kMaxExperts;
 
-// Bucketing, by one 256-thread workgroup once every token's top-k is known:
+// Bucketing, by one workgroup of NT threads once every token's top-k is known:
 // LDS histogram of the T*k selections -> exclusive scan -> slot lists grouped
 // by expert -> work lists for the two expert paths.  `ids` may point to LDS or
 // global memory.  Order inside one expert's list is whatever the LDS atomics
 // give; it never changes a result (every row is computed on its own).
+template <int NT>
 __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem) {
   int* s_cnt = reinterpret_cast<int*>(smem);                // [E]
   int* s_off = s_cnt + kMaxExperts + 2;                      // [E + 1]
   int* s_flag = s_off + kMaxExperts + 2;                     // [E + 1]
   int* s_cur = s_flag + kMaxExperts + 2;                     // [E]
-  int* s_scan = s_cur + kMaxExperts + 2;                     // [256]
+  int* s_scan = s_cur + kMaxExperts + 2;                     // [256]: NT / 64 used
   int* s_tot = s_scan + 256;                                 // [4]
   int* s_mrows = s_tot + 4;                                  // [E + 1] rows per matrix-core item
   int* s_first = s_mrows + kMaxExperts + 2;                  // [E][4] first slots per expert
@@ -214,7 +219,7 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   const int tid = threadIdx.x;
   const int E = a.E, Tk = a.T * a.k;
   const int R = a.mfma_min_rows;
-  for (int e = tid; e < E; e += 256) {
+  for (int e = tid; e < E; e += NT) {
     s_cnt[e] = 0;
     s_pred[e] = 0;
   }
@@ -222,46 +227,46 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   __syncthreads();
   // loops over the slots load 8 ids per thread at a time (indices clamped,
   // every load unconditional) so the loads of a batch overlap
-  for (int s0 = tid; s0 < Tk; s0 += 256 * 8) {
+  for (int s0 = tid; s0 < Tk; s0 += NT * 8) {
     int v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ids[min(s0 + 256 * j, Tk - 1)];
+    for (int j = 0; j < 8; ++j) v[j] = ids[min(s0 + NT * j, Tk - 1)];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (s0 + 256 * j < Tk) atomicAdd(&s_cnt[v[j]], 1);
+      if (s0 + NT * j < Tk) atomicAdd(&s_cnt[v[j]], 1);
   }
-  for (int s0 = tid; s0 < pv; s0 += 256 * 8) {
+  for (int s0 = tid; s0 < pv; s0 += NT * 8) {
     int v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = a.pred[min(s0 + 256 * j, pv - 1)];
+    for (int j = 0; j < 8; ++j) v[j] = a.pred[min(s0 + NT * j, pv - 1)];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (s0 + 256 * j < pv && v[j] >= 0 && v[j] < E) s_pred[v[j]] = 1;
+      if (s0 + NT * j < pv && v[j] >= 0 && v[j] < E) s_pred[v[j]] = 1;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) s_off[e] = s_cnt[e];
+  for (int e = tid; e < E; e += NT) s_off[e] = s_cnt[e];
   __syncthreads();
-  block_excl_scan(s_off, E, s_scan);
-  for (int e = tid; e < E; e += 256) {
+  block_excl_scan<NT>(s_off, E, s_scan);
+  for (int e = tid; e < E; e += NT) {
     a.offs[e] = s_off[e];
     s_cur[e] = s_off[e];
   }
   if (tid == 0) a.offs[E] = Tk;
   __syncthreads();
-  for (int s0 = tid; s0 < Tk; s0 += 256 * 8) {
+  for (int s0 = tid; s0 < Tk; s0 += NT * 8) {
     int v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ids[min(s0 + 256 * j, Tk - 1)];
+    for (int j = 0; j < 8; ++j) v[j] = ids[min(s0 + NT * j, Tk - 1)];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (s0 + 256 * j < Tk) {
+      if (s0 + NT * j < Tk) {
         const int pos = atomicAdd(&s_cur[v[j]], 1), r = pos - s_off[v[j]];
-        a.slots[pos] = s0 + 256 * j;
-        if (r < 4) s_first[v[j] * 4 + r] = s0 + 256 * j;
+        a.slots[pos] = s0 + NT * j;
+        if (r < 4) s_first[v[j] * 4 + r] = s0 + NT * j;
       }
   }
   if (a.has_shared)
-    for (int t = tid; t < a.T; t += 256) a.slots[Tk + t] = Tk + t;
+    for (int t = tid; t < a.T; t += NT) a.slots[Tk + t] = Tk + t;
   __syncthreads();   // every placement is done before s_cur is reused below
   // Work lists: streaming (0 < rows < R) and matrix-core (rows >= R).  With a
   // lookahead prediction the predicted experts come first; the order decides
@@ -269,7 +274,7 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   // counts both halves at once: predicted in the low 16 bits, the rest in the
   // high 16 (each total <= kMaxExperts, so the halves never carry).
   for (int path = 0; path < 2; ++path) {
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += NT) {
       const int c = s_cnt[e];
       const bool on = path == 0 ? (c > 0 && c < R) : (c >= R);
       const bool first = pv ? s_pred[e] != 0 : true;
@@ -277,9 +282,9 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
       s_cur[e] = on ? (first ? 1 : 0x10000) : 0;
     }
     __syncthreads();
-    const int tot = block_excl_scan(s_cur, E, s_scan);
+    const int tot = block_excl_scan<NT>(s_cur, E, s_scan);
     const int n_first = tot & 0xffff;
-    for (int e = tid; e < E; e += 256)
+    for (int e = tid; e < E; e += NT)
       if (s_flag[e]) {
         const int pos = s_flag[e] == 1 ? (s_cur[e] & 0xffff) : n_first + (s_cur[e] >> 16);
         if (path == 0) {   // streaming item: (expert, rows, offset) + its first 4 slots
@@ -319,16 +324,16 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   if (n_mfma > 0) {   // uniform across the workgroup
     for (int wide = 1; wide >= 0; --wide) {
       const int bm = wide ? kMfmaBM : kNarrowBM;
-      for (int i = tid; i < n_mfma; i += 256) {
+      for (int i = tid; i < n_mfma; i += NT) {
         const int rows = s_mrows[i];
         const bool mine = wide ? rows >= a.wide_min_rows : rows < a.wide_min_rows;
         s_flag[i] = mine ? (rows + bm - 1) / bm : 0;
         s_cur[i] = s_flag[i];
       }
       __syncthreads();
-      const int n = block_excl_scan(s_cur, n_mfma, s_scan);
+      const int n = block_excl_scan<NT>(s_cur, n_mfma, s_scan);
       int2* out = wide ? a.mtiles : a.ntiles;
-      for (int i = tid; i < n_mfma; i += 256)
+      for (int i = tid; i < n_mfma; i += NT)
         for (int j = 0; j < s_flag[i]; ++j) out[s_cur[i] + j] = make_int2(i, j * bm);
       __syncthreads();
       if (wide) n_tiles = n; else n_narrow = n;
@@ -986,9 +991,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a, int tpw)
   }
 }
 
-__global__ __launch_bounds__(256) void bucket_kernel(RouterArgs a) {
+// 1024 threads: the histogram and placement loops over all T*k slots are
+// LDS-atomic chains, four times shorter than with 256
+constexpr int kBucketThreads = 1024;
+__global__ __launch_bounds__(kBucketThreads) void bucket_kernel(RouterArgs a) {
   __shared__ __align__(16) uint8_t smem[kBucketSmem];
-  bucket_tokens(a, a.ids_ws, smem);
+  bucket_tokens<kBucketThreads>(a, a.ids_ws, smem);
 }
 
 // --------------------------------------------------------- streaming path --
@@ -2040,7 +2048,7 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
     hipLaunchKernelGGL((router_topk_kernel<64, 16>), dim3(n_wg), dim3(256), 0, s, a, tpw);
   e = hipGetLastError();
   if (e != hipSuccess || mode != 0 || n_wg == 1) return e;   // one workgroup buckets itself
-  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, s, a);
   return hipGetLastError();
 }
 
