@@ -2,16 +2,21 @@
 //
 // Layer definition and record format: include/moe.h.  Kernels, in forward order:
 //   rmsnorm_kernel        optional per-token RMS normalization (stacked layers).
-//   router_gemv_kernel    8-bit router GEMV -> fp32 partial logits per k-split;
-//                         also writes x as fp16 (hi [+ lo]) and per-64 group sums.
+//   router_gemv_kernel    8-bit router GEMV on the VALU -> fp32 partial logits
+//                         per k-split; also writes x as fp16 (hi [+ lo]) and
+//                         per-64 group sums.
+//   router_mfma_kernel    the same on the matrix cores, for bf16 batches of 64
+//                         tokens or more.
 //   router_topk_kernel    sums the partials in fixed order, adds the logit bias,
 //                         top-k by (logit desc, index asc) with DPP reductions,
-//                         softmax over the k; buckets the slots when one
-//                         workgroup covers the batch (else bucket_kernel).
+//                         softmax over the k; when one workgroup covers the
+//                         batch its first wave buckets it (bucket_wave), else
+//                         bucket_kernel does.
 //   gemv_up/down_kernel   streaming expert path (experts with few rows): one
 //                         lane per weight row, 16-byte tile loads, nibbles
-//                         lifted in registers, token rows staged in LDS.
-//   mfma_narrow_kernel    matrix-core path, 32-row tiles (a few tens of rows).
+//                         lifted in registers, token rows staged in LDS; their
+//                         first workgroups run the 32-row matrix-core tiles
+//                         (narrow_tile) of the experts with a few tens of rows.
 //   mfma_wide_kernel      matrix-core path, 128-row tiles, LDS-DMA ring.
 //   combine_kernel        y[t] = [r +] sum_j p[t,j] y_slot[t,j] + y_shared[t].
 //
@@ -19,7 +24,8 @@
 // the exponent trick: (q | 0x6400) is the fp16 value 1024 + q exactly, so
 //     sum_k x_k (s q_k + b) = s * sum_k x_k (1024 + q_k) + (b - 1024 s) * sum_k x_k
 // with fp32 accumulation (the 4-bit path folds this with two group sums, see
-// GemvStream).  The matrix-core paths dequantize to fp16 s*q + b (one rounding).
+// GemvStream; the matrix-core router folds it per group).  The matrix-core
+// expert paths dequantize to fp16 s*q + b (one rounding).
 
 #include "moe_internal.h"
 
@@ -1032,7 +1038,6 @@ template <int NMAT, int P, bool HALF = false>
 struct GemvStream {
   const uint8_t* mat[NMAT];
   int gbeg, gend, lane;
-  int gstr = 1;   // group stride: the wave takes gbeg, gbeg + gstr, ... below gend
   int row = 0, hh = 0;   // HALF: the lane's row of the tile and column half
   uint4 c0[P][NMAT], c1[P][NMAT];
   uint32_t sb[P][NMAT];
@@ -1055,22 +1060,20 @@ struct GemvStream {
   // index past the end is clamped to the last group) so the number of loads
   // in flight is static and the compiler waits only for the buffer it reads.
   // Requires gbeg < gend.
-  __device__ __forceinline__ int glast() const { return gbeg + ((gend - 1 - gbeg) / gstr) * gstr; }
   __device__ __forceinline__ void prefetch() {
 #pragma unroll
-    for (int p = 0; p < P; ++p) load(p, min(gbeg + p * gstr, glast()));
+    for (int p = 0; p < P; ++p) load(p, min(gbeg + p, gend - 1));
   }
   template <int MT, bool LO>
   __device__ __forceinline__ void run(const uint32_t* xl, int xrow_dw, int lo_dw, const float2* xsl,
                                       int G, int nt, float (&acc)[NMAT][MT]) {
     const Lift L;
     constexpr int NW = HALF ? 16 : 32;   // lifted dwords per lane per group
-    const int gl = glast();
     const bool fold = !HALF || hh == 0;
-    for (int g0 = gbeg; g0 < gend; g0 += P * gstr) {
+    for (int g0 = gbeg; g0 < gend; g0 += P) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        const int g = g0 + p * gstr;
+        const int g = g0 + p;
         {
           uint32_t w[NMAT][NW];
           float s[NMAT], bb[NMAT], cf[NMAT];
@@ -1082,7 +1085,7 @@ struct GemvStream {
             bb[m] = fold ? f16f(sb[p][m] >> 16) : 0.f;
             cf[m] = fold ? -1024.f * s[m] : 0.f;
           }
-          load(p, min(g + P * gstr, gl));
+          load(p, min(g + P, gend - 1));
           if (g < gend) {
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
