@@ -156,6 +156,21 @@ def test_repeatable_bitwise(torch_dev):
         assert torch.equal(y, y0) and torch.equal(i, i0) and torch.equal(p, p0)
 
 
+def test_repeatable_bitwise_large_batch(torch_dev):
+    """300 tokens: matrix-core router, top-k over several workgroups, the
+    general bucketing pass (its slot order inside an expert follows LDS
+    atomics) and both matrix-core expert paths; every run is bitwise equal."""
+    import torch
+    wl = synth.WORKLOADS[1]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, 300)
+    x = P.bf16_tensor(synth.make_hidden(0, 1, 300, 2816, tag=9), torch_dev)
+    y0, i0, p0 = m.forward(x, return_selection=True)
+    for _ in range(5):
+        y, i, p = m.forward(x, return_selection=True)
+        assert torch.equal(y, y0) and torch.equal(i, i0) and torch.equal(p, p0)
+
+
 def test_error_paths(torch_dev):
     import torch
     from quantized_routed_expert_bit_amd import MoELayer, MoEError
