@@ -90,6 +90,17 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_ca
 __device__ __forceinline__ uint32_t ld4(const uint8_t* p) {
   return *reinterpret_cast<const uint32_t*>(p);
 }
+// Expert weights, read once per forward, are loaded non-temporally: they
+// then do not push the small data every kernel reuses (token rows, h, the
+// work lists) out of the caches (decode layer at 16 tokens: 79 -> 74 us).
+__device__ __forceinline__ uint4 ld16_nt(const uint8_t* p) {
+  typedef uint32_t u4n __attribute__((ext_vector_type(4)));
+  const u4n v = __builtin_nontemporal_load(reinterpret_cast<const u4n*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld4_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 
 // Streaming unpack of one 16-byte 4-bit piece (32 columns) into 16 fp16
 // pairs with one shift per dword: pairs 0 and 2 of a dword are
@@ -1047,12 +1058,12 @@ struct GemvStream {
     for (int m = 0; m < NMAT; ++m) {
       const uint8_t* t = mat[m] + (size_t)g * kQ4TileBytes;
       if (HALF) {
-        c0[p][m] = ld16(t + hh * 1024 + row * 16);
-        sb[p][m] = ld4(t + kQ4CodeBytes + row * 4);
+        c0[p][m] = ld16_nt(t + hh * 1024 + row * 16);
+        sb[p][m] = ld4_nt(t + kQ4CodeBytes + row * 4);
       } else {
-        c0[p][m] = ld16(t + lane * 16);
-        c1[p][m] = ld16(t + 1024 + lane * 16);
-        sb[p][m] = ld4(t + kQ4CodeBytes + lane * 4);
+        c0[p][m] = ld16_nt(t + lane * 16);
+        c1[p][m] = ld16_nt(t + 1024 + lane * 16);
+        sb[p][m] = ld4_nt(t + kQ4CodeBytes + lane * 4);
       }
     }
   }
@@ -1446,8 +1457,8 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
     }                                                                                  \
     _Pragma("unroll") for (int nb = 0; nb < 2; ++nb) {                                 \
       const uint8_t* t_ = bb[nb] + (size_t)(g) * kQ4TileBytes;                         \
-      rb[q][nb] = ld16(t_ + hi * 1024 + brow[nb] * 16);                                \
-      rs[q][nb] = ld4(t_ + kQ4CodeBytes + brow[nb] * 4);                               \
+      rb[q][nb] = ld16_nt(t_ + hi * 1024 + brow[nb] * 16);                             \
+      rs[q][nb] = ld4_nt(t_ + kQ4CodeBytes + brow[nb] * 4);                            \
     }                                                                                  \
   } while (0)
 #pragma unroll
