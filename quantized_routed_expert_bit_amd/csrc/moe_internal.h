@@ -39,6 +39,15 @@ constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kMfmaBM = 128;
 constexpr int kNarrowBM = 32;
 constexpr int kMfmaWaves = 4;
+// Wide matrix-core launches: one workgroup per (128-row tile, column block)
+// unit; a block is kWideColsUp gate/up columns or kWideColsDn down columns.
+constexpr int kWideWaves = 4;
+constexpr int kWideColsUp = kWideWaves * 32;
+constexpr int kWideColsDn = kWideWaves * 64;
+// Entries per XCD of a wide unit list for nt row tiles, nts of them the
+// shared expert's, with ncr (routed) and ncs (shared) column blocks: tiles are
+// dealt to the 8 XCDs in rounds, so an XCD gets at most ceil(n / 8) of n.
+inline int wide_cap(int nt, int nts, int ncr, int ncs) { return (nt + 7) / 8 * ncr + (nts + 7) / 8 * ncs; }
 
 // misc[] slots (int32) in the workspace
 enum MiscSlot {
@@ -48,12 +57,15 @@ enum MiscSlot {
   kNTiles = 3,      // matrix-core row tiles
   kPredValid = 4,   // predicted slots a lookahead left for the next forward (0: none)
   kNNarrow = 5,     // matrix-core narrow (32-row) tiles
+  kUnitsUp = 8,     // [8] wide gate/up units listed for each XCD
+  kUnitsDn = 16,    // [8] wide down units listed for each XCD
   kMiscInts = 64,
 };
 
 struct WsLayout {
   size_t part, logits, x16, x16lo, xs, ids, p, rank, counts, offs, cnt_tb, misc,
-      slots, items, mitems, mtiles, ntiles, pred, hbuf, hs, yslot, xn, total;
+      slots, items, mitems, mtiles, ntiles, wunits_up, wunits_dn, pred, hbuf, hs, yslot, xn, total;
+  int cap_up, cap_dn;   // entries per XCD of the wide unit lists
 };
 
 // All sizes derived from the config; identical on every call.

@@ -11,13 +11,15 @@
 //                         top-k by (logit desc, index asc) with DPP reductions,
 //                         softmax over the k; when one workgroup covers the
 //                         batch its first wave buckets it (bucket_wave), else
-//                         bucket_kernel does.
+//                         bucket_kernel does; bucketing also writes the
+//                         per-XCD work lists of the 128-row launches.
 //   gemv_up/down_kernel   streaming expert path (experts with few rows): one
 //                         lane per weight row, 16-byte tile loads, nibbles
 //                         lifted in registers, token rows staged in LDS; their
 //                         first workgroups run the 32-row matrix-core tiles
 //                         (narrow_tile) of the experts with a few tens of rows.
-//   mfma_wide_kernel      matrix-core path, 128-row tiles, LDS-DMA ring.
+//   mfma_wide_kernel      matrix-core path, 128-row tiles, LDS-DMA ring;
+//                         outputs leave through LDS as 16-byte stores.
 //   combine_kernel        y[t] = [r +] sum_j p[t,j] y_slot[t,j] + y_shared[t].
 //
 // The streaming dot products use v_dot2_f32_f16 on codes lifted to fp16 with
@@ -212,8 +214,41 @@ struct RouterArgs {
   int4* mitems;
   int2* mtiles;
   int2* ntiles;
+  int2* wunits_up;
+  int2* wunits_dn;
   int mfma_min_rows, wide_min_rows, has_shared;
+  int ncu_r, ncu_s, ncd;   // wide column blocks: routed and shared gate/up, down
+  int cap_up, cap_dn;      // entries per XCD of the wide unit lists
 };
+
+// Work lists of the wide launches, one per XCD: workgroup b runs on XCD b % 8
+// and takes entry b / 8 of that XCD's list.  Row tiles are dealt to the XCDs
+// in rounds of 8 (alternating direction) in the order: the shared expert's
+// tiles, the routed experts' full 128-row tiles, their partial tiles.  Each
+// XCD then runs its longest units first and its shortest last, and the
+// column blocks of a tile, which read the same token rows, stay together.
+// dealt(n, x): tiles XCD x gets of the first n dealt.
+__device__ __forceinline__ int dealt(int n, int x) {
+  const int r = n >> 3, pos = (r & 1) ? 7 - x : x;
+  return r + (pos < (n & 7) ? 1 : 0);
+}
+// Units of tile t, dealt at position q (the nts shared tiles take positions
+// 0 .. nts - 1).
+__device__ void put_units(const RouterArgs& a, int t, int q, bool sh, int nts) {
+  const int r = q >> 3, pos = q & 7, x = (r & 1) ? 7 - pos : pos;
+  const int ds = sh ? r : dealt(nts, x);   // shared tiles before it on XCD x
+  int2* up = a.wunits_up + x * a.cap_up + ds * a.ncu_s + (r - ds) * a.ncu_r;
+  int2* dn = a.wunits_dn + x * a.cap_dn + r * a.ncd;
+  const int ncu = sh ? a.ncu_s : a.ncu_r;
+  for (int c = 0; c < ncu; ++c) up[c] = make_int2(t, c);
+  for (int c = 0; c < a.ncd; ++c) dn[c] = make_int2(t, c);
+}
+// List lengths of XCD x for nt tiles, nts of them shared.
+__device__ __forceinline__ void put_unit_counts(const RouterArgs& a, int nt, int nts, int x) {
+  const int ds = dealt(nts, x), d = dealt(nt, x);
+  a.misc[kUnitsUp + x] = ds * a.ncu_s + (d - ds) * a.ncu_r;
+  a.misc[kUnitsDn + x] = d * a.ncd;
+}
 
 constexpr int kBucketSmem = 5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + 16 * kMaxExperts + kMaxExperts;
 
@@ -338,6 +373,10 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   // matrix-core row tiles (item, first row): 128-row tiles for items with
   // >= wide_min_rows rows, 32-row tiles for the others
   int n_tiles = 0, n_narrow = 0;
+  if (tid < 8) {   // no wide units unless the tile pass below lists some
+    a.misc[kUnitsUp + tid] = 0;
+    a.misc[kUnitsDn + tid] = 0;
+  }
   if (n_mfma > 0) {   // uniform across the workgroup
     for (int wide = 1; wide >= 0; --wide) {
       const int bm = wide ? kMfmaBM : kNarrowBM;
@@ -352,6 +391,37 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
       int2* out = wide ? a.mtiles : a.ntiles;
       for (int i = tid; i < n_mfma; i += NT)
         for (int j = 0; j < s_flag[i]; ++j) out[s_cur[i] + j] = make_int2(i, j * bm);
+      if (wide) {
+        // the shared expert, when on this path, is the last item
+        const bool sh_item = a.has_shared && a.T >= R;
+        const int nts = sh_item ? s_flag[n_mfma - 1] : 0;
+        // dealing order of the routed tiles: full tiles, then partial ones,
+        // each in item order (counts packed: full high, partial low)
+        int* s_fp = s_first;   // free: the streaming items are written
+        for (int i = tid; i < n_mfma; i += NT) {
+          const int rows = s_mrows[i];
+          s_fp[i] = (s_flag[i] > 0 && !(sh_item && i == n_mfma - 1))
+                        ? ((rows / kMfmaBM) << 16) | ((rows % kMfmaBM) ? 1 : 0) : 0;
+        }
+        __syncthreads();
+        const int nf = block_excl_scan<NT>(s_fp, n_mfma, s_scan) >> 16;
+        for (int t = tid; t < n; t += NT) {
+          // item of tile t: the last one whose first tile is <= t (it has tiles)
+          int lo = 0, hi = n_mfma - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_cur[mid] <= t) lo = mid; else hi = mid - 1;
+          }
+          const int j = t - s_cur[lo];
+          if (sh_item && lo == n_mfma - 1) {
+            put_units(a, t, j, true, nts);
+          } else {
+            const int f = s_mrows[lo] / kMfmaBM;
+            put_units(a, t, nts + (j < f ? (s_fp[lo] >> 16) + j : nf + (s_fp[lo] & 0xffff)), false, nts);
+          }
+        }
+        if (tid < 8) put_unit_counts(a, n, nts, tid);
+      }
       __syncthreads();
       if (wide) n_tiles = n; else n_narrow = n;
     }
@@ -435,6 +505,17 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
   int pg0 = xg & 0xffff, pg1 = (tg & 0xffff) + (xg >> 16);
   int pm0 = xm & 0xffff, pm1 = (tm & 0xffff) + (xm >> 16);
   int pw = xt & 0xffff, pn = xt >> 16;
+  // dealing order of the routed 128-row tiles: full tiles, then partial
+  // ones, each in item order (per-lane counts packed: full high, partial low)
+  int fp = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = s_cnt[e];
+    if (c >= W) fp += ((c / kMfmaBM) << 16) | ((c % kMfmaBM) ? 1 : 0);
+  }
+  const int ifp = wave_incl_scan(fp);
+  const int nf = __builtin_amdgcn_readlane(ifp, 63) >> 16;
+  int pf = (ifp - fp) >> 16, pp = (ifp - fp) & 0xffff;
+  const int nts = a.has_shared && a.T >= W ? (a.T + kMfmaBM - 1) / kMfmaBM : 0;
   for (int e = e0; e < e1; ++e) {
     const int c = s_cnt[e];
     if (c == 0) continue;
@@ -447,9 +528,15 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
     } else {
       const int pos = first ? pm0++ : pm1++;
       a.mitems[pos] = make_int4(e, c, s_off[e], 0);
-      if (c >= W)
-        for (int j = 0; j * kMfmaBM < c; ++j) a.mtiles[pw++] = make_int2(pos, j * kMfmaBM);
-      else
+      if (c >= W) {
+        const int nt = (c + kMfmaBM - 1) / kMfmaBM, f = c / kMfmaBM;
+        for (int j = 0; j < nt; ++j) {
+          put_units(a, pw, nts + (j < f ? pf + j : nf + pp), false, nts);
+          a.mtiles[pw++] = make_int2(pos, j * kMfmaBM);
+        }
+        pf += f;
+        pp += nt - f;
+      } else
         for (int j = 0; j * kNarrowBM < c; ++j) a.ntiles[pn++] = make_int2(pos, j * kNarrowBM);
     }
   }
@@ -462,7 +549,10 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
       const int bm = wide ? kMfmaBM : kNarrowBM, nt = (T + bm - 1) / bm;
       int2* out = wide ? a.mtiles + n_tiles : a.ntiles + n_narrow;
       if (lane == 0) a.mitems[n_mfma] = make_int4(E, T, Tk, 0);
-      for (int j = lane; j < nt; j += 64) out[j] = make_int2(n_mfma, j * bm);
+      for (int j = lane; j < nt; j += 64) {
+        out[j] = make_int2(n_mfma, j * bm);
+        if (wide) put_units(a, n_tiles + j, j, true, nts);
+      }
       ++n_mfma;
       if (wide) n_tiles += nt; else n_narrow += nt;
     } else {
@@ -473,6 +563,7 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
       ++n_gemv;
     }
   }
+  if (lane < 8) put_unit_counts(a, n_tiles, nts, lane);
   if (lane == 0) {
     a.misc[kNGemv] = n_gemv;
     a.misc[kNMfma] = n_mfma;
@@ -1159,10 +1250,21 @@ struct MfmaArgs {
   const int4* mitems;
   const int2* mtiles;
   const int2* ntiles;
+  const int2* wunits_up;   // wide units (tile, column block): per-XCD lists
+  const int2* wunits_dn;
+  int cap_up, cap_dn;
   const int* misc;
   const int* slots;
   float* yslot;
 };
+
+// SwiGLU of one (gate, up) pair: g * sigmoid(g) * u, with the hardware
+// base-2 exponential and reciprocal (each within about 1 ulp).  For very
+// negative g the exponential overflows to +inf and the result is 0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504f);
+  return g * u * __builtin_amdgcn_rcpf(1.f + e);
+}
 
 // 8 nibbles (one dword of codes) -> 8 fp16 weights s*q + b in MFMA slot order.
 __device__ __forceinline__ f16x8 dequant8(const Lift& L, uint32_t dw, f16x2 s2, f16x2 b2) {
@@ -1217,10 +1319,10 @@ constexpr int kWideA = kMfmaBM * 64;          // halfs per A plane per stage (16
 
 // NW waves (4 or 8): the workgroup's columns are NW x 32 (gate/up pairs) or
 // NW x 64 (down), so 8 waves read each token row once per 256 columns.
-template <bool UP, bool LO, int NW>
+template <bool UP, bool LO, int NW, int NST = 3>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) {
   constexpr int NA = LO ? 2 : 1;
-  constexpr int NST = 3;
+  constexpr int D = NST - 1;                    // groups copied ahead
   constexpr int kWideB = NW * 2 * 512;          // halfs of B codes per stage
   constexpr int kWideS = NW * 128;              // halfs of B scale/bias per stage
   constexpr int STAGE = NA * kWideA + kWideB + kWideS;    // halfs
@@ -1228,18 +1330,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   __shared__ __align__(16) uint16_t ring[NST * STAGE];
   __shared__ int s_src[kMfmaBM];    // element offset of each row's A source
   __shared__ int s_slot[kMfmaBM];
-  // (tile, column block) units.  Workgroup b runs on XCD b % 8, and every
-  // column block of tile t on XCD t % 8, so the tile's token rows, which
-  // each column block reads in full, are fetched into one L2: b = ((t / 8) *
-  // nblk + cblk) * 8 + t % 8 (measured 2.5 % faster than column blocks in
-  // consecutive workgroups; giving each XCD a contiguous run of tiles was
-  // 1.7x slower).  The grid is an upper bound (tiles rounded up to a
-  // multiple of 8); units past the forward's tile count exit.
+  // (tile, column block) units from the bucketing pass's per-XCD lists:
+  // workgroup b runs on XCD b % 8 and takes entry b / 8 of its list, so an
+  // XCD's units start in list order (longest first) and a tile's column
+  // blocks, which read the same token rows, run together in one L2.  The
+  // grid is an upper bound; workgroups past their list's end exit.
   constexpr int CB = NW * (UP ? 32 : 64);       // columns per workgroup
-  const int nblk = ((UP ? (a.Is > a.I ? a.Is : a.I) : a.H) + CB - 1) / CB;
-  const int q8 = (int)blockIdx.x >> 3;
-  const int cblk = q8 % nblk, tile_i = (q8 / nblk) * 8 + ((int)blockIdx.x & 7);
-  if (tile_i >= a.misc[kNTiles]) return;
+  static_assert(CB == (UP ? kWideColsUp : kWideColsDn), "unit lists assume kWideWaves waves");
+  const int xcd = (int)blockIdx.x & 7, ib = (int)blockIdx.x >> 3;
+  if (ib >= a.misc[(UP ? kUnitsUp : kUnitsDn) + xcd]) return;
+  const int2 un = UP ? a.wunits_up[xcd * a.cap_up + ib] : a.wunits_dn[xcd * a.cap_dn + ib];
+  const int tile_i = un.x, cblk = un.y;
   const int2 tl = a.mtiles[tile_i];
   const int4 it = a.mitems[tl.x];
   const int e = it.x, m_tot = it.y, loff = it.z, m0 = tl.y;
@@ -1312,16 +1413,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
       for (int j = 0; j < 16; ++j) acc[mb][nb][j] = 0.f;
   const int nmb = (mrows + 31) >> 5;
 
-  issue(0, 0);
-  issue(min(1, Kg - 1), 1);
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(min(d, Kg - 1), d);
   // the main loop, specialized on the number of 32-row blocks in the tile
   auto run = [&](auto nmb_c) {
     constexpr int NMB = decltype(nmb_c)::value;
-    int cs = 0, ns = 2;                     // stage of group g, of group g + 2
+    int cs = 0, ns = D;                     // stage of group g, of group g + D
     for (int g = 0; g < Kg; ++g) {
-      wait_vmcnt<kOps>();                   // this wave's group-g copies are in LDS
+      wait_vmcnt<kOps * (D - 1)>();         // this wave's group-g copies are in LDS
       lds_barrier();                        // ... and every wave's; group g-1 is consumed
-      issue(min(g + 2, Kg - 1), ns);
+      issue(min(g + D, Kg - 1), ns);
       if (won) {
         const uint16_t* st = ring + cs * STAGE;
         const uint4* bq = reinterpret_cast<const uint4*>(st + NA * kWideA + wave * 1024);
@@ -1364,25 +1465,67 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
     default: run(std::integral_constant<int, 4>{}); break;
   }
   wait_vmcnt<0>();                          // no copy may still target LDS at exit
-  if (!won) return;
+  if (UP) {
+    // h rows go out through LDS: each wave stages its 32 columns of the
+    // tile's rows (fp16, in h column order) and then stores 16-byte pieces of
+    // the 64-byte row segments, instead of one 2-byte store per value.  Rows
+    // are padded to 80 bytes, so rows r and r + 4 (one store step) use
+    // different banks.  The ring is free once every wave has left the loop.
+    constexpr int RS = 40;
+    static_assert(kWideWaves * kMfmaBM * RS <= NST * STAGE, "staging fits the ring");
+    __syncthreads();
+    uint16_t* stg = ring + wave * (kMfmaBM * RS);
+    if (won) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    if (mb < nmb) {
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb < nmb) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int row = mb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-        if (row < mrows) {
-          const int slot = s_slot[row];
-          if (UP) {
-            const float gv = acc[mb][0][j], uv = acc[mb][1][j];
-            const float hv = gv / (1.f + expf(-gv)) * uv;
-            const int col = n0 + l32;
-            a.hdst[h_off(slot, Tk, a.I, a.Is) + pair_pos4(col)] = f16bits((_Float16)hv);
-          } else {
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-              a.yslot[(size_t)slot * a.H + n0 + nb * 32 + l32] = acc[mb][nb][j];
+          for (int j = 0; j < 16; ++j) {
+            const int row = mb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+            stg[row * RS + pair_pos4(l32)] = f16bits((_Float16)swiglu(acc[mb][0][j], acc[mb][1][j]));
           }
+        }
+      }
+    }
+    __syncthreads();
+    if (!won) return;
+    for (int i = lane; i < mrows * 4; i += 64) {
+      const int row = i >> 2, q = i & 3;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + row * RS + q * 8);
+      *reinterpret_cast<uint4*>(a.hdst + h_off(s_slot[row], Tk, a.I, a.Is) + n0 + q * 8) = v;
+    }
+    return;
+  }
+  // fp32 slot rows through LDS as well, 64 rows at a time: per wave 64 rows x
+  // 64 columns (rows padded to 72 floats, so rows r and r + 4 use different
+  // banks), then 16-byte stores of the 256-byte row segments.
+  constexpr int RD = 72;
+  static_assert(kWideWaves * 64 * RD * 4 <= NST * STAGE * 2, "staging fits the ring");
+  float* stf = reinterpret_cast<float*>(ring) + wave * (64 * RD);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (half * 2 < nmb) {
+      __syncthreads();    // the ring (or the previous half) is no longer read
+      if (won) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+          if (half * 2 + m2 < nmb) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int row = m2 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) stf[row * RD + nb * 32 + l32] = acc[half * 2 + m2][nb][j];
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if (won) {
+        const int r0 = half * 64, nr = min(64, mrows - r0);
+        for (int i = lane; i < nr * 16; i += 64) {
+          const int row = i >> 4, q = i & 15;
+          const float4 v = *reinterpret_cast<const float4*>(stf + row * RD + q * 4);
+          *reinterpret_cast<float4*>(a.yslot + (size_t)s_slot[r0 + row] * a.H + n0 + q * 4) = v;
         }
       }
     }
@@ -1522,7 +1665,7 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
     if (row < mrows) {
       const int sl = s_slot[row];
       if (UP) {
-        const float hv = v[0][jj] / (1.f + expf(-v[0][jj])) * v[1][jj];
+        const float hv = swiglu(v[0][jj], v[1][jj]);
         a.hdst[h_off(sl, Tk, a.I, a.Is) + pair_pos4(n0 + l32)] = f16bits((_Float16)hv);
       } else {
 #pragma unroll
@@ -1763,7 +1906,7 @@ void gemv_up_kernel(
           us += SPLIT ? red[0][wpm + j][t][l + 32] : red[NM - 1][j][t][l + 32];
         }
       }
-      const float hv = gs / (1.f + expf(-gs)) * us;
+      const float hv = swiglu(gs, us);
       // h in fp16, odd columns stored divided by 16 (the streaming down
       // pass stages them as they are); S1 sums what is stored, S2 the h
       // those values stand for, per 32-column half (the down pass adds the
@@ -2038,9 +2181,16 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   a.mitems = reinterpret_cast<int4*>(wsp(d, d.L.mitems));
   a.mtiles = reinterpret_cast<int2*>(wsp(d, d.L.mtiles));
   a.ntiles = reinterpret_cast<int2*>(wsp(d, d.L.ntiles));
+  a.wunits_up = reinterpret_cast<int2*>(wsp(d, d.L.wunits_up));
+  a.wunits_dn = reinterpret_cast<int2*>(wsp(d, d.L.wunits_dn));
   a.mfma_min_rows = d.mfma_min_rows;
   a.wide_min_rows = d.wide_min_rows;
   a.has_shared = d.has_shared;
+  a.ncu_r = (d.I + kWideColsUp - 1) / kWideColsUp;
+  a.ncu_s = d.has_shared ? (d.Is + kWideColsUp - 1) / kWideColsUp : 0;
+  a.ncd = (d.H + kWideColsDn - 1) / kWideColsDn;
+  a.cap_up = d.L.cap_up;
+  a.cap_dn = d.L.cap_dn;
   if (!x_f32 && T >= kRmTok)   // large bf16 batches: the GEMV on the matrix cores
     hipLaunchKernelGGL(router_mfma_kernel, dim3(a.n_rb, a.KS, (T + kRmTok - 1) / kRmTok), dim3(256),
                        0, s, a);
@@ -2231,6 +2381,10 @@ static MfmaArgs mfma_args(const LayerDev& d, int T) {
   m.hdst = reinterpret_cast<uint16_t*>(wsp(d, d.L.hbuf));
   m.mitems = reinterpret_cast<const int4*>(wsp(d, d.L.mitems));
   m.mtiles = reinterpret_cast<const int2*>(wsp(d, d.L.mtiles));
+  m.wunits_up = reinterpret_cast<const int2*>(wsp(d, d.L.wunits_up));
+  m.wunits_dn = reinterpret_cast<const int2*>(wsp(d, d.L.wunits_dn));
+  m.cap_up = d.L.cap_up;
+  m.cap_dn = d.L.cap_dn;
   m.ntiles = reinterpret_cast<const int2*>(wsp(d, d.L.ntiles));
   m.misc = reinterpret_cast<const int*>(wsp(d, d.L.misc));
   m.slots = reinterpret_cast<const int*>(wsp(d, d.L.slots));
@@ -2240,21 +2394,33 @@ static MfmaArgs mfma_args(const LayerDev& d, int T) {
 
 bool mfma_needed(const LayerDev& d, int T) { return mfma_tiles_max(d, T) > 0; }
 
+// Grid of a wide launch: 8 x the longest per-XCD list possible for T
+// tokens (nt bounds the tiles, the shared expert's included).
+template <bool UP>
+static int wide_grid(const LayerDev& d, int T, int nt) {
+  const int nts = d.has_shared ? (T + kMfmaBM - 1) / kMfmaBM : 0;
+  const int per = UP ? wide_cap(nt, nts, (d.I + kWideColsUp - 1) / kWideColsUp,
+                                (d.Is + kWideColsUp - 1) / kWideColsUp)
+                     : wide_cap(nt, 0, (d.H + kWideColsDn - 1) / kWideColsDn, 0);
+  const int cap = UP ? d.L.cap_up : d.L.cap_dn;
+  return 8 * (per < cap ? per : cap);
+}
+
 
 
 hipError_t launch_mfma_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const int nt = mfma_tiles_max(d, T);
   if (nt == 0) return hipSuccess;
-  const int imax = d.Is > d.I ? d.Is : d.I;
   const MfmaArgs m = mfma_args(d, T);
-  // one-dimensional grid; the kernel maps it onto (tile, column block)
-  // 4 waves (128 columns): measured faster than 8 waves (256 columns), which
-  // halve the token-row reads but leave one workgroup per CU
-  const dim3 grid(((imax + 127) / 128) * ((nt + 7) / 8) * 8);
+  // one workgroup per unit (an upper bound: the shared expert's tiles take
+  // its column blocks, every other tile the routed ones).  4 waves (128
+  // columns): measured faster than 8 waves (256 columns), which halve the
+  // token-row reads but leave one workgroup per CU.
+  const dim3 grid(wide_grid<true>(d, T, nt));
   if (x_f32)
-    hipLaunchKernelGGL((mfma_wide_kernel<true, true, 4>), grid, dim3(256), 0, s, m);
+    hipLaunchKernelGGL((mfma_wide_kernel<true, true, kWideWaves>), grid, dim3(64 * kWideWaves), 0, s, m);
   else
-    hipLaunchKernelGGL((mfma_wide_kernel<true, false, 4>), grid, dim3(256), 0, s, m);
+    hipLaunchKernelGGL((mfma_wide_kernel<true, false, kWideWaves>), grid, dim3(64 * kWideWaves), 0, s, m);
   return hipGetLastError();
 }
 
@@ -2262,8 +2428,8 @@ hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s) {
   const int nt = mfma_tiles_max(d, T);
   if (nt == 0) return hipSuccess;
   const MfmaArgs m = mfma_args(d, T);
-  hipLaunchKernelGGL((mfma_wide_kernel<false, false, 4>), dim3(((d.H + 255) / 256) * ((nt + 7) / 8) * 8),
-                     dim3(256), 0, s, m);
+  hipLaunchKernelGGL((mfma_wide_kernel<false, false, kWideWaves>), dim3(wide_grid<false>(d, T, nt)),
+                     dim3(64 * kWideWaves), 0, s, m);
   return hipGetLastError();
 }
 
