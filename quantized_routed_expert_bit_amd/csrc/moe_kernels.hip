@@ -190,6 +190,44 @@ __device__ int block_excl_scan(int* data, int n, int* scratch) {
   return total;
 }
 
+// Two exclusive scans at once (one pass, the same two barriers): d0 and d1
+// over [0, n); returns both totals.  scratch holds 2 * NT / 64 ints.
+template <int NT>
+__device__ int2 block_excl_scan2(int* d0, int* d1, int n, int* scratch) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWV = NT / 64;
+  const int per = (n + NT - 1) / NT;
+  const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
+  int s0 = 0, s1 = 0;
+  for (int i = b0; i < b1; ++i) {
+    s0 += d0[i];
+    s1 += d1[i];
+  }
+  const int i0 = wave_incl_scan(s0), i1 = wave_incl_scan(s1);
+  if (lane == 63) {
+    scratch[wave] = i0;
+    scratch[NWV + wave] = i1;
+  }
+  __syncthreads();
+  int r0 = i0 - s0, r1 = i1 - s1, t0 = 0, t1 = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    r0 += w < wave ? scratch[w] : 0;
+    r1 += w < wave ? scratch[NWV + w] : 0;
+    t0 += scratch[w];
+    t1 += scratch[NWV + w];
+  }
+  for (int i = b0; i < b1; ++i) {
+    const int v0 = d0[i], v1 = d1[i];
+    d0[i] = r0;
+    d1[i] = r1;
+    r0 += v0;
+    r1 += v1;
+  }
+  __syncthreads();
+  return make_int2(t0, t1);
+}
+
 // ------------------------------------------------------------------ router --
 
 struct RouterArgs {
@@ -233,15 +271,15 @@ __device__ __forceinline__ int dealt(int n, int x) {
   return r + (pos < (n & 7) ? 1 : 0);
 }
 // Units of tile t, dealt at position q (the nts shared tiles take positions
-// 0 .. nts - 1).
-__device__ void put_units(const RouterArgs& a, int t, int q, bool sh, int nts) {
+// 0 .. nts - 1): column blocks c0, c0 + cs, ...
+__device__ void put_units(const RouterArgs& a, int t, int q, bool sh, int nts, int c0, int cs) {
   const int r = q >> 3, pos = q & 7, x = (r & 1) ? 7 - pos : pos;
   const int ds = sh ? r : dealt(nts, x);   // shared tiles before it on XCD x
   int2* up = a.wunits_up + x * a.cap_up + ds * a.ncu_s + (r - ds) * a.ncu_r;
   int2* dn = a.wunits_dn + x * a.cap_dn + r * a.ncd;
   const int ncu = sh ? a.ncu_s : a.ncu_r;
-  for (int c = 0; c < ncu; ++c) up[c] = make_int2(t, c);
-  for (int c = 0; c < a.ncd; ++c) dn[c] = make_int2(t, c);
+  for (int c = c0; c < ncu; c += cs) up[c] = make_int2(t, c);
+  for (int c = c0; c < a.ncd; c += cs) dn[c] = make_int2(t, c);
 }
 // List lengths of XCD x for nt tiles, nts of them shared.
 __device__ __forceinline__ void put_unit_counts(const RouterArgs& a, int nt, int nts, int x) {
@@ -251,6 +289,8 @@ __device__ __forceinline__ void put_unit_counts(const RouterArgs& a, int nt, int
 }
 
 constexpr int kBucketSmem = 5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + 16 * kMaxExperts + kMaxExperts;
+constexpr int kBucketRegSlots = 16;   // slots per thread kept in registers
+constexpr int kBucketSlotOff = (kBucketSmem + 15) & ~15;   // LDS slot list (register case)
 
 // Bucketing, by one workgroup of NT threads once every token's top-k is known:
 // LDS histogram of the T*k selections -> exclusive scan -> slot lists grouped
@@ -277,15 +317,28 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   }
   const int pv = a.misc[kPredValid];
   __syncthreads();
-  // loops over the slots load 8 ids per thread at a time (indices clamped,
-  // every load unconditional) so the loads of a batch overlap
-  for (int s0 = tid; s0 < Tk; s0 += NT * 8) {
-    int v[8];
+  // Up to NT * KR slots (the prefill batch) stay in registers: the count an
+  // increment returns is the slot's rank among its expert's slots, and the
+  // placement below needs no second atomic.  Larger batches are counted,
+  // then placed with atomic cursors.  The loops load 8 ids per thread at a
+  // time (indices clamped, every load unconditional) so the loads overlap.
+  constexpr int KR = kBucketRegSlots;
+  const bool in_regs = Tk <= NT * KR;
+  int v[KR], rk[KR];
+  if (in_regs) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ids[min(s0 + NT * j, Tk - 1)];
+    for (int j = 0; j < KR; ++j) v[j] = ids[min(tid + NT * j, Tk - 1)];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (s0 + NT * j < Tk) atomicAdd(&s_cnt[v[j]], 1);
+    for (int j = 0; j < KR; ++j) rk[j] = tid + NT * j < Tk ? atomicAdd(&s_cnt[v[j]], 1) : 0;
+  } else {
+    for (int s0 = tid; s0 < Tk; s0 += NT * 8) {
+      int w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = ids[min(s0 + NT * j, Tk - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + NT * j < Tk) atomicAdd(&s_cnt[w[j]], 1);
+    }
   }
   for (int s0 = tid; s0 < pv; s0 += NT * 8) {
     int v[8];
@@ -304,55 +357,71 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
     s_cur[e] = s_off[e];
   }
   if (tid == 0) a.offs[E] = Tk;
-  __syncthreads();
-  for (int s0 = tid; s0 < Tk; s0 += NT * 8) {
-    int v[8];
+  if (in_regs) {
+    // the slot list is assembled in LDS and copied out in 16-byte pieces:
+    // one CU's scattered 4-byte stores would take several microseconds
+    int* s_sl = reinterpret_cast<int*>(smem + kBucketSlotOff);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ids[min(s0 + NT * j, Tk - 1)];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (s0 + NT * j < Tk) {
-        const int pos = atomicAdd(&s_cur[v[j]], 1), r = pos - s_off[v[j]];
-        a.slots[pos] = s0 + NT * j;
-        if (r < 4) s_first[v[j] * 4 + r] = s0 + NT * j;
+    for (int j = 0; j < KR; ++j)
+      if (tid + NT * j < Tk) {
+        s_sl[s_off[v[j]] + rk[j]] = tid + NT * j;
+        if (rk[j] < 4) s_first[v[j] * 4 + rk[j]] = tid + NT * j;
       }
+    __syncthreads();
+    for (int i = tid * 4; i < Tk; i += NT * 4) {
+      if (i + 4 <= Tk) {
+        *reinterpret_cast<int4*>(a.slots + i) = *reinterpret_cast<const int4*>(s_sl + i);
+      } else {
+        for (int q = i; q < Tk; ++q) a.slots[q] = s_sl[q];
+      }
+    }
+  } else {
+    __syncthreads();   // the cursors are set
+    for (int s0 = tid; s0 < Tk; s0 += NT * 8) {
+      int w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = ids[min(s0 + NT * j, Tk - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + NT * j < Tk) {
+          const int pos = atomicAdd(&s_cur[w[j]], 1), r = pos - s_off[w[j]];
+          a.slots[pos] = s0 + NT * j;
+          if (r < 4) s_first[w[j] * 4 + r] = s0 + NT * j;
+        }
+    }
   }
   if (a.has_shared)
     for (int t = tid; t < a.T; t += NT) a.slots[Tk + t] = Tk + t;
   __syncthreads();   // every placement is done before s_cur is reused below
   // Work lists: streaming (0 < rows < R) and matrix-core (rows >= R).  With a
   // lookahead prediction the predicted experts come first; the order decides
-  // only when an expert's weights are read, never a value.  One scan per path
-  // counts both halves at once: predicted in the low 16 bits, the rest in the
-  // high 16 (each total <= kMaxExperts, so the halves never carry).
-  for (int path = 0; path < 2; ++path) {
-    for (int e = tid; e < E; e += NT) {
-      const int c = s_cnt[e];
-      const bool on = path == 0 ? (c > 0 && c < R) : (c >= R);
-      const bool first = pv ? s_pred[e] != 0 : true;
-      s_flag[e] = on ? (first ? 1 : 2) : 0;
-      s_cur[e] = on ? (first ? 1 : 0x10000) : 0;
-    }
-    __syncthreads();
-    const int tot = block_excl_scan<NT>(s_cur, E, s_scan);
-    const int n_first = tot & 0xffff;
-    for (int e = tid; e < E; e += NT)
-      if (s_flag[e]) {
-        const int pos = s_flag[e] == 1 ? (s_cur[e] & 0xffff) : n_first + (s_cur[e] >> 16);
-        if (path == 0) {   // streaming item: (expert, rows, offset) + its first 4 slots
-          const int c = s_cnt[e];
-          const int* f = s_first + e * 4;
-          a.items[2 * pos] = make_int4(e, c, s_off[e], 0);
-          a.items[2 * pos + 1] = make_int4(f[0], f[min(1, c - 1)], f[min(2, c - 1)], f[min(3, c - 1)]);
-        } else {
-          a.mitems[pos] = make_int4(e, s_cnt[e], s_off[e], 0);
-          s_mrows[pos] = s_cnt[e];
-        }
-      }
-    if (tid == 0) s_tot[path] = n_first + (tot >> 16);
-    __syncthreads();
+  // only when an expert's weights are read, never a value.  One dual scan
+  // counts both paths, each packed: predicted in the low 16 bits, the rest
+  // in the high 16 (each total <= kMaxExperts, so the halves never carry).
+  int* s_aux = s_flag;
+  for (int e = tid; e < E; e += NT) {
+    const int c = s_cnt[e], inc = (pv ? s_pred[e] != 0 : true) ? 1 : 0x10000;
+    s_cur[e] = c > 0 && c < R ? inc : 0;
+    s_aux[e] = c >= R ? inc : 0;
   }
-  int n_gemv = s_tot[0], n_mfma = s_tot[1];
+  __syncthreads();
+  const int2 tl = block_excl_scan2<NT>(s_cur, s_aux, E, s_scan);
+  const int g_first = tl.x & 0xffff, m_first = tl.y & 0xffff;
+  for (int e = tid; e < E; e += NT) {
+    const int c = s_cnt[e];
+    const bool first = pv ? s_pred[e] != 0 : true;
+    if (c > 0 && c < R) {   // streaming item: (expert, rows, offset) + its first 4 slots
+      const int pos = first ? (s_cur[e] & 0xffff) : g_first + (s_cur[e] >> 16);
+      const int* f = s_first + e * 4;
+      a.items[2 * pos] = make_int4(e, c, s_off[e], 0);
+      a.items[2 * pos + 1] = make_int4(f[0], f[min(1, c - 1)], f[min(2, c - 1)], f[min(3, c - 1)]);
+    } else if (c >= R) {
+      const int pos = first ? (s_aux[e] & 0xffff) : m_first + (s_aux[e] >> 16);
+      a.mitems[pos] = make_int4(e, c, s_off[e], 0);
+      s_mrows[pos] = c;
+    }
+  }
+  int n_gemv = g_first + (tl.x >> 16), n_mfma = m_first + (tl.y >> 16);
   if (a.has_shared) {
     if (a.T >= R) {
       if (tid == 0) {
@@ -370,61 +439,60 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
     }
   }
   __syncthreads();
-  // matrix-core row tiles (item, first row): 128-row tiles for items with
-  // >= wide_min_rows rows, 32-row tiles for the others
-  int n_tiles = 0, n_narrow = 0;
-  if (tid < 8) {   // no wide units unless the tile pass below lists some
+  // Matrix-core row tiles (item, first row): 128-row tiles for items with >=
+  // wide_min_rows rows, 32-row tiles for the others, in item order; and the
+  // wide launches' per-XCD unit lists.  One dual scan: 128-row tiles per item
+  // packed (full << 16 | partial), 32-row tiles per item.  The shared
+  // expert, when on this path, is the last item.
+  int n_tiles = 0, n_narrow = 0, nts = 0;
+  if (tid < 8) {   // no wide units unless the pass below lists some
     a.misc[kUnitsUp + tid] = 0;
     a.misc[kUnitsDn + tid] = 0;
   }
   if (n_mfma > 0) {   // uniform across the workgroup
-    for (int wide = 1; wide >= 0; --wide) {
-      const int bm = wide ? kMfmaBM : kNarrowBM;
-      for (int i = tid; i < n_mfma; i += NT) {
-        const int rows = s_mrows[i];
-        const bool mine = wide ? rows >= a.wide_min_rows : rows < a.wide_min_rows;
-        s_flag[i] = mine ? (rows + bm - 1) / bm : 0;
-        s_cur[i] = s_flag[i];
-      }
-      __syncthreads();
-      const int n = block_excl_scan<NT>(s_cur, n_mfma, s_scan);
-      int2* out = wide ? a.mtiles : a.ntiles;
-      for (int i = tid; i < n_mfma; i += NT)
-        for (int j = 0; j < s_flag[i]; ++j) out[s_cur[i] + j] = make_int2(i, j * bm);
-      if (wide) {
-        // the shared expert, when on this path, is the last item
-        const bool sh_item = a.has_shared && a.T >= R;
-        const int nts = sh_item ? s_flag[n_mfma - 1] : 0;
-        // dealing order of the routed tiles: full tiles, then partial ones,
-        // each in item order (counts packed: full high, partial low)
-        int* s_fp = s_first;   // free: the streaming items are written
-        for (int i = tid; i < n_mfma; i += NT) {
-          const int rows = s_mrows[i];
-          s_fp[i] = (s_flag[i] > 0 && !(sh_item && i == n_mfma - 1))
-                        ? ((rows / kMfmaBM) << 16) | ((rows % kMfmaBM) ? 1 : 0) : 0;
-        }
-        __syncthreads();
-        const int nf = block_excl_scan<NT>(s_fp, n_mfma, s_scan) >> 16;
-        for (int t = tid; t < n; t += NT) {
-          // item of tile t: the last one whose first tile is <= t (it has tiles)
-          int lo = 0, hi = n_mfma - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_cur[mid] <= t) lo = mid; else hi = mid - 1;
-          }
-          const int j = t - s_cur[lo];
-          if (sh_item && lo == n_mfma - 1) {
-            put_units(a, t, j, true, nts);
-          } else {
-            const int f = s_mrows[lo] / kMfmaBM;
-            put_units(a, t, nts + (j < f ? (s_fp[lo] >> 16) + j : nf + (s_fp[lo] & 0xffff)), false, nts);
-          }
-        }
-        if (tid < 8) put_unit_counts(a, n, nts, tid);
-      }
-      __syncthreads();
-      if (wide) n_tiles = n; else n_narrow = n;
+    const int W = a.wide_min_rows;
+    for (int i = tid; i < n_mfma; i += NT) {
+      const int rows = s_mrows[i];
+      s_cur[i] = rows >= W ? ((rows / kMfmaBM) << 16) | ((rows % kMfmaBM) ? 1 : 0) : 0;
+      s_aux[i] = rows >= W ? 0 : (rows + kNarrowBM - 1) / kNarrowBM;
     }
+    __syncthreads();
+    const int2 tt = block_excl_scan2<NT>(s_cur, s_aux, n_mfma, s_scan);
+    n_tiles = (tt.x >> 16) + (tt.x & 0xffff);
+    n_narrow = tt.y;
+    const bool sh_wide = a.has_shared && a.T >= W;   // then the last item
+    nts = sh_wide ? (a.T + kMfmaBM - 1) / kMfmaBM : 0;
+    const int nf = (tt.x >> 16) - (sh_wide ? a.T / kMfmaBM : 0);   // routed full tiles
+    for (int i = tid; i < n_mfma; i += NT) {
+      const int rows = s_mrows[i];
+      if (rows >= W) {
+        const int t0 = (s_cur[i] >> 16) + (s_cur[i] & 0xffff);
+        for (int j = 0; j * kMfmaBM < rows; ++j) a.mtiles[t0 + j] = make_int2(i, j * kMfmaBM);
+      } else {
+        for (int j = 0; j * kNarrowBM < rows; ++j) a.ntiles[s_aux[i] + j] = make_int2(i, j * kNarrowBM);
+      }
+    }
+    // unit lists: eight threads per 128-row tile, each writing every eighth
+    // column block; routed tiles are dealt full ones first (item order), then
+    // partial ones
+    for (int it = tid; it < n_tiles * 8; it += NT) {
+      const int t = it >> 3, sub = it & 7;
+      // item of tile t: the last one whose first tile is <= t (it has tiles)
+      int lo = 0, hi = n_mfma - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((s_cur[mid] >> 16) + (s_cur[mid] & 0xffff) <= t) lo = mid; else hi = mid - 1;
+      }
+      const int j = t - (s_cur[lo] >> 16) - (s_cur[lo] & 0xffff);
+      if (sh_wide && lo == n_mfma - 1) {
+        put_units(a, t, j, true, nts, sub, 8);
+      } else {
+        const int f = s_mrows[lo] / kMfmaBM;
+        put_units(a, t, nts + (j < f ? (s_cur[lo] >> 16) + j : nf + (s_cur[lo] & 0xffff)), false, nts,
+                  sub, 8);
+      }
+    }
+    if (tid < 8) put_unit_counts(a, n_tiles, nts, tid);
   }
   if (tid == 0) {
     a.misc[kNGemv] = n_gemv;
@@ -531,7 +599,7 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
       if (c >= W) {
         const int nt = (c + kMfmaBM - 1) / kMfmaBM, f = c / kMfmaBM;
         for (int j = 0; j < nt; ++j) {
-          put_units(a, pw, nts + (j < f ? pf + j : nf + pp), false, nts);
+          put_units(a, pw, nts + (j < f ? pf + j : nf + pp), false, nts, 0, 1);
           a.mtiles[pw++] = make_int2(pos, j * kMfmaBM);
         }
         pf += f;
@@ -551,7 +619,7 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
       if (lane == 0) a.mitems[n_mfma] = make_int4(E, T, Tk, 0);
       for (int j = lane; j < nt; j += 64) {
         out[j] = make_int2(n_mfma, j * bm);
-        if (wide) put_units(a, n_tiles + j, j, true, nts);
+        if (wide) put_units(a, n_tiles + j, j, true, nts, 0, 1);
       }
       ++n_mfma;
       if (wide) n_tiles += nt; else n_narrow += nt;
@@ -1103,7 +1171,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a, int tpw)
 // LDS-atomic chains, four times shorter than with 256
 constexpr int kBucketThreads = 1024;
 __global__ __launch_bounds__(kBucketThreads) void bucket_kernel(RouterArgs a) {
-  __shared__ __align__(16) uint8_t smem[kBucketSmem];
+  __shared__ __align__(16) uint8_t smem[kBucketSlotOff + kBucketThreads * kBucketRegSlots * 4];
   bucket_tokens<kBucketThreads>(a, a.ids_ws, smem);
 }
 
