@@ -171,6 +171,27 @@ def test_repeatable_bitwise_large_batch(torch_dev):
         assert torch.equal(y, y0) and torch.equal(i, i0) and torch.equal(p, p0)
 
 
+def test_large_batch_atomic_placement(torch_dev):
+    """3000 tokens x top-6 = 18,000 slots: more than the bucketing pass keeps
+    in registers (16 per thread of 1,024), so slots are placed with atomic
+    cursors; every expert and the shared one run as many full and partial
+    128-row tiles spread over all eight per-XCD unit lists.  Checked against
+    the oracle on every token, and bitwise across runs."""
+    import torch
+    H, E, k, I, Is, T = 256, 16, 6, 128, 192, 3000
+    li = synth.LayerInputs(12, 91, 0, synth.LayerShape(H, E, k, I, Is), "normal0.5")
+    m = _layer(li, torch_dev, T)
+    ol = P.oracle_layer(li)
+    xb = synth.make_hidden(12, 91, T, H)
+    x = P.bf16_tensor(xb, torch_dev)
+    y0, i0, p0 = m.forward(x, return_selection=True)
+    P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y0.cpu().numpy(), i0.cpu().numpy(),
+                    p0.cpu().numpy(), "atomic placement T=3000")
+    for _ in range(2):
+        y, i, p = m.forward(x, return_selection=True)
+        assert torch.equal(y, y0) and torch.equal(i, i0) and torch.equal(p, p0)
+
+
 def test_error_paths(torch_dev):
     import torch
     from quantized_routed_expert_bit_amd import MoELayer, MoEError
