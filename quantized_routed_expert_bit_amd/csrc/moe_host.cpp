@@ -71,21 +71,12 @@ WsLayout ws_layout(const moe_config& c) {
     return r;
   };
   L.part = take(KS * T * Epad * 4);
-  L.logits = take(0);
   L.x16 = take(T * H * 2);
   L.x16lo = take(T * H * 2);
   L.xs = take(T * G * 8);
   L.ids = take(Tk * 4);
   L.p = take(Tk * 4);
-  L.rank = take(Tk * 4);
-  // counts, cnt_tb and misc are contiguous ints (zeroed together at bind time)
-  L.counts = o;
-  o += E * 4;
-  L.cnt_tb = o;
-  o += T * 4;
-  L.misc = o;
-  o += kMiscInts * 4;
-  o = al(o);
+  L.misc = take(kMiscInts * 4);   // zeroed at bind time
   L.offs = take((E + 1) * 4);
   L.slots = take((Tk + T) * 4);
   L.items = take((E + 1) * 32);   // (expert, rows, offset, 0) + first 4 slots

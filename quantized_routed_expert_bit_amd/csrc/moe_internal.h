@@ -51,7 +51,6 @@ inline int wide_cap(int nt, int nts, int ncr, int ncs) { return (nt + 7) / 8 * n
 
 // misc[] slots (int32) in the workspace
 enum MiscSlot {
-  kCntAll = 0,      // token blocks whose top-k is done (self-resetting)
   kNGemv = 1,       // items on the streaming path
   kNMfma = 2,       // items on the matrix-core path
   kNTiles = 3,      // matrix-core row tiles
@@ -63,7 +62,7 @@ enum MiscSlot {
 };
 
 struct WsLayout {
-  size_t part, logits, x16, x16lo, xs, ids, p, rank, counts, offs, cnt_tb, misc,
+  size_t part, x16, x16lo, xs, ids, p, offs, misc,
       slots, items, mitems, mtiles, ntiles, wunits_up, wunits_dn, pred, hbuf, hs, yslot, xn, total;
   int cap_up, cap_dn;   // entries per XCD of the wide unit lists
 };

@@ -500,7 +500,6 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
     a.misc[kNTiles] = n_tiles;
     a.misc[kNNarrow] = n_narrow;
     a.misc[kPredValid] = 0;
-    a.misc[kCntAll] = 0;
   }
 }
 
@@ -638,7 +637,6 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
     a.misc[kNTiles] = n_tiles;
     a.misc[kNNarrow] = n_narrow;
     a.misc[kPredValid] = 0;
-    a.misc[kCntAll] = 0;
   }
 }
 
@@ -2511,10 +2509,9 @@ hipError_t launch_combine(const LayerDev& d, int T, const float* p, const float*
 }
 
 hipError_t launch_ws_init(const LayerDev& d, hipStream_t s) {
-  // counts [E], cnt_tb [..], misc [kMiscInts] must start at zero; they are
-  // contiguous ints in the layout (counts .. misc end).
-  int* base = reinterpret_cast<int*>(wsp(d, d.L.counts));
-  const size_t n = (d.L.misc + kMiscInts * sizeof(int) - d.L.counts) / sizeof(int);
+  // misc [kMiscInts] must start at zero (no lookahead prediction pending)
+  int* base = reinterpret_cast<int*>(wsp(d, d.L.misc));
+  const size_t n = kMiscInts;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, base,
                      (int)n, 0);
   return hipGetLastError();
