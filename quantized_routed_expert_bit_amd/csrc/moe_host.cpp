@@ -81,14 +81,13 @@ WsLayout ws_layout(const moe_config& c) {
   L.slots = take((Tk + T) * 4);
   L.items = take((E + 1) * 32);   // (expert, rows, offset, 0) + first 4 slots
   L.mitems = take((E + 1) * 16);
-  L.mtiles = take(((Tk + kMfmaBM - 1) / kMfmaBM + E + (T + kMfmaBM - 1) / kMfmaBM + 1) * 8);
   {   // wide unit lists, one per XCD: routed tiles (rt bounds them) and shared tiles
     const int rt = (int)((Tk + kMfmaBM - 1) / kMfmaBM + E + 1), st = Ts ? (int)((T + kMfmaBM - 1) / kMfmaBM) : 0;
     L.cap_up = wide_cap(rt + st, st, (int)((I + kWideColsUp - 1) / kWideColsUp),
                         (int)((Is + kWideColsUp - 1) / kWideColsUp));
     L.cap_dn = wide_cap(rt + st, 0, (int)((H + kWideColsDn - 1) / kWideColsDn), 0);
-    L.wunits_up = take((size_t)8 * L.cap_up * 8);
-    L.wunits_dn = take((size_t)8 * L.cap_dn * 8);
+    L.wunits_up = take((size_t)8 * L.cap_up * 16);
+    L.wunits_dn = take((size_t)8 * L.cap_dn * 16);
   }
   L.ntiles = take(((Tk + kNarrowBM - 1) / kNarrowBM + E + (T + kNarrowBM - 1) / kNarrowBM + 1) * 8);
   L.pred = take(Tk * 4);

@@ -63,7 +63,7 @@ enum MiscSlot {
 
 struct WsLayout {
   size_t part, x16, x16lo, xs, ids, p, offs, misc,
-      slots, items, mitems, mtiles, ntiles, wunits_up, wunits_dn, pred, hbuf, hs, yslot, xn, total;
+      slots, items, mitems, ntiles, wunits_up, wunits_dn, pred, hbuf, hs, yslot, xn, total;
   int cap_up, cap_dn;   // entries per XCD of the wide unit lists
 };
 

@@ -250,10 +250,9 @@ struct RouterArgs {
   int* slots;
   int4* items;
   int4* mitems;
-  int2* mtiles;
   int2* ntiles;
-  int2* wunits_up;
-  int2* wunits_dn;
+  int4* wunits_up;
+  int4* wunits_dn;
   int mfma_min_rows, wide_min_rows, has_shared;
   int ncu_r, ncu_s, ncd;   // wide column blocks: routed and shared gate/up, down
   int cap_up, cap_dn;      // entries per XCD of the wide unit lists
@@ -270,16 +269,19 @@ __device__ __forceinline__ int dealt(int n, int x) {
   const int r = n >> 3, pos = (r & 1) ? 7 - x : x;
   return r + (pos < (n & 7) ? 1 : 0);
 }
-// Units of tile t, dealt at position q (the nts shared tiles take positions
-// 0 .. nts - 1): column blocks c0, c0 + cs, ...
-__device__ void put_units(const RouterArgs& a, int t, int q, bool sh, int nts, int c0, int cs) {
+// Units of a row tile (expert e, slot list position first, rows rows),
+// dealt at position q (the nts shared tiles take positions 0 .. nts - 1):
+// column blocks c0, c0 + cs, ...  An entry is (e, first, rows, column block),
+// everything a wide workgroup needs before it reads the tile's slots.
+__device__ void put_units(const RouterArgs& a, int e, int first, int rows, int q, bool sh, int nts,
+                          int c0, int cs) {
   const int r = q >> 3, pos = q & 7, x = (r & 1) ? 7 - pos : pos;
   const int ds = sh ? r : dealt(nts, x);   // shared tiles before it on XCD x
-  int2* up = a.wunits_up + x * a.cap_up + ds * a.ncu_s + (r - ds) * a.ncu_r;
-  int2* dn = a.wunits_dn + x * a.cap_dn + r * a.ncd;
+  int4* up = a.wunits_up + x * a.cap_up + ds * a.ncu_s + (r - ds) * a.ncu_r;
+  int4* dn = a.wunits_dn + x * a.cap_dn + r * a.ncd;
   const int ncu = sh ? a.ncu_s : a.ncu_r;
-  for (int c = c0; c < ncu; c += cs) up[c] = make_int2(t, c);
-  for (int c = c0; c < a.ncd; c += cs) dn[c] = make_int2(t, c);
+  for (int c = c0; c < ncu; c += cs) up[c] = make_int4(e, first, rows, c);
+  for (int c = c0; c < a.ncd; c += cs) dn[c] = make_int4(e, first, rows, c);
 }
 // List lengths of XCD x for nt tiles, nts of them shared.
 __device__ __forceinline__ void put_unit_counts(const RouterArgs& a, int nt, int nts, int x) {
@@ -288,7 +290,7 @@ __device__ __forceinline__ void put_unit_counts(const RouterArgs& a, int nt, int
   a.misc[kUnitsDn + x] = d * a.ncd;
 }
 
-constexpr int kBucketSmem = 5 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + 16 * kMaxExperts + kMaxExperts;
+constexpr int kBucketSmem = 6 * (kMaxExperts + 2) * 4 + 256 * 4 + 16 + 16 * kMaxExperts + kMaxExperts;
 constexpr int kBucketRegSlots = 16;   // slots per thread kept in registers
 constexpr int kBucketSlotOff = (kBucketSmem + 15) & ~15;   // LDS slot list (register case)
 
@@ -307,7 +309,8 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
   int* s_tot = s_scan + 256;                                 // [4]
   int* s_mrows = s_tot + 4;                                  // [E + 1] rows per matrix-core item
   int* s_first = s_mrows + kMaxExperts + 2;                  // [E][4] first slots per expert
-  unsigned char* s_pred = reinterpret_cast<unsigned char*>(s_first + 4 * kMaxExperts);   // [E]
+  int* s_mexp = s_first + 4 * kMaxExperts;                   // [E + 1] expert of each matrix-core item
+  unsigned char* s_pred = reinterpret_cast<unsigned char*>(s_mexp + kMaxExperts + 2);   // [E]
   const int tid = threadIdx.x;
   const int E = a.E, Tk = a.T * a.k;
   const int R = a.mfma_min_rows;
@@ -419,6 +422,7 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
       const int pos = first ? (s_aux[e] & 0xffff) : m_first + (s_aux[e] >> 16);
       a.mitems[pos] = make_int4(e, c, s_off[e], 0);
       s_mrows[pos] = c;
+      s_mexp[pos] = e;
     }
   }
   int n_gemv = g_first + (tl.x >> 16), n_mfma = m_first + (tl.y >> 16);
@@ -427,6 +431,7 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
       if (tid == 0) {
         a.mitems[n_mfma] = make_int4(E, a.T, Tk, 0);
         s_mrows[n_mfma] = a.T;
+        s_mexp[n_mfma] = E;
       }
       ++n_mfma;
     } else {
@@ -439,11 +444,11 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
     }
   }
   __syncthreads();
-  // Matrix-core row tiles (item, first row): 128-row tiles for items with >=
-  // wide_min_rows rows, 32-row tiles for the others, in item order; and the
-  // wide launches' per-XCD unit lists.  One dual scan: 128-row tiles per item
-  // packed (full << 16 | partial), 32-row tiles per item.  The shared
-  // expert, when on this path, is the last item.
+  // Matrix-core row tiles: items with >= wide_min_rows rows take 128-row
+  // tiles, listed as the wide launches' per-XCD units; the others take
+  // 32-row tiles (item, first row), in item order.  One dual scan: 128-row
+  // tiles per item packed (full << 16 | partial), 32-row tiles per item.  The
+  // shared expert, when on this path, is the last item.
   int n_tiles = 0, n_narrow = 0, nts = 0;
   if (tid < 8) {   // no wide units unless the pass below lists some
     a.misc[kUnitsUp + tid] = 0;
@@ -465,12 +470,8 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
     const int nf = (tt.x >> 16) - (sh_wide ? a.T / kMfmaBM : 0);   // routed full tiles
     for (int i = tid; i < n_mfma; i += NT) {
       const int rows = s_mrows[i];
-      if (rows >= W) {
-        const int t0 = (s_cur[i] >> 16) + (s_cur[i] & 0xffff);
-        for (int j = 0; j * kMfmaBM < rows; ++j) a.mtiles[t0 + j] = make_int2(i, j * kMfmaBM);
-      } else {
+      if (rows < W)
         for (int j = 0; j * kNarrowBM < rows; ++j) a.ntiles[s_aux[i] + j] = make_int2(i, j * kNarrowBM);
-      }
     }
     // unit lists: eight threads per 128-row tile, each writing every eighth
     // column block; routed tiles are dealt full ones first (item order), then
@@ -484,12 +485,14 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
         if ((s_cur[mid] >> 16) + (s_cur[mid] & 0xffff) <= t) lo = mid; else hi = mid - 1;
       }
       const int j = t - (s_cur[lo] >> 16) - (s_cur[lo] & 0xffff);
+      const int e = s_mexp[lo], first = (e == E ? Tk : s_off[e]) + j * kMfmaBM;
+      const int rows = min(kMfmaBM, s_mrows[lo] - j * kMfmaBM);
       if (sh_wide && lo == n_mfma - 1) {
-        put_units(a, t, j, true, nts, sub, 8);
+        put_units(a, e, first, rows, j, true, nts, sub, 8);
       } else {
         const int f = s_mrows[lo] / kMfmaBM;
-        put_units(a, t, nts + (j < f ? (s_cur[lo] >> 16) + j : nf + (s_cur[lo] & 0xffff)), false, nts,
-                  sub, 8);
+        put_units(a, e, first, rows, nts + (j < f ? (s_cur[lo] >> 16) + j : nf + (s_cur[lo] & 0xffff)),
+                  false, nts, sub, 8);
       }
     }
     if (tid < 8) put_unit_counts(a, n_tiles, nts, tid);
@@ -571,7 +574,7 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
   const int xg = ig - ng, xm = im - nm, xt = it - ntl;
   int pg0 = xg & 0xffff, pg1 = (tg & 0xffff) + (xg >> 16);
   int pm0 = xm & 0xffff, pm1 = (tm & 0xffff) + (xm >> 16);
-  int pw = xt & 0xffff, pn = xt >> 16;
+  int pn = xt >> 16;
   // dealing order of the routed 128-row tiles: full tiles, then partial
   // ones, each in item order (per-lane counts packed: full high, partial low)
   int fp = 0;
@@ -598,8 +601,8 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
       if (c >= W) {
         const int nt = (c + kMfmaBM - 1) / kMfmaBM, f = c / kMfmaBM;
         for (int j = 0; j < nt; ++j) {
-          put_units(a, pw, nts + (j < f ? pf + j : nf + pp), false, nts, 0, 1);
-          a.mtiles[pw++] = make_int2(pos, j * kMfmaBM);
+          put_units(a, e, s_off[e] + j * kMfmaBM, min(kMfmaBM, c - j * kMfmaBM),
+                    nts + (j < f ? pf + j : nf + pp), false, nts, 0, 1);
         }
         pf += f;
         pp += nt - f;
@@ -614,11 +617,12 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
     if (T >= R) {
       const bool wide = T >= W;
       const int bm = wide ? kMfmaBM : kNarrowBM, nt = (T + bm - 1) / bm;
-      int2* out = wide ? a.mtiles + n_tiles : a.ntiles + n_narrow;
       if (lane == 0) a.mitems[n_mfma] = make_int4(E, T, Tk, 0);
       for (int j = lane; j < nt; j += 64) {
-        out[j] = make_int2(n_mfma, j * bm);
-        if (wide) put_units(a, n_tiles + j, j, true, nts, 0, 1);
+        if (wide)
+          put_units(a, E, Tk + j * bm, min(bm, T - j * bm), j, true, nts, 0, 1);
+        else
+          a.ntiles[n_narrow + j] = make_int2(n_mfma, j * bm);
       }
       ++n_mfma;
       if (wide) n_tiles += nt; else n_narrow += nt;
@@ -1315,10 +1319,9 @@ struct MfmaArgs {
   const uint16_t* hsrc;    // down: h rows
   uint16_t* hdst;          // up: h rows
   const int4* mitems;
-  const int2* mtiles;
   const int2* ntiles;
-  const int2* wunits_up;   // wide units (tile, column block): per-XCD lists
-  const int2* wunits_dn;
+  const int4* wunits_up;   // wide units (expert, first slot, rows, column block): per-XCD lists
+  const int4* wunits_dn;
   int cap_up, cap_dn;
   const int* misc;
   const int* slots;
@@ -1406,12 +1409,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   static_assert(CB == (UP ? kWideColsUp : kWideColsDn), "unit lists assume kWideWaves waves");
   const int xcd = (int)blockIdx.x & 7, ib = (int)blockIdx.x >> 3;
   if (ib >= a.misc[(UP ? kUnitsUp : kUnitsDn) + xcd]) return;
-  const int2 un = UP ? a.wunits_up[xcd * a.cap_up + ib] : a.wunits_dn[xcd * a.cap_dn + ib];
-  const int tile_i = un.x, cblk = un.y;
-  const int2 tl = a.mtiles[tile_i];
-  const int4 it = a.mitems[tl.x];
-  const int e = it.x, m_tot = it.y, loff = it.z, m0 = tl.y;
-  const int mrows = min(kMfmaBM, m_tot - m0);
+  const int4 un = UP ? a.wunits_up[xcd * a.cap_up + ib] : a.wunits_dn[xcd * a.cap_dn + ib];
+  const int e = un.x, first = un.y, mrows = un.z, cblk = un.w;
   const bool sh = e == a.E;
   const int inter = sh ? a.Is : a.I;
   const int G = a.H >> 6;
@@ -1424,7 +1423,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   const bool won = n0 < ncols;
   const int Tk = a.T * a.k;
   if (tid < kMfmaBM) {
-    const int slot = a.slots[loff + m0 + (tid < mrows ? tid : 0)];
+    const int slot = a.slots[first + (tid < mrows ? tid : 0)];
     s_slot[tid] = slot;
     s_src[tid] = UP ? (slot < Tk ? slot / a.k : slot - Tk) * a.H : (int)h_off(slot, Tk, a.I, a.Is);
   }
@@ -2255,10 +2254,9 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   a.slots = reinterpret_cast<int*>(wsp(d, d.L.slots));
   a.items = reinterpret_cast<int4*>(wsp(d, d.L.items));
   a.mitems = reinterpret_cast<int4*>(wsp(d, d.L.mitems));
-  a.mtiles = reinterpret_cast<int2*>(wsp(d, d.L.mtiles));
   a.ntiles = reinterpret_cast<int2*>(wsp(d, d.L.ntiles));
-  a.wunits_up = reinterpret_cast<int2*>(wsp(d, d.L.wunits_up));
-  a.wunits_dn = reinterpret_cast<int2*>(wsp(d, d.L.wunits_dn));
+  a.wunits_up = reinterpret_cast<int4*>(wsp(d, d.L.wunits_up));
+  a.wunits_dn = reinterpret_cast<int4*>(wsp(d, d.L.wunits_dn));
   a.mfma_min_rows = d.mfma_min_rows;
   a.wide_min_rows = d.wide_min_rows;
   a.has_shared = d.has_shared;
@@ -2456,9 +2454,8 @@ static MfmaArgs mfma_args(const LayerDev& d, int T) {
   m.hsrc = reinterpret_cast<const uint16_t*>(wsp(d, d.L.hbuf));
   m.hdst = reinterpret_cast<uint16_t*>(wsp(d, d.L.hbuf));
   m.mitems = reinterpret_cast<const int4*>(wsp(d, d.L.mitems));
-  m.mtiles = reinterpret_cast<const int2*>(wsp(d, d.L.mtiles));
-  m.wunits_up = reinterpret_cast<const int2*>(wsp(d, d.L.wunits_up));
-  m.wunits_dn = reinterpret_cast<const int2*>(wsp(d, d.L.wunits_dn));
+  m.wunits_up = reinterpret_cast<const int4*>(wsp(d, d.L.wunits_up));
+  m.wunits_dn = reinterpret_cast<const int4*>(wsp(d, d.L.wunits_dn));
   m.cap_up = d.L.cap_up;
   m.cap_dn = d.L.cap_dn;
   m.ntiles = reinterpret_cast<const int2*>(wsp(d, d.L.ntiles));
