@@ -1416,7 +1416,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   const int G = a.H >> 6;
   const int Kg = UP ? G : inter >> 6;
   const int ncols = UP ? inter : a.H;
-  if (cblk * CB >= ncols) return;
+  if (cblk * CB >= ncols) return;   // (never for a listed unit; a guard)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5, l32 = lane & 31;
   const int n0 = cblk * CB + wave * (UP ? 32 : 64);

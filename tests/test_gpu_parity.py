@@ -193,6 +193,20 @@ def test_large_batch_atomic_placement(torch_dev):
         assert torch.equal(y, y0) and torch.equal(i, i0) and torch.equal(p, p0)
 
 
+def test_every_expert_wide_large_batch(torch_dev):
+    """300 tokens with every expert (and the shared one) on 128-row tiles,
+    however few rows it has: mostly partial tiles, one to four row blocks,
+    dealt over the per-XCD unit lists by the bucketing pass."""
+    wl = synth.WORKLOADS[1]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, 300, mfma_min_rows=1, wide_min_rows=1)
+    ol = P.oracle_layer(li)
+    xb = synth.make_hidden(0, 1, 300, wl.shape.hidden, tag=21)
+    y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+    P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                    p.cpu().numpy(), "all wide T=300")
+
+
 def test_error_paths(torch_dev):
     import torch
     from quantized_routed_expert_bit_amd import MoELayer, MoEError
