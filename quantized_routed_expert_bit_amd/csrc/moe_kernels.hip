@@ -1398,7 +1398,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   constexpr int STAGE = NA * kWideA + kWideB + kWideS;    // halfs
   constexpr int AJ = 16 / NW;                   // A DMA instructions per wave per plane
   __shared__ __align__(16) uint16_t ring[NST * STAGE];
-  __shared__ int s_src[kMfmaBM];    // element offset of each row's A source
+  __shared__ size_t s_src[kMfmaBM];   // element offset of each row's A source (h rows pass 2^31)
   __shared__ int s_slot[kMfmaBM];
   // (tile, column block) units from the bucketing pass's per-XCD lists:
   // workgroup b runs on XCD b % 8 and takes entry b / 8 of its list, so an
@@ -1425,7 +1425,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   if (tid < kMfmaBM) {
     const int slot = a.slots[first + (tid < mrows ? tid : 0)];
     s_slot[tid] = slot;
-    s_src[tid] = UP ? (slot < Tk ? slot / a.k : slot - Tk) * a.H : (int)h_off(slot, Tk, a.I, a.Is);
+    s_src[tid] = UP ? (size_t)(slot < Tk ? slot / a.k : slot - Tk) * a.H : h_off(slot, Tk, a.I, a.Is);
   }
   const uint8_t* rec = sh ? a.shared : a.bank + (size_t)e * a.stride;
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
@@ -2112,8 +2112,9 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, int T, int h
                                                       const float* __restrict__ p,
                                                       const float* __restrict__ yslot,
                                                       const float* residual, float* y) {
-  const int t = blockIdx.y;
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  // flat grid, token-major (a token's column blocks are neighbours)
+  const int nb = (H + 255) / 256, t = (int)blockIdx.x / nb;
+  const int c = ((int)blockIdx.x - t * nb) * 256 + threadIdx.x;
   if (c >= H) return;
   const int Tk = T * k;
   float acc = 0.f;
@@ -2509,7 +2510,7 @@ hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s) {
 hipError_t launch_combine(const LayerDev& d, int T, const float* p, const float* residual, float* y,
                           hipStream_t s) {
   const float* yslot = reinterpret_cast<const float*>(wsp(d, d.L.yslot));
-  hipLaunchKernelGGL(combine_kernel, dim3((d.H + 255) / 256, T), dim3(256), 0, s, d.H, d.k, T,
+  hipLaunchKernelGGL(combine_kernel, dim3(T * ((d.H + 255) / 256)), dim3(256), 0, s, d.H, d.k, T,
                      d.has_shared, p, yslot, residual, y);
   return hipGetLastError();
 }

@@ -133,6 +133,32 @@ def test_layer_parity_edge_shapes(torch_dev, shape):
                         p.cpu().numpy(), f"edge T={t}")
 
 
+def test_h_offsets_past_2_31(torch_dev):
+    """65,535 tokens, 3 of 3 experts, 16,384-wide intermediate: the h rows of the
+    slots past 131,072 start beyond element 2^31 of the h buffer (6.4 GB), so
+    the down kernels' row offsets must be 64-bit.  Sampled tokens (every token is
+    computed on its own) against the oracle, including slots on both sides of
+    the boundary."""
+    import torch
+    free, _ = torch.cuda.mem_get_info(torch_dev)
+    if free < 12 * 2 ** 30:
+        pytest.skip("needs 12 GiB of free device memory")
+    H, E, k, I, T = 64, 3, 3, 16384, 65535
+    P.log(f"large offsets: H={H} E={E} k={k} I={I} T={T}")
+    li = synth.LayerInputs(11, 92, 0, synth.LayerShape(H, E, k, I, 0), "normal0.5")
+    m = _layer(li, torch_dev, T)
+    ol = P.oracle_layer(li)
+    xb = synth.make_hidden(11, 92, T, H)
+    y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+    torch.cuda.synchronize()
+    first_past = (2 ** 31 // I + k - 1) // k   # first token with a slot past the boundary
+    sample = np.r_[0:8, first_past - 8:first_past + 8, T - 8:T]
+    P.check_forward(ol, oracle.bf16_bits_to_f64(xb[sample]), y.cpu().numpy()[sample],
+                    ids.cpu().numpy()[sample], p.cpu().numpy()[sample], "large offsets, sampled")
+    del m, y, ids, p
+    torch.cuda.empty_cache()
+
+
 def test_fp32_input_parity(torch_dev):
     import torch
     wl = synth.WORKLOADS[0]
