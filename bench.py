@@ -213,6 +213,74 @@ def cpu_baseline(layer0, sh, T):
                        f"generation excluded): {el:.2f} s")
 
 
+def run_large(args, dev, n_inputs=4):
+    """The large decode layer (hidden 7168, 512 experts, top-16, intermediate
+    2048, shared expert 2048; a 12.7 GB bank generated on the device) at 1, 8
+    and 64 tokens per forward.  The timed graph rotates over n_inputs token
+    batches, so successive forwards read different experts (the active set is
+    larger than the 256 MB Infinity Cache)."""
+    import torch
+    import synth
+    from quantized_routed_expert_bit_amd import MoELayer
+    from tests.parity import bf16_tensor
+    wl = synth.WORKLOADS[3]
+    sh = wl.shape
+    bank, stride = synth.gpu_bank(0, 3, 0, sh.hidden, sh.inter, sh.n_experts, dev)
+    shared, _ = synth.gpu_bank(0, 3, 0, sh.hidden, sh.shared_inter, 1, dev, shared=True)
+    router = synth.make_router(0, 3, 0, sh.hidden, sh.n_experts)
+    bias = synth.make_router_bias(0, 3, 0, sh.n_experts, wl.bias)
+    m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, max(wl.batches))
+    m.set_weights(torch.from_numpy(router).to(dev), bank, stride, shared,
+                  None if bias is None else torch.from_numpy(bias).to(dev))
+    log("  large layer uploaded")
+    out = {}
+    for T in wl.batches:
+        xs = [bf16_tensor(synth.make_hidden(0, 3, T, sh.hidden, tag=200 + i), dev) for i in range(n_inputs)]
+        y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
+        distinct = []
+        for x in xs:
+            _, ids, _ = m.forward(x, return_selection=True)
+            distinct.append(int((np.bincount(ids.cpu().numpy().reshape(-1), minlength=sh.n_experts) > 0).sum()))
+        for i in range(args.warmup):
+            m.forward(xs[i % n_inputs], y=y)
+        torch.cuda.synchronize()
+        steps = args.steps
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                m.forward(xs[i % n_inputs], y=y)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        del g
+        kp = min(steps, 40)
+        m.profile_start(kp)
+        torch.cuda._sleep(int(2.4e9 * 0.05))
+        for i in range(kp):
+            m.forward(xs[i % n_inputs], y=y)
+        torch.cuda.synchronize()
+        kern, _ = m.profile_read()
+        d = float(np.mean(distinct))
+        alg = d * record_bytes(sh.hidden, sh.inter) + record_bytes(sh.hidden, sh.shared_inter) + \
+            sh.n_experts * sh.hidden * 17 / 16 + T * sh.hidden * 6 + T * sh.top_k * 8
+        us = el * 1e6 / steps
+        out[f"T{T}"] = {"tokens_s": round(T * steps / el, 1), "us_per_step": round(us, 2),
+                        "distinct_experts": d, "alg_bytes_per_step": int(alg),
+                        "layer_GB_s": round(alg / (us * 1e-6) / 1e9, 1),
+                        "layer_frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "kernel_us": {k: round(v * 1e3, 3) for k, v in kern.items()}}
+        log(f"large T={T}: {out[f'T{T}']}")
+    m.close()
+    del bank, shared
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,8 +291,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the T=1 and T=4 lines")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
-    ap.add_argument("--workload", choices=("all", "decode", "prefill"), default="all",
-                    help="decode: only the 16-token decode line; prefill: only the prefill line")
+    ap.add_argument("--workload", choices=("all", "decode", "prefill", "large"), default="all",
+                    help="decode: only the 16-token decode line; prefill: only the prefill line; "
+                         "large: only the hidden-7168, 512-expert decode layer at 1, 8 and 64 tokens")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -237,6 +306,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.workload == "prefill":
         print(json.dumps({"prefill": run_prefill(args, dev)}), flush=True)
+        return
+    if args.workload == "large":
+        print(json.dumps({"large_decode": run_large(args, dev)}), flush=True)
         return
     if args.workload == "decode":
         args.no_extra = args.no_prefill = args.no_cpu_baseline = True

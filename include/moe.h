@@ -178,7 +178,8 @@ int moe_router_logits(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_to
  * tokens routed to it in one forward (T for the shared expert).  Rows below
  * mfma_min_rows take the streaming dot-product path; rows in
  * [mfma_min_rows, wide_min_rows) take the matrix-core path in 32-row tiles;
- * rows >= wide_min_rows take it in 128-row tiles.  Defaults 4 and 32.
+ * rows >= wide_min_rows take it in 128-row tiles.  Defaults: 4 and 32, or 2
+ * and 32 when hidden >= 4096.
  * mfma_min_rows = 1 sends every expert to the matrix cores; values above
  * max_tokens keep them all on the streaming path.  Never changes the selected
  * experts.  Errors: MOE_EINVAL unless 1 <= mfma_min_rows <= wide_min_rows. */

@@ -160,7 +160,11 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
   d.Is = d.has_shared ? cfg->shared_inter : 0;
   d.rmsnorm = (cfg->flags & MOE_F_RMSNORM) ? 1 : 0;
   d.max_tokens = cfg->max_tokens;
-  d.mfma_min_rows = 4;
+  // Experts with 2 or 3 rows stream at hidden 2816 (16 tokens: 77.7 against
+  // 83 us per forward when they take 32-row matrix-core tiles) but take the
+  // tiles at hidden 7168, where each tile wave's K chain is long (8 tokens:
+  // 501 against 551 us; 64 tokens: 2218 against 3040 us).
+  d.mfma_min_rows = cfg->hidden >= 4096 ? 2 : 4;
   d.wide_min_rows = 32;
   d.L = ws_layout(*cfg);
   if (hipSetDevice(cfg->device) != hipSuccess ||
