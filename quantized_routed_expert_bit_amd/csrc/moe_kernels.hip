@@ -2360,10 +2360,13 @@ hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
   size_t lds = (size_t)mt * ((x_f32 ? d.H : d.H / 2) + 2 * (d.H / 64)) * 4;
-  // units: 64-row blocks, or their 32-row halves while the 64-row units
-  // would not give every CU two workgroups
+  // units: 64-row blocks with one matrix per wave when there are many of
+  // them (more resident workgroups to hide each one's staging), else their
+  // 32-row halves with both matrices per wave (twice the workgroups, a
+  // shorter chain per wave).  (64-row units with both matrices per wave were
+  // measured slower than either.)
   const int units64 = (shared_streams(d, T) ? d.Is / 64 : 0) + routed_stream_items(d, T) * (d.I / 64);
-  const bool half = units64 < 2 * d.n_cu;
+  const bool split = units64 >= 1024, half = !split;
   const int rpu = half ? 32 : 64;
   const int nsh = shared_streams(d, T) ? d.Is / rpu : 0, nunits = d.I / rpu;
   const int units = nsh + routed_stream_items(d, T) * nunits;
@@ -2372,17 +2375,10 @@ hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s) {
   const int nsht = narrow_shared_tiles(d, T), ncbs = d.Is / 32, ncbr = d.I / 32;
   const int nn = nsht * ncbs + (narrow_tiles_max(d, T) - nsht) * ncbr;
   if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
-  // many workgroups: one matrix per wave (more resident workgroups to hide
-  // each one's staging); few: both matrices per wave (shorter per-wave
-  // chain)
-  const bool split = units64 >= 1024;
   const size_t red_bytes = (size_t)(split ? 1 : 2) * kGemvWaves * kGemvTokV2 * 64 * 4;
   if (lds < red_bytes) lds = red_bytes;
-  // (split implies 64-row units: 1024 of them exceed the 32-row threshold)
-  auto* kern = x_f32 ? (split ? gemv_up_kernel<true, true, false>
-                              : half ? gemv_up_kernel<true, false, true> : gemv_up_kernel<true, false, false>)
-                     : (split ? gemv_up_kernel<false, true, false>
-                              : half ? gemv_up_kernel<false, false, true> : gemv_up_kernel<false, false, false>);
+  auto* kern = x_f32 ? (split ? gemv_up_kernel<true, true, false> : gemv_up_kernel<true, false, true>)
+                     : (split ? gemv_up_kernel<false, true, false> : gemv_up_kernel<false, false, true>);
   hipLaunchKernelGGL(kern, dim3(nn + units), dim3(kGemvThreads), lds, s, d.bank, d.stride,
                      d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.x16lo, p.xs, p.items, p.misc,
                      p.slots, p.hbuf, p.hs, nsh, nunits, mt, mfma_args(d, T), nsht, ncbs, ncbr);

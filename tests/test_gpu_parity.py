@@ -99,8 +99,9 @@ def test_layer_parity_decode(torch_dev, cfg):
 
 def test_streaming_unit_layouts(torch_dev):
     """Decode batch sizes that select each streaming layout at the decode
-    shape: 32-row gate/up units (2 tokens), 64-row units with both matrices
-    per wave (8), one matrix per wave with four-row-block down units (12)."""
+    shape: 32-row gate/up units with two-row-block down units (2 and 8
+    tokens), 64-row gate/up units with one matrix per wave and four-row-block
+    down units (12)."""
     wl = synth.WORKLOADS[1]
     li = synth.layer_inputs(wl)
     m = _layer(li, torch_dev, 12)
