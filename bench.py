@@ -213,6 +213,36 @@ def cpu_baseline(layer0, sh, T):
                        f"generation excluded): {el:.2f} s")
 
 
+def measure_ceilings(dev):
+    """What this GPU reaches on plain work, beside the spec peaks: a 1 GiB
+    device-to-device copy (bytes read + written per second) and a dense fp16
+    8192^3 matrix product through torch (hipBLASLt)."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, dtype=torch.float16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.float16, device=dev)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+    t_copy = timed(lambda: dst.copy_(src), 20)
+    t_mm = timed(lambda: torch.mm(a, b), 20)
+    out = {"copy_GB_s": round(2 * src.numel() / t_copy / 1e9, 1),
+           "f16_gemm_TFLOP_s": round(2 * 8192 ** 3 / t_mm / 1e12, 1),
+           "what": "1 GiB device-to-device copy (read + write bytes); torch.mm fp16 8192^3"}
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_large(args, dev, n_inputs=4):
     """The large decode layer (hidden 7168, 512 experts, top-16, intermediate
     2048, shared expert 2048; a 12.7 GB bank generated on the device) at 1, 8
@@ -376,12 +406,19 @@ def main():
         out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers[0], sh, T)
+    if not args.no_extra:
+        c = measure_ceilings(dev)
+        c["gemv_up_frac_of_copy"] = round(achieved / c["copy_GB_s"], 4)
+        out["ceilings"] = c
     if not args.no_prefill:
         for m in layers:
             m.close()
         del layers
         torch.cuda.empty_cache()
         out["prefill"] = run_prefill(args, dev)
+        if "ceilings" in out:
+            out["ceilings"]["prefill_layer_frac_of_gemm"] = round(
+                out["prefill"]["layer_TFLOP_s"] / out["ceilings"]["f16_gemm_TFLOP_s"], 4)
     print(json.dumps(out), flush=True)
 
 
