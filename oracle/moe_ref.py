@@ -166,12 +166,15 @@ class OracleLayer:
     def logits(self, x: np.ndarray) -> np.ndarray:
         return router_logits(x, self.wr, self.beta)
 
-    def forward(self, x: np.ndarray, logits=None, force_ids=None) -> dict:
+    def forward(self, x: np.ndarray, logits=None, force_ids=None, pool=None) -> dict:
         """x fp64 [T, H] -> dict(y, ids, p, gap, logits).
 
         ``force_ids`` [T, k] replaces the top-k selection (the layer evaluated
         on a given selection; p is still the softmax of the oracle's logits of
-        those experts).  Used where the top-k is not unique within a tolerance."""
+        those experts).  Used where the top-k is not unique within a tolerance.
+        ``pool`` (an executor with ``map``) evaluates the experts concurrently;
+        each expert's rows are computed on their own either way, so the result
+        is the same."""
         x = np.asarray(x, dtype=np.float64)
         t = x.shape[0]
         lg = self.logits(x) if logits is None else logits
@@ -181,10 +184,13 @@ class OracleLayer:
         p = softmax_selected(lg, ids)
         # out[t, j] = FFN_{ids[t,j]}(x[t]); tokens sharing an expert are one matmul
         out = np.zeros((t, self.top_k, self.hidden))
-        for e in np.unique(ids):
+
+        def one(e):
             rows, cols = np.nonzero(ids == e)
             wg, wu, wd = expert_matrices(self.get_record(int(e)), self.hidden, self.inter)
-            out[rows, cols] = expert_ffn(x[rows], wg, wu, wd)
+            return rows, cols, expert_ffn(x[rows], wg, wu, wd)
+        for rows, cols, o in (pool.map if pool is not None else map)(one, np.unique(ids)):
+            out[rows, cols] = o
         y = np.zeros((t, self.hidden))
         for j in range(self.top_k):                      # fixed order: j ascending
             y += p[:, j:j + 1] * out[:, j]
@@ -201,16 +207,16 @@ def rms_normalize(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
 
 
 def oracle_stack(layers, x0: np.ndarray, lookahead_k: int | None = None,
-                 norm: bool = False) -> dict:
+                 norm: bool = False, pool=None) -> dict:
     """r_0 = x0; y_l = layer_l(n(r_l)); r_{l+1} = r_l + y_l, with n the RMS norm
     when ``norm`` (else the identity).  With lookahead_k, also the next layer's
     router on n(r_l) (its top-lookahead_k ids), for reporting only: it never
-    feeds back into the result."""
+    feeds back into the result.  ``pool`` is passed to each layer's forward."""
     r = np.asarray(x0, dtype=np.float64)
     per_layer = []
     for li, layer in enumerate(layers):
         xin = rms_normalize(r) if norm else r
-        res = layer.forward(xin)
+        res = layer.forward(xin, pool=pool)
         res["input"] = r
         if lookahead_k is not None and li + 1 < len(layers):
             pred, _ = select_topk(layers[li + 1].logits(xin), lookahead_k)

@@ -359,3 +359,97 @@ def test_stack_without_norm_grows_quadratically():
     small = oracle.expert_ffn(10 * x, *mats)
     big = oracle.expert_ffn(100 * x, *mats)
     assert 50 < np.abs(big).max() / np.abs(small).max() < 200      # ~ 10^2
+
+
+# ------------------------------------------- stack with the RMS pre-norm ----
+
+def _scalar_rms(v, eps=1e-6):
+    ms = sum(a * a for a in v) / len(v)
+    return [a / math.sqrt(ms + eps) for a in v]
+
+
+def test_stack_with_norm_matches_scalar_loops():
+    """Two tiny layers, r_{l+1} = r_l + layer_l(r_l / rms(r_l)), every step as
+    pure-Python scalar loops (norm, router, top-k, softmax, FFNs, residual)
+    against oracle_stack(norm=True).  The input is scaled by 5 so the norm
+    changes the layer input and the residual differs from the normalized rows
+    (a residual taken from the normalized rows, a norm left out, or a norm
+    applied to the output would each fail)."""
+    H, E, k, I, Is, T = 64, 4, 2, 64, 64, 2
+    layers, scal = [], []
+    for l in range(2):
+        router = synth.make_router(8, 95, l, H, E)
+        recs = [synth.make_record(8, 95, l, e, H, I) for e in range(E)]
+        shared = synth.make_record(8, 95, l, 0, H, Is, shared=True)
+        beta = np.random.default_rng(30 + l).standard_normal(E) * 0.01
+        layers.append(oracle.OracleLayer(H, E, k, I, Is, router, beta,
+                                         (lambda rs: (lambda e: rs[e]))(recs), shared))
+        scal.append((router, beta, recs, shared))
+    x = 5.0 * oracle.bf16_bits_to_f64(synth.make_hidden(8, 95, T, H))
+    r = x.tolist()
+    for router, beta, recs, shared in scal:
+        xin = [_scalar_rms(row) for row in r]
+        ys, _, _ = _scalar_layer(xin, router, beta, recs, shared, H, E, k, I, Is)
+        r = [[a + b for a, b in zip(rr, yy)] for rr, yy in zip(r, ys.tolist())]
+    res = oracle.oracle_stack(layers, x, norm=True)
+    want = np.array(r)
+    assert np.allclose(res["out"], want, rtol=1e-11, atol=1e-13 * np.abs(want).max())
+    # each layer's "input" is the un-normalized residual it was fed
+    assert np.array_equal(res["layers"][0]["input"], x)
+
+
+def test_stack_with_norm_residual_identity():
+    """With the norm on: out = x + sum_l y_l, and y_l = layer_l(rms(r_l)) for
+    the residual r_l that layer saw."""
+    layers = []
+    for l in range(3):
+        router = synth.make_router(1, 94, l, 128, 8)
+        recs = [synth.make_record(1, 94, l, e, 128, 64) for e in range(8)]
+        layers.append(oracle.OracleLayer(128, 8, 2, 64, 0, router, None,
+                                         (lambda rs: (lambda e: rs[e]))(recs)))
+    x = np.random.default_rng(6).standard_normal((4, 128)) * 3.0
+    res = oracle.oracle_stack(layers, x, norm=True)
+    ys = [lr["y"] for lr in res["layers"]]
+    assert np.allclose(res["out"], x + sum(ys), rtol=1e-15, atol=1e-14)
+    r = x
+    for layer, lr in zip(layers, res["layers"]):
+        assert np.array_equal(lr["input"], r)
+        again = layer.forward(r / np.sqrt(np.mean(r * r, axis=1, keepdims=True) + 1e-6))
+        assert np.allclose(again["y"], lr["y"], rtol=1e-14, atol=1e-15)
+        r = r + lr["y"]
+
+
+def test_forced_selection_is_hand_assembled_sum():
+    """forward(force_ids=S): y = sum_j softmax(l[S])_j FFN_{S_j}(x) + FFN_s(x),
+    assembled here with torch (float64, CPU) and scipy's softmax, on a forced
+    selection that differs from the top-k (the lowest-logit experts), so an
+    ignored force_ids fails."""
+    from scipy.special import softmax
+    H, E, k, I, Is = 128, 6, 2, 64, 128
+    layer, recs, shared = _tiny_layer(H, E, k, I, Is, beta=np.linspace(0, 0.5, E))
+    x = np.random.default_rng(13).standard_normal((3, H))
+    lg = layer.logits(x)
+    top, _ = oracle.select_topk(lg, k)
+    forced = np.argsort(lg, axis=1)[:, :k]           # the k lowest logits
+    assert not any(set(a) == set(b) for a, b in zip(top.tolist(), forced.tolist()))
+    res = layer.forward(x, force_ids=forced)
+    assert np.array_equal(res["ids"], forced)
+    for t in range(3):
+        p = softmax(lg[t, forced[t]])
+        assert np.allclose(res["p"][t], p, rtol=1e-14, atol=0)
+        y = _torch_ffn(x[t:t + 1], *oracle.expert_matrices(shared, H, Is))[0]
+        for j in range(k):
+            y = y + p[j] * _torch_ffn(x[t:t + 1], *oracle.expert_matrices(recs[forced[t, j]], H, I))[0]
+        assert np.allclose(res["y"][t], y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+
+
+def test_concurrent_expert_evaluation_is_identical():
+    """forward(pool=executor) gives bitwise the same result as the serial loop."""
+    from concurrent.futures import ThreadPoolExecutor
+    layer, _, _ = _tiny_layer(beta=np.zeros(6))
+    x = np.random.default_rng(14).standard_normal((9, 128))
+    a = layer.forward(x)
+    with ThreadPoolExecutor(4) as ex:
+        b = layer.forward(x, pool=ex)
+    for key in ("y", "ids", "p", "gap", "logits"):
+        assert np.array_equal(a[key], b[key]), key
