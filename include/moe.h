@@ -139,21 +139,33 @@ typedef struct moe_weights {
  * is invalid).  Pure host computation. */
 uint64_t moe_workspace_bytes(const moe_config *cfg);
 
-/* Validate cfg and create a context on cfg->device.  *out is set only on
- * success.  Errors: MOE_EINVAL (null or struct_size mismatch), MOE_EUNSUPPORTED
- * (shape outside the ranges above, group != 64), MOE_EHIP. */
+/* Validate cfg and create a context on cfg->device: the "open the model" step
+ * of the engine API the WASTE page lists (section "WASTE'in hedefi ve uygulama
+ * biçimi": open, set the RAM cap, generate, save a session, close), for one
+ * layer.  The context owns a side stream and two events (default priority).
+ * *out is set only on success.  Errors: MOE_EINVAL (null or struct_size
+ * mismatch), MOE_EUNSUPPORTED (shape outside the ranges above, group != 64),
+ * MOE_EHIP. */
 int moe_open(const moe_config *cfg, moe_ctx **out);
 
 /* Bind weights.  Copies every record header (and the shared one) to the host
  * with one synchronous copy on `stream`, validates each with
- * moe_check_record_header, and initialises the workspace's counters.  On any
- * failure the context keeps no weights (a later forward gives MOE_ESTATE).
- * Errors: MOE_EINVAL, MOE_EBADRECORD, MOE_ENOMEM (workspace too small),
- * MOE_EHIP. */
+ * moe_check_record_header (magic, expert id and offsets are checked before a
+ * record is ever used: WASTE page, "Disk streaming mimarisi"), and initialises
+ * the workspace's counters.  On any failure the context keeps no weights (a
+ * later forward gives MOE_ESTATE): it refuses rather than computes from
+ * unvalidated records.  Errors: MOE_EINVAL, MOE_EBADRECORD, MOE_ENOMEM
+ * (workspace too small), MOE_EHIP. */
 int moe_set_weights(moe_ctx *ctx, const moe_weights *w, void *stream);
 
 /* Run the layer on T = n_tokens rows of x (x_dtype MOE_BF16 or MOE_F32,
- * row-major [T, H]).  Writes y (fp32 [T, H]) = layer(x), or residual +
+ * row-major [T, H]): the "generate" step of the engine API, one layer of it
+ * (router on the GPU from resident weights, top-k, routed and shared experts,
+ * combine: TurboFieldfare page, "Token üretim süreci").  Two arguments go
+ * beyond the layer itself: `residual` fuses the residual add of a stack, and
+ * `lookahead_next` is the WASTE page's next-layer router run one residual
+ * ahead ("Önceden okuma ve router tahmini"); a flag in the config would have
+ * left the next layer's context unnamed.  Writes y (fp32 [T, H]) = layer(x), or residual +
  * layer(x) when residual (fp32 [T, H]) is non-NULL -- the residual stream
  * update r_{l+1} = r_l + y_l of a stack of layers (with MOE_F_RMSNORM the layer
  * sees the normalized x, the residual add does not); y may alias residual (an
@@ -169,8 +181,9 @@ int moe_forward(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
                 float *y, const float *residual, int32_t *ids_out, float *p_out,
                 moe_ctx *lookahead_next, void *stream);
 
-/* Router step only: logits fp32 [T, E] (including router_bias).  Same
- * argument rules as moe_forward. */
+/* Router step only: logits fp32 [T, E] (including router_bias), of the
+ * normalized rows when the context has MOE_F_RMSNORM.  Same argument rules as
+ * moe_forward. */
 int moe_router_logits(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
                       float *logits, void *stream);
 
@@ -201,7 +214,9 @@ int moe_set_path_rows(moe_ctx *ctx, int32_t mfma_min_rows, int32_t wide_min_rows
 int moe_profile_start(moe_ctx *ctx, int32_t max_calls);
 int moe_profile_read(moe_ctx *ctx, float *avg_ms, int32_t *n_calls, int32_t n_slots);
 
-/* Free the context (NULL is a no-op).  Does not touch borrowed memory. */
+/* Free the context (NULL is a no-op): the "close" step of the engine API
+ * (WASTE page, "WASTE'in hedefi ve uygulama biçimi").  Does not touch
+ * borrowed memory. */
 void moe_close(moe_ctx *ctx);
 
 const char *moe_strerror(int code);

@@ -390,8 +390,18 @@ int moe_router_logits(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_to
   int rc = check_forward(ctx, x, x_dtype, n_tokens, logits);
   if (rc != MOE_OK) return rc;
   if (n_tokens == 0) return MOE_OK;
-  hipError_t e = launch_router(ctx->d, x, x_dtype == MOE_F32, n_tokens, 1, logits, nullptr,
-                               nullptr, static_cast<hipStream_t>(stream));
+  const LayerDev& d = ctx->d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* xin = x;
+  int f32 = x_dtype == MOE_F32;
+  hipError_t e;
+  if (d.rmsnorm) {   // the router sees what the layer sees
+    e = launch_rmsnorm(d, x, f32, n_tokens, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "rmsnorm launch");
+    xin = d.ws + d.L.xn;
+    f32 = 1;
+  }
+  e = launch_router(d, xin, f32, n_tokens, 1, logits, nullptr, nullptr, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "router launch");
   return MOE_OK;
 }

@@ -25,9 +25,10 @@
 // The streaming dot products use v_dot2_f32_f16 on codes lifted to fp16 with
 // the exponent trick: (q | 0x6400) is the fp16 value 1024 + q exactly, so
 //     sum_k x_k (s q_k + b) = s * sum_k x_k (1024 + q_k) + (b - 1024 s) * sum_k x_k
-// with fp32 accumulation (the 4-bit path folds this with two group sums, see
-// GemvStream; the matrix-core router folds it per group).  The matrix-core
-// expert paths dequantize to fp16 s*q + b (one rounding).
+// with fp32 accumulation (the 4-bit expert path folds this with two group
+// sums, see GemvStream).  The router (VALU and matrix cores) first centres its
+// 8-bit codes to q - 128 (center8) and folds (b + 128 s) * sum x instead.  The
+// matrix-core expert paths dequantize to fp16 s*q + b (one rounding).
 
 #include "moe_internal.h"
 
@@ -83,6 +84,18 @@ struct Lift {
     return r;
   }
 };
+// 8-bit codes centred for the router: a lifted pair (1024 + q, 1024 + q') minus
+// 1152 is (q - 128, q' - 128), exact in fp16 (one v_pk_add_f16).  The router's
+// dot products then carry sum x (q - 128), the size of the logit itself,
+// instead of 1024 sum x + sum x q, whose fp32 rounding the fold's
+// cancellation would expose when a group's inputs share a large mean (the
+// residual stream deep in a stack).
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t center8(uint32_t lifted) {
+  const h2v c = {(_Float16)1152.f, (_Float16)1152.f};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, lifted) - c);
+}
+
 // Position of column c (within a 64-column group) in the paired fp16 order the
 // 4-bit and 8-bit dot products consume.
 __device__ __forceinline__ int pair_pos4(int c) { return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1); }
@@ -778,10 +791,11 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouterArgs a) {
 #pragma unroll
           for (int dw = 0; dw < 4; ++dw)
 #pragma unroll
-            for (int p = 0; p < 2; ++p) w[(cc * 4 + dw) * 2 + p] = L.q8(d[dw], p);
+            for (int p = 0; p < 2; ++p) w[(cc * 4 + dw) * 2 + p] = center8(L.q8(d[dw], p));
         }
+        // sum x (s q + b) = s * sum x (q - 128) + (b + 128 s) * sum x
         const float s = f16f(sbw[j] & 0xffffu), b = f16f(sbw[j] >> 16);
-        const float cf = fmaf(-1024.f, s, b);
+        const float cf = fmaf(128.f, s, b);
 #pragma unroll
         for (int t = 0; t < kRouterTokMax; ++t) {
           if (t < nt) {
@@ -952,9 +966,9 @@ __device__ void topk_select(const RouterArgs& a, float* s_lg, int* s_ids, int nt
 // owns tokens 32 (w & 1) .. +31 (one 32-row MFMA block) against experts
 // 32 (w >> 1) .. +31.  Per 64-wide group the token rows are converted to fp16
 // (the 8-bit pair order) into an LDS double buffer, the next groups' rows and
-// codes being loaded meanwhile; B is the lifted codes (1024 + q, exact in
+// codes being loaded meanwhile; B is the centred codes (q - 128, exact in
 // fp16), and the group's products are folded into the logits as
-// s * P + (b - 1024 s) * sum(x) in fp32, as in the VALU GEMV.  Writes the
+// s * P + (b + 128 s) * sum(x) in fp32, as in the VALU GEMV.  Writes the
 // same k-split partials; the eb == 0 workgroups also publish x16 and the
 // streaming path's group sums.
 constexpr int kRmTok = 64;   // tokens per matrix-core router tile
@@ -1061,12 +1075,12 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
     if (gl >= ng) break;
     const int buf = gl & 1;
     const uint32_t sb = sbq[gl];
-    const float s = f16f(sb & 0xffffu), cf = fmaf(-1024.f, s, f16f(sb >> 16));
+    const float s = f16f(sb & 0xffffu), cf = fmaf(128.f, s, f16f(sb >> 16));
     f32x16 pr;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const u4v bw = {L.q8(cd[gl][kk][0], 0), L.q8(cd[gl][kk][0], 1), L.q8(cd[gl][kk][1], 0),
-                      L.q8(cd[gl][kk][1], 1)};
+      const u4v bw = {center8(L.q8(cd[gl][kk][0], 0)), center8(L.q8(cd[gl][kk][0], 1)),
+                      center8(L.q8(cd[gl][kk][1], 0)), center8(L.q8(cd[gl][kk][1], 1))};
       const f16x8 bf = __builtin_bit_cast(f16x8, bw);
       const int seg = (2 * kk + hi) ^ ((m >> 1) & 7);
       const f16x8 af = *reinterpret_cast<const f16x8*>(&xa[buf][m * 64 + seg * 8]);
@@ -1079,7 +1093,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
         pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, pr, 0, 0, 0);
       }
     }
-    // fold: logit += s * P + (b - 1024 s) * sum(x) for each (token, expert)
+    // fold: logit += s * P + (b + 128 s) * sum(x) for each (token, expert)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const float4 xv = *reinterpret_cast<const float4*>(&xsum[buf][32 * (wave & 1) + 8 * j4 + 4 * hi]);

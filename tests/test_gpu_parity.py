@@ -30,8 +30,12 @@ def _layer(li, dev, max_tokens, mfma_min_rows=None, wide_min_rows=None):
 
 
 def test_dequant_bit_exact(torch_dev):
-    """GPU decoding of 4-bit and 8-bit tiles equals the oracle's exactly (s*q+b
-    is exact in fp32 for these data)."""
+    """The record decoding (tile order, nibble order, scale/bias placement) as
+    the library's debug kernel reads it equals the oracle's exactly (s*q+b is
+    exact in fp32 for these data).  This pins the storage format on the GPU
+    side; the hot kernels' arithmetic (the streaming path's folded exponent
+    trick, the matrix-core path's fp16 weights) is checked by the layer parity
+    tests against the output tolerances, not here."""
     import torch
     from quantized_routed_expert_bit_amd import debug_dequant
     P.log("dequant: record gate section + router, config-1 shapes")
@@ -59,13 +63,13 @@ def test_router_logits(torch_dev, cfg):
     ref = ol.logits(oracle.bf16_bits_to_f64(xb))
     err = np.abs(lg - ref).max()
     P.log(f"router cfg{cfg}: max |logit err| = {err:.3e}")
-    assert err < 2e-5
+    assert err < 4e-6
     # fp32 input takes the hi/lo split path
     x32 = (np.random.default_rng(1).standard_normal((T, wl.shape.hidden))).astype(np.float32)
     lg = m.router_logits(torch.from_numpy(x32).to(torch_dev)).cpu().numpy()
     err = np.abs(lg - ol.logits(x32.astype(np.float64))).max()
     P.log(f"router cfg{cfg} fp32 input: max |logit err| = {err:.3e}")
-    assert err < 2e-5
+    assert err < 4e-6
 
 
 @pytest.mark.parametrize("T", [128, 300])
@@ -80,7 +84,7 @@ def test_router_logits_matrix_core(torch_dev, T):
     lg = m.router_logits(P.bf16_tensor(xb, torch_dev)).cpu().numpy()
     err = np.abs(lg - ol.logits(oracle.bf16_bits_to_f64(xb))).max()
     P.log(f"router matrix-core T={T}: max |logit err| = {err:.3e}")
-    assert err < 2e-5
+    assert err < 4e-6
 
 
 @pytest.mark.parametrize("cfg", [0, 1])
