@@ -131,7 +131,9 @@ typedef struct moe_weights {
     const void *bank;            /* E expert records */
     uint64_t    record_stride;   /* bytes between records, multiple of 4096 */
     const void *shared_record;   /* shared-expert record, NULL iff no MOE_F_SHARED */
-    void       *workspace;       /* >= moe_workspace_bytes(cfg) bytes, 256-aligned */
+    void       *workspace;       /* >= moe_workspace_bytes(cfg) bytes, 256-aligned; or
+                                    NULL with workspace_bytes 0: the context then runs
+                                    moe_forward_noalloc only */
     uint64_t    workspace_bytes;
 } moe_weights;
 
@@ -180,6 +182,28 @@ int moe_set_weights(moe_ctx *ctx, const moe_weights *w, void *stream);
 int moe_forward(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
                 float *y, const float *residual, int32_t *ids_out, float *p_out,
                 moe_ctx *lookahead_next, void *stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The layer of moe_forward, computed by the same kernels (so
+ * bitwise the same y, ids and p), but its workspace is the library's static
+ * scratch array of MOE_NOALLOC_SCRATCH_BYTES on the context's GPU (each GPU
+ * the library runs on holds one until the process ends) instead of the bound
+ * workspace; the call allocates nothing.  Every call on a GPU shares that
+ * GPU's array, which keeps the last call's contents: each call clears what
+ * must start at zero itself, and calls that overlap on one GPU (on two
+ * streams or from two threads, whatever their contexts) race.  There is no
+ * lookahead argument (a prediction lives in the next layer's own workspace).
+ * A context bound with workspace NULL and workspace_bytes 0 runs only this
+ * call (moe_forward and moe_router_logits give MOE_ESTATE) and cannot be
+ * another forward's lookahead context.  Errors: as moe_forward, and
+ * MOE_ENOMEM when a forward of n_tokens tokens needs more than
+ * MOE_NOALLOC_SCRATCH_BYTES (moe_workspace_bytes of the config with
+ * max_tokens = n_tokens). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int moe_forward_noalloc(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
+                        float *y, const float *residual, int32_t *ids_out, float *p_out,
+                        void *stream);
 
 /* Router step only: logits fp32 [T, E] (including router_bias), of the
  * normalized rows when the context has MOE_F_RMSNORM.  Same argument rules as

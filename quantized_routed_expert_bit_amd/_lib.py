@@ -13,9 +13,11 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EBADRECORD, MOE_ESTATE, MO
 MOE_BF16, MOE_F32 = 1, 2
 MOE_F_SHARED = 1
 MOE_F_RMSNORM = 2
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every function include/moe.h declares
 EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
+            "moe_forward_noalloc",
             "moe_router_logits", "moe_set_path_rows", "moe_close", "moe_strerror",
             "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
             "moe_profile_start", "moe_profile_read")
@@ -59,6 +61,9 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_void_p, c_void_p]
     lib.moe_forward.restype = c_int
+    lib.moe_forward_noalloc.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p]
+    lib.moe_forward_noalloc.restype = c_int
     lib.moe_router_logits.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]
     lib.moe_router_logits.restype = c_int
     lib.moe_set_path_rows.argtypes = [c_void_p, c_int32, c_int32]

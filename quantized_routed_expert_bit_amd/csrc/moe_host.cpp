@@ -27,6 +27,8 @@ struct moe_ctx {
   // caller's stream with two events (created at open, default priority)
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  // this device's copy of the library's static scratch (moe_forward_noalloc)
+  uint8_t* scratch = nullptr;
 };
 
 static void prof_clear(moe_ctx* c) {
@@ -181,6 +183,10 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
     return MOE_EHIP;
   }
   d.n_cu = n_cu;
+  if (noalloc_scratch(cfg->device, &c->scratch) != hipSuccess) {
+    moe_close(c);
+    return MOE_EHIP;
+  }
   *out = c;
   return MOE_OK;
 }
@@ -191,8 +197,10 @@ int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
   const moe_config& c = ctx->cfg;
   if (!w || w->struct_size != sizeof(moe_weights))
     return fail(ctx, MOE_EINVAL, "moe_weights is NULL or has the wrong struct_size");
-  if (!w->router || !w->bank || !w->workspace)
-    return fail(ctx, MOE_EINVAL, "router, bank and workspace must be non-NULL");
+  if (!w->router || !w->bank)
+    return fail(ctx, MOE_EINVAL, "router and bank must be non-NULL");
+  if (!w->workspace && w->workspace_bytes != 0)
+    return fail(ctx, MOE_EINVAL, "workspace is NULL but workspace_bytes is not 0");
   if (((uintptr_t)w->workspace & 255) || ((uintptr_t)w->router & 15) || ((uintptr_t)w->bank & 255))
     return fail(ctx, MOE_EINVAL, "workspace and bank must be 256-byte aligned, router 16-byte");
   if (ctx->d.has_shared != (w->shared_record != nullptr))
@@ -201,7 +209,7 @@ int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
     return fail(ctx, MOE_EINVAL, "shared_record must be 256-byte aligned");
   if (w->record_stride == 0 || w->record_stride % 4096)
     return fail(ctx, MOE_EINVAL, "record_stride must be a positive multiple of 4096");
-  if (w->workspace_bytes < ctx->d.L.total)
+  if (w->workspace && w->workspace_bytes < ctx->d.L.total)
     return fail(ctx, MOE_ENOMEM, "workspace has %llu bytes, needs %llu",
                 (unsigned long long)w->workspace_bytes, (unsigned long long)ctx->d.L.total);
   hipError_t e = hipSetDevice(c.device);
@@ -234,8 +242,10 @@ int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
   d.stride = w->record_stride;
   d.shared = static_cast<const uint8_t*>(w->shared_record);
   d.ws = static_cast<uint8_t*>(w->workspace);
-  e = launch_ws_init(d, s);
-  if (e != hipSuccess) return hip_fail(ctx, e, "workspace init");
+  if (d.ws) {
+    e = launch_ws_init(d, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "workspace init");
+  }
   ctx->has_weights = true;
   ctx->err.clear();
   return MOE_OK;
@@ -252,21 +262,11 @@ static int check_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n
   return MOE_OK;
 }
 
-int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
-                const float* residual, int32_t* ids_out, float* p_out, moe_ctx* next,
-                void* stream) {
-  int rc = check_forward(ctx, x, x_dtype, n_tokens, y);
-  if (rc != MOE_OK) return rc;
-  if (next) {
-    if (next == ctx) return fail(ctx, MOE_EINVAL, "lookahead context is this context");
-    if (!next->has_weights) return fail(ctx, MOE_ESTATE, "lookahead context has no weights");
-    if (next->cfg.hidden != ctx->cfg.hidden || next->cfg.max_tokens < n_tokens ||
-        next->d.rmsnorm != ctx->d.rmsnorm)
-      return fail(ctx, MOE_EINVAL, "lookahead context does not match this layer");
-  }
-  if (n_tokens == 0) return MOE_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const LayerDev& d = ctx->d;
+// One forward on the workspace d.ws points at (the bound one, or the static
+// scratch for moe_forward_noalloc).  Arguments are already checked.
+static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t x_dtype,
+                        int32_t n_tokens, float* y, const float* residual, int32_t* ids_out,
+                        float* p_out, moe_ctx* next, hipStream_t s) {
   // Timing events are recorded only on a stream that is not being captured
   // into a graph (inside a capture an event record would only be a dependency).
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -338,6 +338,50 @@ int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, 
   return MOE_OK;
 }
 
+int moe_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
+                const float* residual, int32_t* ids_out, float* p_out, moe_ctx* next,
+                void* stream) {
+  int rc = check_forward(ctx, x, x_dtype, n_tokens, y);
+  if (rc != MOE_OK) return rc;
+  if (!ctx->d.ws)
+    return fail(ctx, MOE_ESTATE, "no workspace bound (this context runs moe_forward_noalloc only)");
+  if (next) {
+    if (next == ctx) return fail(ctx, MOE_EINVAL, "lookahead context is this context");
+    if (!next->has_weights) return fail(ctx, MOE_ESTATE, "lookahead context has no weights");
+    if (!next->d.ws) return fail(ctx, MOE_EINVAL, "lookahead context has no workspace bound");
+    if (next->cfg.hidden != ctx->cfg.hidden || next->cfg.max_tokens < n_tokens ||
+        next->d.rmsnorm != ctx->d.rmsnorm)
+      return fail(ctx, MOE_EINVAL, "lookahead context does not match this layer");
+  }
+  if (n_tokens == 0) return MOE_OK;
+  return forward_impl(ctx, ctx->d, x, x_dtype, n_tokens, y, residual, ids_out, p_out, next,
+                      static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_noalloc(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
+                        const float* residual, int32_t* ids_out, float* p_out, void* stream) {
+  int rc = check_forward(ctx, x, x_dtype, n_tokens, y);
+  if (rc != MOE_OK) return rc;
+  if (n_tokens == 0) return MOE_OK;
+  // The workspace layout for exactly this batch, placed in the static scratch.
+  LayerDev d = ctx->d;
+  moe_config c = ctx->cfg;
+  c.max_tokens = n_tokens;
+  d.L = ws_layout(c);
+  if (d.L.total > kNoallocScratchBytes)
+    return fail(ctx, MOE_ENOMEM,
+                "a forward of %d tokens needs %llu bytes of scratch; the static scratch holds %llu",
+                n_tokens, (unsigned long long)d.L.total, (unsigned long long)kNoallocScratchBytes);
+  if (!ctx->scratch) return fail(ctx, MOE_ESTATE, "no static scratch on this device");
+  d.ws = ctx->scratch;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Another call may have left its state in the shared array: clear the
+  // counters (no lookahead prediction pending) with a fill kernel.
+  hipError_t e = launch_ws_init(d, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "scratch init");
+  return forward_impl(ctx, d, x, x_dtype, n_tokens, y, residual, ids_out, p_out, nullptr, s);
+}
+
 int moe_profile_start(moe_ctx* ctx, int32_t max_calls) {
   if (!ctx || max_calls < 1 || max_calls > 100000) return MOE_EINVAL;
   prof_clear(ctx);
@@ -389,6 +433,7 @@ int moe_router_logits(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_to
                       float* logits, void* stream) {
   int rc = check_forward(ctx, x, x_dtype, n_tokens, logits);
   if (rc != MOE_OK) return rc;
+  if (!ctx->d.ws) return fail(ctx, MOE_ESTATE, "no workspace bound");
   if (n_tokens == 0) return MOE_OK;
   const LayerDev& d = ctx->d;
   hipStream_t s = static_cast<hipStream_t>(stream);

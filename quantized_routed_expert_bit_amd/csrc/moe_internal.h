@@ -28,6 +28,8 @@ constexpr int kRouterGPW = 8;
 constexpr int kRouterTokMax = 16;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
+constexpr int kMaxDevices = 64;
+constexpr size_t kNoallocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
 
 // Streaming (GEMV) expert path: up to kGemvTok tokens per pass over the weights.
 constexpr int kGemvTok = 16;
@@ -106,5 +108,8 @@ hipError_t launch_ws_init(const LayerDev& d, hipStream_t s);
 hipError_t launch_rmsnorm(const LayerDev& d, const void* x, int x_f32, int T, hipStream_t s);
 hipError_t launch_debug_dequant(const void* tiles, int bits, int rows, int cols, float* out,
                                 hipStream_t s);
+// Device address of the library's static scratch array (kNoallocScratchBytes)
+// on `device`, which must be the current device; looked up once per device.
+hipError_t noalloc_scratch(int device, uint8_t** out);
 
 }  // namespace qreb

@@ -34,6 +34,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace qreb {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -2532,6 +2534,34 @@ hipError_t launch_ws_init(const LayerDev& d, hipStream_t s) {
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, base,
                      (int)n, 0);
   return hipGetLastError();
+}
+
+// ------------------------------------------------ allocation-free scratch ----
+// The device memory of moe_forward_noalloc: one file-scope array, of which
+// every GPU the library runs on holds its own copy, at its own address, until
+// the process ends.  In host code the array's name is only a stand-in for the
+// symbol, never an address: the runtime is asked for each device's address
+// once, with that device current, and that pointer is what the kernels get.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+hipError_t noalloc_scratch(int device, uint8_t** out) {
+  static std::mutex mu;
+  static uint8_t* ptr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device) return hipErrorInvalidDevice;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[device] = static_cast<uint8_t*>(p);
+  }
+  *out = ptr[device];
+  return hipSuccess;
 }
 
 hipError_t launch_debug_dequant(const void* tiles, int bits, int rows, int cols, float* out,

@@ -49,12 +49,14 @@ class MoELayer:
             raise MoEError(rc, f"{what}: {msg}")
 
     def set_weights(self, router, bank, record_stride, shared=None, router_bias=None,
-                    workspace=None):
-        if workspace is None:
+                    workspace=None, no_workspace=False):
+        """Bind the weights.  `workspace` defaults to a new device tensor;
+        with no_workspace=True none is bound and only forward_noalloc runs."""
+        if workspace is None and not no_workspace:
             workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
         w = L.MoeWeights(ctypes.sizeof(L.MoeWeights), _ptr(router), _ptr(router_bias),
                          _ptr(bank), record_stride, _ptr(shared), _ptr(workspace),
-                         workspace.numel())
+                         0 if workspace is None else workspace.numel())
         self._keep = (router, bank, shared, router_bias, workspace)
         self._check(self.lib.moe_set_weights(self.ctx, ctypes.byref(w), _stream()),
                     "moe_set_weights")
@@ -85,6 +87,23 @@ class MoELayer:
         return (y, ids, p) if return_selection else y
 
     __call__ = forward
+
+    def forward_noalloc(self, x, return_selection=False, y=None, residual=None):
+        """forward() on the library's static scratch (moe_forward_noalloc):
+        the library allocates nothing; y, ids and p are the caller's (created
+        here only when not given)."""
+        T = x.shape[0]
+        x = x.contiguous()
+        if y is None:
+            y = torch.empty((T, self.hidden), dtype=torch.float32, device=self.device)
+        ids = p = None
+        if return_selection:
+            ids = torch.empty((T, self.top_k), dtype=torch.int32, device=self.device)
+            p = torch.empty((T, self.top_k), dtype=torch.float32, device=self.device)
+        self._check(self.lib.moe_forward_noalloc(self.ctx, _ptr(x), self._dtype(x), T, _ptr(y),
+                                                 _ptr(residual), _ptr(ids), _ptr(p), _stream()),
+                    "moe_forward_noalloc")
+        return (y, ids, p) if return_selection else y
 
     def router_logits(self, x):
         T = x.shape[0]
