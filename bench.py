@@ -1,19 +1,27 @@
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
-Default workload: the decode layer (hidden 2816, 128 experts, top-8,
-intermediate 704, shared expert 2112) at 16 tokens per forward.  A step is one
-moe_forward: router + top-k + bucketing, gate/up, down, combine.  Steps rotate
-over several copies of the layer (distinct weights, like consecutive layers of
-a model) so the active weights come from HBM, not from the 256 MB last-level
-cache.  The timed region is one HIP graph holding K forwards; HIP events that
-the library records around each kernel inside that graph give per-kernel
-durations for the roofline line.
+Headline workload: the skewed 8-layer stack at the large-expert shape (hidden
+7168, 512 experts, top-16, intermediate 2048, shared expert 2048; 101.5 GB of
+expert records, generated on the device), 256 tokens, router logits biased by
+the log of a Zipf(1.1) prior, fp32 residual stream, each layer's router also
+run on the current input for the next layer (lookahead on).  A step is one
+pass of the batch through all eight layers (8 moe_forward calls: router, top-k
+and bucketing, gate/up, down, combine with the residual add).  The value is
+tokens/s through the stack.
 
-Prints ONE JSON line (rank 0, one GPU).
+The timed region is one HIP-graph replay of K steps, bracketed by device
+synchronisation and timed with HIP events on the stream it runs on.  Per-kernel
+durations come from the library's own event pairs around each kernel in an
+eager pass over the same steps.  The other workloads (the large decode layer at
+1, 8 and 64 tokens, the decode layer at 1, 4 and 16 tokens, the 2048-token
+prefill) are reported as extra entries, each with its fraction of the roofline.
+
+Prints ONE JSON line (one GPU).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
 METRIC = "MoE layer tokens/s; decode HBM GB/s and prefill TFLOP/s as % of MI355X peak"
+KERNELS = ("router", "gemv_up", "gemv_down", "mfma_up", "mfma_down", "combine")
 
 
 def log(*a):
@@ -38,179 +47,461 @@ def record_bytes(h, i):
     return 3 * h * i * 9 // 16
 
 
-def measured_traffic():
-    """HBM bytes per launch of the streaming gate/up kernel at this workload,
-    from the committed rocprofv3 FETCH_SIZE + WRITE_SIZE passes (calibrated
-    against a plain copy); None once the kernel sources differ from the ones
-    the counters were taken on."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "gemv_up_decode_T16_hbm_traffic.md")
+def layer_bytes(sh, T, distinct, x_bytes=2, residual=False):
+    """Algorithmic bytes of one forward: the distinct routed records, the
+    shared record, the 8-bit router (8.5 bits per weight), x, y (fp32), ids and
+    p, and the residual read when the forward adds one."""
+    b = distinct * record_bytes(sh.hidden, sh.inter) + sh.n_experts * sh.hidden * 17 / 16
+    if sh.has_shared:
+        b += record_bytes(sh.hidden, sh.shared_inter)
+    b += T * sh.hidden * (x_bytes + 4 + (4 if residual else 0)) + T * sh.top_k * 8
+    return b
+
+
+def layer_flops(sh, T):
+    return T * 2 * (sh.top_k * 3 * sh.hidden * sh.inter + 3 * sh.hidden * sh.shared_inter
+                    + sh.n_experts * sh.hidden)
+
+
+def kernel_work(cnt, sh, T, rmin, rwide):
+    """Algorithmic bytes and FLOPs per launch of each expert kernel, from the
+    rows per expert of one forward.  Experts below wide_min_rows rows (and the
+    shared expert below it) run in the streaming launches (gate/up, down),
+    which also carry the 32-row matrix-core tiles; the others in the 128-row
+    matrix-core launches.  Bytes: each record section once (4.5 bits per
+    weight); FLOPs: 2 per weight per row."""
+    gu, dn = 2 * sh.hidden * sh.inter, sh.hidden * sh.inter
+    w = {k: [0.0, 0.0] for k in ("gemv_up", "gemv_down", "mfma_up", "mfma_down")}
+    for c in cnt[cnt > 0]:
+        up, down = ("mfma_up", "mfma_down") if c >= rwide else ("gemv_up", "gemv_down")
+        w[up][0] += gu * 9 / 16
+        w[up][1] += 2 * c * gu
+        w[down][0] += dn * 9 / 16
+        w[down][1] += 2 * c * dn
+    if sh.has_shared:
+        gus, dns = 2 * sh.hidden * sh.shared_inter, sh.hidden * sh.shared_inter
+        up, down = ("mfma_up", "mfma_down") if T >= rwide else ("gemv_up", "gemv_down")
+        w[up][0] += gus * 9 / 16
+        w[up][1] += 2 * T * gus
+        w[down][0] += dns * 9 / 16
+        w[down][1] += 2 * T * dns
+    return w
+
+
+def roofline(kernel, bytes_, flops, us):
+    """The kernel's bound is the larger of its two ideal times (bytes at the
+    HBM peak, FLOPs at the dense fp16 matrix-core peak)."""
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_F16_PEAK_TFS * 1e12)
+    if t_mfma > t_hbm:
+        ach = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFS, 4), "kernel": kernel,
+                "flops_per_launch": int(flops), "bytes_per_launch": int(bytes_),
+                "avg_launch_us": round(us, 3)}
+    ach = bytes_ / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": kernel, "bytes_per_launch": int(bytes_),
+            "flops_per_launch": int(flops), "avg_launch_us": round(us, 3)}
+
+
+def source_sha256():
+    h = hashlib.sha256()
+    for f in ("moe_kernels.hip", "moe_internal.h"):
+        with open(os.path.join(ROOT, "quantized_routed_expert_bit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of a kernel on a workload, from the committed
+    rocprofv3 FETCH_SIZE + WRITE_SIZE passes (calibrated against a plain copy);
+    None once the kernel sources differ from the ones the counters were taken
+    on."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                       if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
-        h = hashlib.sha256()
-        for f in ("moe_kernels.hip", "moe_internal.h"):
-            with open(os.path.join(ROOT, "quantized_routed_expert_bit_amd", "csrc", f), "rb") as fh:
-                h.update(fh.read())
-        if h.hexdigest() != fields["source_sha256"].strip():
+        if source_sha256() != fields["source_sha256"].strip():
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
 
-def build_layers(wl_index, n_copies, max_tokens, dev):
-    import synth
-    from quantized_routed_expert_bit_amd import MoELayer
-    from tests.parity import upload_layer
-    wl = synth.WORKLOADS[wl_index]
-    sh = wl.shape
-    layers = []
-    for l in range(n_copies):
-        li = synth.LayerInputs(0, wl.index, l, sh, wl.bias)
-        w = upload_layer(li, dev)
-        m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, max_tokens)
-        m.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
-        m._w, m._li = w, li
-        layers.append(m)
-        log(f"  layer copy {l} uploaded")
-    return wl, layers
-
-
-def run_case(layers, sh, T, steps, warmup, tag=0):
-    """Warm up eagerly, capture `steps` forwards in one graph, replay it once
-    (the timed region).  Returns timings and routing stats."""
+def timed_graph(step, steps):
+    """Capture `steps` calls of step(i) in one HIP graph, replay it once
+    untimed (upload), then time one replay with HIP events on the stream it
+    runs on, between two device synchronisations.  Returns seconds."""
     import torch
-    import synth
-    from tests.parity import bf16_tensor
-    dev = torch.device("cuda", 0)
-    n = len(layers)
-    xs = [bf16_tensor(synth.make_hidden(0, layers[l]._li.cfg, T, sh.hidden, tag=100 + l + tag), dev)
-          for l in range(n)]
-    ys = [torch.empty((T, sh.hidden), dtype=torch.float32, device=dev) for _ in range(n)]
-    # routing per copy (deterministic): distinct experts and rows
-    distinct, streamed = [], []
-    rwide = layers[0].wide_min_rows
-    for l in range(n):
-        _, ids, _ = layers[l].forward(xs[l], return_selection=True)
-        cnt = np.bincount(ids.cpu().numpy().reshape(-1), minlength=sh.n_experts)
-        distinct.append(int((cnt > 0).sum()))
-        # experts in the streaming launches: streamed, or in 32-row matrix-core tiles
-        streamed.append(int(((cnt > 0) & (cnt < rwide)).sum()))
-    for i in range(warmup):
-        layers[i % n].forward(xs[i % n], y=ys[i % n])
-    torch.cuda.synchronize()
-    # timed region: one graph replay of `steps` forwards
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for i in range(steps):
-            layers[i % n].forward(xs[i % n], y=ys[i % n])
-    g.replay()                       # untimed replay (graph upload)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+            step(i)
     g.replay()
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    del g
-    # kernel timing pass: the same forwards eagerly, with the library's event
-    # pairs around each kernel; a spin kernel holds the GPU while the host
-    # queues them, so no kernel waits on the host.
-    kp = min(steps, 120)
-    per_copy = [(kp + n - 1 - l) // n for l in range(n)]
-    for l in range(n):
-        layers[l].profile_start(per_copy[l])
-    t_first = torch.cuda.Event(enable_timing=True)
-    t_last = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(2.4e9 * 0.05))          # ~50 ms of GPU spin
-    t_first.record()
-    for i in range(kp):
-        layers[i % n].forward(xs[i % n], y=ys[i % n])
-    t_last.record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    eager_ms = t_first.elapsed_time(t_last) / kp
-    prof = [layers[l].profile_read() for l in range(n)]
-    kern = {}
-    for name in prof[0][0]:
-        tot = sum(p[0][name] * p[1] for p in prof)
-        cnt = sum(p[1] for p in prof if p[0][name] > 0)
-        kern[name] = tot / cnt if cnt else 0.0
-    d_avg = float(np.average(distinct, weights=per_copy))
-    s_avg = float(np.average(streamed, weights=per_copy))
-    return dict(elapsed=el, ms_per_step=el * 1e3 / steps, tok_s=T * steps / el, kern_ms=kern,
-                distinct=d_avg, streamed=s_avg, per_copy=per_copy, distinct_per_copy=distinct,
-                eager_ms_per_step=eager_ms)
+    host = time.perf_counter() - t0
+    del g
+    return e0.elapsed_time(e1) * 1e-3, host
 
 
-def path_flops(ids, sh, T, rmin, rwide):
-    """FLOPs of the expert FFNs on each path, from the actual routing."""
-    cnt = np.bincount(ids.reshape(-1), minlength=sh.n_experts)
-    per_row = 2 * 3 * sh.hidden * sh.inter
-    out = {"stream": 0.0, "narrow": 0.0, "wide": 0.0}
-    for c in cnt[cnt > 0]:
-        out["stream" if c < rmin else ("narrow" if c < rwide else "wide")] += c * per_row
-    if sh.has_shared:
-        out["stream" if T < rmin else ("narrow" if T < rwide else "wide")] += \
-            T * 2 * 3 * sh.hidden * sh.shared_inter
-    return out, cnt
-
-
-def run_prefill(args, dev):
-    """The prefill workload: 16 chunks of 128 tokens (2048) per forward, router
-    logit bias N(0, 0.5); bound by the matrix cores."""
+def profiled(layers, step, n_steps):
+    """Average ms per launch of each kernel slot over n_steps eager steps, from
+    the library's event pairs (a spin kernel first holds the GPU while the host
+    queues the steps).  Returns ({kernel: ms}, {kernel: launches per step})."""
     import torch
-    import synth
-    from tests.parity import bf16_tensor
-    wl, layers = build_layers(2, 2, 2048, dev)
-    sh = wl.shape
-    T = wl.batches[0]
-    r = run_case(layers, sh, T, max(4, args.steps // 20), 2, tag=50)
-    _, ids, _ = layers[0].forward(bf16_tensor(synth.make_hidden(0, 2, T, sh.hidden, tag=150), dev),
-                                  return_selection=True)
-    fl, cnt = path_flops(ids.cpu().numpy(), sh, T, layers[0].mfma_min_rows, layers[0].wide_min_rows)
-    k = r["kern_ms"]
-    wide_ms = k["mfma_up"] + k["mfma_down"]
-    total_flops = T * 2 * (sh.top_k * 3 * sh.hidden * sh.inter + 3 * sh.hidden * sh.shared_inter
-                           + sh.n_experts * sh.hidden)
-    res = {"tokens_s": round(r["tok_s"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2),
-           "layer_TFLOP_s": round(total_flops / (r["ms_per_step"] * 1e-3) / 1e12, 1),
-           "layer_frac_mfma_peak": round(total_flops / (r["ms_per_step"] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFS, 4),
-           "wide_mfma_TFLOP_s": round(fl["wide"] / (wide_ms * 1e-3) / 1e12, 1) if wide_ms else None,
-           "wide_frac_mfma_peak": round(fl["wide"] / (wide_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFS, 4) if wide_ms else None,
-           "path_gflop": {kk: round(v / 1e9, 2) for kk, v in fl.items()},
-           "rows_per_expert": {"min": int(cnt.min()), "median": float(np.median(cnt)), "max": int(cnt.max())},
-           "kernel_us": {kk: round(v * 1e3, 3) for kk, v in k.items()},
-           "distinct_experts": r["distinct"]}
-    log(f"prefill: {res}")
     for m in layers:
-        m.close()
-    return res
+        m.profile_start(n_steps * 4)
+    torch.cuda._sleep(int(2.4e9 * 0.05))
+    for i in range(n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    tot = {k: 0.0 for k in KERNELS}
+    n = {k: 0 for k in KERNELS}
+    for m in layers:
+        avg, calls = m.profile_read()
+        for k in KERNELS:
+            if avg[k] > 0:
+                tot[k] += avg[k] * calls
+                n[k] += calls
+    return ({k: tot[k] / n[k] if n[k] else 0.0 for k in KERNELS},
+            {k: n[k] / n_steps for k in KERNELS})
 
 
-def cpu_baseline(layer0, sh, T):
-    """The oracle (fp64 NumPy) on one forward of the same workload."""
-    import oracle
-    import synth
-    from tests.parity import oracle_layer
+def host_info():
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        info["affinity_cpus"] = os.cpu_count()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info["blas"] = [{k: i.get(k) for k in ("internal_api", "version", "num_threads",
+                                                 "threading_layer")}
+                        for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:
-        threads = os.cpu_count()
-    ol = oracle_layer(layer0._li, cache=True)
-    xb = synth.make_hidden(0, layer0._li.cfg, T, sh.hidden, tag=100)
-    x64 = oracle.bf16_bits_to_f64(xb)
-    ids = ol.forward(x64[:1])["ids"]          # warm: regenerate the records the batch uses
-    for e in np.unique(oracle.select_topk(ol.logits(x64), sh.top_k)[0]):
-        ol.get_record(int(e))
-    t0 = time.perf_counter()
-    ol.forward(x64)
-    el = time.perf_counter() - t0
-    return dict(value=round(T / el, 3), unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"one oracle forward of the {T}-token batch on layer copy 0 (fp64 dequant "
-                       f"of every active record + router, top-k, FFNs, combine; record "
-                       f"generation excluded): {el:.2f} s")
+        info["blas"] = None
+    return info
+
+
+# ------------------------------------------------------------- workloads ----
+
+def make_large_layer(dev, cfg, layer, max_tokens, rmsnorm=False):
+    """One layer at the large-expert shape, its bank generated on the device."""
+    import torch
+    import synth
+    from quantized_routed_expert_bit_amd import MoELayer
+    wl = synth.WORKLOADS[cfg]
+    sh = wl.shape
+    bank, stride = synth.gpu_bank(0, cfg, layer, sh.hidden, sh.inter, sh.n_experts, dev)
+    shared, _ = synth.gpu_bank(0, cfg, layer, sh.hidden, sh.shared_inter, 1, dev, shared=True)
+    router = synth.make_router(0, cfg, layer, sh.hidden, sh.n_experts)
+    bias = synth.make_router_bias(0, cfg, layer, sh.n_experts, wl.bias)
+    m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, max_tokens,
+                 rmsnorm=rmsnorm)
+    m.set_weights(torch.from_numpy(router).to(dev), bank, stride, shared,
+                  None if bias is None else torch.from_numpy(bias).to(dev))
+    m._host = dict(router=router, bias=bias, stride=stride)
+    return m
+
+
+def run_stack(args, dev):
+    """The 8-layer stack, 256 tokens, lookahead on (the headline)."""
+    import torch
+    import synth
+    wl = synth.WORKLOADS[4]
+    sh = wl.shape
+    T = wl.batches[0]
+    layers = []
+    for l in range(wl.layers):
+        layers.append(make_large_layer(dev, 4, l, T, rmsnorm=True))
+        log(f"  stack layer {l} generated")
+    x32 = synth.bf16_tensor(synth.make_hidden(0, 4, T, sh.hidden), dev).float()
+    r = torch.empty_like(x32)
+    L = len(layers)
+
+    def step(_i):
+        # r_1 = x + MoE_0(x); r_{l+1} = r_l + MoE_l(r_l) in place; each layer
+        # also runs the next layer's router on its input (lookahead)
+        for l, m in enumerate(layers):
+            nxt = layers[l + 1] if l + 1 < L else None
+            src = x32 if l == 0 else r
+            m.forward(src, y=r, residual=src, lookahead=nxt)
+
+    # routing of each layer on the stack's own trajectory
+    counts = []
+    rr = x32.clone()
+    for l, m in enumerate(layers):
+        out = torch.empty_like(rr)
+        _, ids, _ = m.forward(rr, return_selection=True, y=out, residual=rr)
+        counts.append(np.bincount(ids.cpu().numpy().reshape(-1), minlength=sh.n_experts))
+        rr = out
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    el, host = timed_graph(step, args.steps)
+    us_step = el * 1e6 / args.steps
+    kern, per_step = profiled(layers, step, min(args.steps, 10))
+    rmin, rwide = layers[0].mfma_min_rows, layers[0].wide_min_rows
+    work = [kernel_work(c, sh, T, rmin, rwide) for c in counts]
+    distinct = [int((c > 0).sum()) for c in counts]
+    alg = sum(layer_bytes(sh, T, d, x_bytes=4, residual=True) for d in distinct)
+    flops = L * layer_flops(sh, T)
+    # the dominant kernel: the largest share of the step
+    share = {k: kern[k] * per_step[k] for k in KERNELS}
+    dom = max(("gemv_up", "gemv_down", "mfma_up", "mfma_down"), key=lambda k: share[k])
+    b = float(np.mean([w[dom][0] for w in work]))
+    f = float(np.mean([w[dom][1] for w in work]))
+    rl = roofline(dom, b, f, kern[dom] * 1e3)
+    rl["traffic"] = measured_traffic(f"{dom}_stack_hbm_traffic.md")
+    res = dict(
+        tokens_s=T * args.steps / el, us_per_step=us_step, host_us_per_step=host * 1e6 / args.steps,
+        roofline=rl,
+        stack_hbm={"alg_bytes_per_step": int(alg), "GB_s": round(alg / (el / args.steps) / 1e9, 1),
+                   "frac": round(alg / (el / args.steps) / 1e9 / HBM_PEAK_GBS, 4)},
+        stack_mfma={"flops_per_step": int(flops),
+                    "TFLOP_s": round(flops / (el / args.steps) / 1e12, 1),
+                    "frac": round(flops / (el / args.steps) / 1e12 / MFMA_F16_PEAK_TFS, 4)},
+        kernel_us_per_launch={k: round(v * 1e3, 3) for k, v in kern.items()},
+        kernel_us_per_step={k: round(share[k] * 1e3, 2) for k in KERNELS},
+        distinct_experts_per_layer=distinct,
+        rows_top_expert_per_layer=[int(c.max()) for c in counts],
+        wide_experts_per_layer=[int((c >= rwide).sum()) for c in counts])
+    log(f"stack: {res}")
+    return res, layers, x32
+
+
+def cpu_baseline_stack(layers, x32, n_sample=8):
+    """The oracle (fp64 NumPy, as it stands) on a bounded sample of the stack
+    workload: layer 0 with its 256-token batch.  Router logits, top-k and
+    softmax for all tokens and the shared expert on all tokens are timed in
+    full; the routed-expert loop (dequantize a record, run its rows) is timed
+    on the first n_sample of the layer's active experts, in the oracle's own
+    order, and scaled to all of them; the layer time x 8 layers gives
+    tokens/s through the stack.  Timed once with BLAS limited to one thread
+    and once with all affinity cores.  Reading the records back from the GPU
+    is excluded."""
+    import oracle
+    import synth
+    m = layers[0]
+    sh = synth.WORKLOADS[4].shape
+    T = x32.shape[0]
+    bank, stride, shared = m._keep[1], m._host["stride"], m._keep[2]
+    x = oracle.rms_normalize(x32.cpu().numpy().astype(np.float64))
+    ol = oracle.OracleLayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter,
+                            m._host["router"], m._host["bias"], None, shared.cpu().numpy())
+    ids0, _ = oracle.select_topk(ol.logits(x), sh.top_k)
+    uniq = np.unique(ids0)
+    recs = {int(e): bank[int(e) * stride:(int(e) + 1) * stride].cpu().numpy() for e in uniq[:n_sample]}
+    info = host_info()
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        threadpool_limits = None
+    out = {}
+    for label, nth in (("1_thread", 1), ("all_cores", info["affinity_cpus"])):
+        ctx = threadpool_limits(limits=nth, user_api="blas") if threadpool_limits else None
+        try:
+            t0 = time.perf_counter()
+            lg = ol.logits(x)
+            ids, _ = oracle.select_topk(lg, sh.top_k)
+            oracle.softmax_selected(lg, ids)
+            t_route = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            for e in uniq[:n_sample]:
+                rows, _ = np.nonzero(ids == e)
+                oracle.expert_ffn(x[rows], *oracle.expert_matrices(recs[int(e)], sh.hidden, sh.inter))
+            t_exp = (time.perf_counter() - t0) / min(n_sample, len(uniq)) * len(uniq)
+            t0 = time.perf_counter()
+            oracle.expert_ffn(x, *oracle.expert_matrices(ol.shared_record, sh.hidden, sh.shared_inter))
+            t_sh = time.perf_counter() - t0
+        finally:
+            if ctx is not None:
+                ctx.__exit__(None, None, None)
+        t_layer = t_route + t_exp + t_sh
+        out[label] = {"tokens_s": round(T / (len(layers) * t_layer), 5), "threads": nth,
+                      "layer_s": round(t_layer, 2), "route_s": round(t_route, 3),
+                      "experts_s": round(t_exp, 2), "shared_s": round(t_sh, 2)}
+    log(f"cpu baseline: {out}")
+    return dict(value=out["all_cores"]["tokens_s"], unit="tokens/s", cores=int(info["affinity_cpus"]),
+                kind="oracle",
+                sample=(f"layer 0 of the stack, 256 tokens: router, top-k, softmax and the shared "
+                        f"expert timed in full; the routed-expert loop timed on {n_sample} of the "
+                        f"{len(uniq)} active experts and scaled; x {len(layers)} layers"),
+                one_thread=out["1_thread"], all_cores=out["all_cores"], host=info)
+
+
+def run_large(args, dev, n_inputs=4):
+    """The large decode layer (a 12.7 GB bank generated on the device) at 1, 8
+    and 64 tokens per forward.  The timed graph rotates over n_inputs token
+    batches, so successive forwards read different experts (the active set is
+    larger than the 256 MB Infinity Cache)."""
+    import torch
+    import synth
+    wl = synth.WORKLOADS[3]
+    sh = wl.shape
+    m = make_large_layer(dev, 3, 0, max(wl.batches))
+    log("  large layer generated")
+    out = {}
+    for T in wl.batches:
+        xs = [synth.bf16_tensor(synth.make_hidden(0, 3, T, sh.hidden, tag=200 + i), dev)
+              for i in range(n_inputs)]
+        y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
+        counts = []
+        for x in xs:
+            _, ids, _ = m.forward(x, return_selection=True)
+            counts.append(np.bincount(ids.cpu().numpy().reshape(-1), minlength=sh.n_experts))
+        for i in range(args.warmup):
+            m.forward(xs[i % n_inputs], y=y)
+        torch.cuda.synchronize()
+        el, _ = timed_graph(lambda i: m.forward(xs[i % n_inputs], y=y), args.steps)
+        kern, _ = profiled([m], lambda i: m.forward(xs[i % n_inputs], y=y), min(args.steps, 40))
+        us = el * 1e6 / args.steps
+        d = float(np.mean([(c > 0).sum() for c in counts]))
+        alg = layer_bytes(sh, T, d)
+        work = [kernel_work(c, sh, T, m.mfma_min_rows, m.wide_min_rows) for c in counts]
+        up_b = float(np.mean([w["gemv_up"][0] for w in work]))
+        up_f = float(np.mean([w["gemv_up"][1] for w in work]))
+        out[f"T{T}"] = {"tokens_s": round(T / (us * 1e-6), 1), "us_per_step": round(us, 2),
+                        "distinct_experts": d, "alg_bytes_per_step": int(alg),
+                        "layer_GB_s": round(alg / (us * 1e-6) / 1e9, 1),
+                        "layer_frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "gemv_up_roofline": roofline("gemv_up", up_b, up_f, kern["gemv_up"] * 1e3),
+                        "kernel_us": {k: round(v * 1e3, 3) for k, v in kern.items()}}
+        log(f"large T={T}: {out[f'T{T}']}")
+    m.close()
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_decode(args, dev, batches=(1, 4, 16), copies=6):
+    """The decode layer (hidden 2816, 128 experts, top-8, intermediate 704,
+    shared expert 2112) at 1, 4 and 16 tokens; forwards rotate over `copies`
+    layer copies (2.6 GB of weights), so each streams its experts from HBM."""
+    import torch
+    import synth
+    from quantized_routed_expert_bit_amd import MoELayer
+    wl = synth.WORKLOADS[1]
+    sh = wl.shape
+    layers = []
+    for l in range(copies):
+        li = synth.LayerInputs(0, 1, l, sh, wl.bias)
+        w = synth.upload_layer(li, dev)
+        mm = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, max(batches))
+        mm.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
+        mm._w = w
+        layers.append(mm)
+    log("  decode layer copies uploaded")
+    out = {}
+    for T in batches:
+        xs = [synth.bf16_tensor(synth.make_hidden(0, 1, T, sh.hidden, tag=100 + l + T), dev)
+              for l in range(copies)]
+        ys = [torch.empty((T, sh.hidden), dtype=torch.float32, device=dev) for _ in range(copies)]
+        counts = []
+        for l in range(copies):
+            _, ids, _ = layers[l].forward(xs[l], return_selection=True)
+            counts.append(np.bincount(ids.cpu().numpy().reshape(-1), minlength=sh.n_experts))
+        step = lambda i: layers[i % copies].forward(xs[i % copies], y=ys[i % copies])  # noqa: E731
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        el, _ = timed_graph(step, args.steps)
+        kern, _ = profiled(layers, step, min(args.steps, 120))
+        us = el * 1e6 / args.steps
+        d = float(np.mean([(c > 0).sum() for c in counts]))
+        alg = layer_bytes(sh, T, d)
+        m0 = layers[0]
+        work = [kernel_work(c, sh, T, m0.mfma_min_rows, m0.wide_min_rows) for c in counts]
+        up_b = float(np.mean([w["gemv_up"][0] for w in work]))
+        up_f = float(np.mean([w["gemv_up"][1] for w in work]))
+        dn_b = float(np.mean([w["gemv_down"][0] for w in work]))
+        dn_f = float(np.mean([w["gemv_down"][1] for w in work]))
+        out[f"T{T}"] = {"tokens_s": round(T / (us * 1e-6), 1), "us_per_step": round(us, 2),
+                        "distinct_experts": d, "alg_bytes_per_step": int(alg),
+                        "layer_GB_s": round(alg / (us * 1e-6) / 1e9, 1),
+                        "layer_frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "gemv_up_roofline": roofline("gemv_up", up_b, up_f, kern["gemv_up"] * 1e3),
+                        "gemv_down_roofline": roofline("gemv_down", dn_b, dn_f, kern["gemv_down"] * 1e3),
+                        "kernel_us": {k: round(v * 1e3, 3) for k, v in kern.items()}}
+        if T == 16:
+            out["T16"]["gemv_up_roofline"]["traffic"] = measured_traffic("gemv_up_decode_T16_hbm_traffic.md")
+        log(f"decode T={T}: {out[f'T{T}']}")
+    for mm in layers:
+        mm.close()
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_prefill(args, dev, copies=2):
+    """The prefill workload: 16 chunks of 128 tokens (2048) per forward, router
+    logit bias N(0, 0.5); the expert GEMMs run on the matrix cores."""
+    import torch
+    import synth
+    from quantized_routed_expert_bit_amd import MoELayer
+    wl = synth.WORKLOADS[2]
+    sh = wl.shape
+    T = wl.batches[0]
+    layers = []
+    for l in range(copies):
+        li = synth.LayerInputs(0, 2, l, sh, wl.bias)
+        w = synth.upload_layer(li, dev)
+        mm = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, T)
+        mm.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
+        mm._w = w
+        layers.append(mm)
+    xs = [synth.bf16_tensor(synth.make_hidden(0, 2, T, sh.hidden, tag=150 + l), dev) for l in range(copies)]
+    ys = [torch.empty((T, sh.hidden), dtype=torch.float32, device=dev) for _ in range(copies)]
+    counts = []
+    for l in range(copies):
+        _, ids, _ = layers[l].forward(xs[l], return_selection=True)
+        counts.append(np.bincount(ids.cpu().numpy().reshape(-1), minlength=sh.n_experts))
+    step = lambda i: layers[i % copies].forward(xs[i % copies], y=ys[i % copies])  # noqa: E731
+    for i in range(2):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(4, args.steps // 2)
+    el, _ = timed_graph(step, n)
+    kern, _ = profiled(layers, step, min(n, 8))
+    us = el * 1e6 / n
+    m0 = layers[0]
+    work = [kernel_work(c, sh, T, m0.mfma_min_rows, m0.wide_min_rows) for c in counts]
+    wf = float(np.mean([w["mfma_up"][1] + w["mfma_down"][1] for w in work]))
+    wb = float(np.mean([w["mfma_up"][0] + w["mfma_down"][0] for w in work]))
+    wide_us = (kern["mfma_up"] + kern["mfma_down"]) * 1e3
+    fl = layer_flops(sh, T)
+    res = {"tokens_s": round(T / (us * 1e-6), 1), "us_per_step": round(us, 2),
+           "layer_TFLOP_s": round(fl / (us * 1e-6) / 1e12, 1),
+           "layer_frac_mfma_peak": round(fl / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFS, 4),
+           "wide_roofline": roofline("mfma_up+mfma_down", wb, wf, wide_us) if wide_us else None,
+           "mfma_up_roofline": roofline("mfma_up", float(np.mean([w["mfma_up"][0] for w in work])),
+                                        float(np.mean([w["mfma_up"][1] for w in work])),
+                                        kern["mfma_up"] * 1e3) if kern["mfma_up"] else None,
+           "rows_per_expert": {"min": int(counts[0].min()), "median": float(np.median(counts[0])),
+                               "max": int(counts[0].max())},
+           "distinct_experts": float(np.mean([(c > 0).sum() for c in counts])),
+           "kernel_us": {k: round(v * 1e3, 3) for k, v in kern.items()}}
+    log(f"prefill: {res}")
+    for mm in layers:
+        mm.close()
+    del layers
+    torch.cuda.empty_cache()
+    return res
 
 
 def measure_ceilings(dev):
@@ -243,87 +534,16 @@ def measure_ceilings(dev):
     return out
 
 
-def run_large(args, dev, n_inputs=4):
-    """The large decode layer (hidden 7168, 512 experts, top-16, intermediate
-    2048, shared expert 2048; a 12.7 GB bank generated on the device) at 1, 8
-    and 64 tokens per forward.  The timed graph rotates over n_inputs token
-    batches, so successive forwards read different experts (the active set is
-    larger than the 256 MB Infinity Cache)."""
-    import torch
-    import synth
-    from quantized_routed_expert_bit_amd import MoELayer
-    from tests.parity import bf16_tensor
-    wl = synth.WORKLOADS[3]
-    sh = wl.shape
-    bank, stride = synth.gpu_bank(0, 3, 0, sh.hidden, sh.inter, sh.n_experts, dev)
-    shared, _ = synth.gpu_bank(0, 3, 0, sh.hidden, sh.shared_inter, 1, dev, shared=True)
-    router = synth.make_router(0, 3, 0, sh.hidden, sh.n_experts)
-    bias = synth.make_router_bias(0, 3, 0, sh.n_experts, wl.bias)
-    m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, max(wl.batches))
-    m.set_weights(torch.from_numpy(router).to(dev), bank, stride, shared,
-                  None if bias is None else torch.from_numpy(bias).to(dev))
-    log("  large layer uploaded")
-    out = {}
-    for T in wl.batches:
-        xs = [bf16_tensor(synth.make_hidden(0, 3, T, sh.hidden, tag=200 + i), dev) for i in range(n_inputs)]
-        y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
-        distinct = []
-        for x in xs:
-            _, ids, _ = m.forward(x, return_selection=True)
-            distinct.append(int((np.bincount(ids.cpu().numpy().reshape(-1), minlength=sh.n_experts) > 0).sum()))
-        for i in range(args.warmup):
-            m.forward(xs[i % n_inputs], y=y)
-        torch.cuda.synchronize()
-        steps = args.steps
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            for i in range(steps):
-                m.forward(xs[i % n_inputs], y=y)
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        g.replay()
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        del g
-        kp = min(steps, 40)
-        m.profile_start(kp)
-        torch.cuda._sleep(int(2.4e9 * 0.05))
-        for i in range(kp):
-            m.forward(xs[i % n_inputs], y=y)
-        torch.cuda.synchronize()
-        kern, _ = m.profile_read()
-        d = float(np.mean(distinct))
-        alg = d * record_bytes(sh.hidden, sh.inter) + record_bytes(sh.hidden, sh.shared_inter) + \
-            sh.n_experts * sh.hidden * 17 / 16 + T * sh.hidden * 6 + T * sh.top_k * 8
-        us = el * 1e6 / steps
-        out[f"T{T}"] = {"tokens_s": round(T * steps / el, 1), "us_per_step": round(us, 2),
-                        "distinct_experts": d, "alg_bytes_per_step": int(alg),
-                        "layer_GB_s": round(alg / (us * 1e-6) / 1e9, 1),
-                        "layer_frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                        "kernel_us": {k: round(v * 1e3, 3) for k, v in kern.items()}}
-        log(f"large T={T}: {out[f'T{T}']}")
-    m.close()
-    del bank, shared
-    torch.cuda.empty_cache()
-    return out
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--batch", type=int, default=16)
-    ap.add_argument("--copies", type=int, default=6, help="layer copies the steps rotate over")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=("all", "stack", "large", "decode", "prefill"),
+                    default="all",
+                    help="all: the stack headline plus every extra entry; stack: the headline "
+                         "only; large / decode / prefill: that workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the T=1 and T=4 lines")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill line")
-    ap.add_argument("--workload", choices=("all", "decode", "prefill", "large"), default="all",
-                    help="decode: only the 16-token decode line; prefill: only the prefill line; "
-                         "large: only the hidden-7168, 512-expert decode layer at 1, 8 and 64 tokens")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -334,91 +554,55 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
-    if args.workload == "prefill":
-        print(json.dumps({"prefill": run_prefill(args, dev)}), flush=True)
-        return
     if args.workload == "large":
         print(json.dumps({"large_decode": run_large(args, dev)}), flush=True)
         return
     if args.workload == "decode":
-        args.no_extra = args.no_prefill = args.no_cpu_baseline = True
-    T = args.batch
-    wl, layers = build_layers(1, args.copies, max(T, 16), dev)
-    sh = wl.shape
-    res = run_case(layers, sh, T, args.steps, args.warmup)
-    log(f"T={T}: {res['ms_per_step']*1e3:.1f} us/step, kernels {res['kern_ms']}")
-
-    # dominant kernel: the gate/up launch of the streaming path, which also
-    # carries the 32-row matrix-core tiles.  Algorithmic bytes per launch =
-    # (routed experts with fewer than wide_min_rows rows, + the shared expert
-    # when the batch is below that) * 2*H*I*4.5/8.
-    shared_streams = sh.has_shared and T < layers[0].wide_min_rows
-    up_bytes = res["streamed"] * 2 * sh.hidden * sh.inter * 9 / 16 + \
-        (2 * sh.hidden * sh.shared_inter * 9 / 16 if shared_streams else 0)
-    up_ms = res["kern_ms"]["gemv_up"]
-    achieved = up_bytes / (up_ms * 1e-3) / 1e9
-    layer_bytes = res["distinct"] * record_bytes(sh.hidden, sh.inter) + \
-        (record_bytes(sh.hidden, sh.shared_inter) if sh.has_shared else 0) + \
-        sh.n_experts * sh.hidden * 17 / 16 + T * sh.hidden * 6 + T * sh.top_k * 8
+        print(json.dumps({"decode": run_decode(args, dev)}), flush=True)
+        return
+    if args.workload == "prefill":
+        print(json.dumps({"prefill": run_prefill(args, dev)}), flush=True)
+        return
+    import synth
+    sh = synth.WORKLOADS[4].shape
+    res, layers, x32 = run_stack(args, dev)
     out = {
         "metric": METRIC,
-        "value": round(res["tok_s"], 1),
+        "value": round(res["tokens_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(res["ms_per_step"], 5),
+        "ms_per_step": round(res["us_per_step"] * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"decode MoE layer: hidden {sh.hidden}, {sh.n_experts} experts, "
-                               f"top-{sh.top_k}, intermediate {sh.inter}, shared expert "
-                               f"{sh.shared_inter}, {T} tokens per forward, 4-bit g64 experts, "
-                               f"8-bit router, {args.copies} rotating layer copies",
-                   "tokens_per_step": T, "layer_copies": args.copies, "launch": "hip_graph"},
-        "roofline": {"bound": "hbm", "kernel": "gemv_up", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if T == 16 else None,
-                     "bytes_per_launch": int(up_bytes),
-                     "avg_launch_us": round(up_ms * 1e3, 3)},
-        "layer_hbm": {"alg_bytes_per_step": int(layer_bytes),
-                      "GB_s": round(layer_bytes / (res["ms_per_step"] * 1e-3) / 1e9, 1),
-                      "frac": round(layer_bytes / (res["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "kernel_us": {k: round(v * 1e3, 3) for k, v in res["kern_ms"].items()},
-        "eager_us_per_step": round(res["eager_ms_per_step"] * 1e3, 2),
-        "distinct_experts": res["distinct"],
-        "streamed_experts": res["streamed"],
+        "config": {"workload": f"skewed 8-layer MoE stack: hidden {sh.hidden}, {sh.n_experts} "
+                               f"experts, top-{sh.top_k}, intermediate {sh.inter}, shared expert "
+                               f"{sh.shared_inter}, 4-bit g64 experts, 8-bit router, Zipf(1.1) "
+                               f"router prior, 256 tokens, fp32 residual, lookahead on",
+                   "layers": 8, "tokens_per_step": 256, "launch": "hip_graph",
+                   "timing": "HIP events around one graph replay of `steps` steps"},
+        "roofline": res["roofline"],
+        "stack": {k: v for k, v in res.items() if k not in ("roofline",)},
     }
-    if not args.no_extra:
-        extra = {}
-        for Tx in (1, 4):
-            r = run_case(layers, sh, Tx, args.steps, args.warmup, tag=Tx)
-            ub = r["streamed"] * 2 * sh.hidden * sh.inter * 9 / 16 + \
-                (2 * sh.hidden * sh.shared_inter * 9 / 16
-                 if sh.has_shared and Tx < layers[0].wide_min_rows else 0)
-            extra[f"T{Tx}"] = {"tokens_s": round(r["tok_s"], 1), "us_per_step": round(r["ms_per_step"] * 1e3, 2),
-                               "gemv_up_GB_s": round(ub / (r["kern_ms"]["gemv_up"] * 1e-3) / 1e9, 1),
-                               "kernel_us": {k: round(v * 1e3, 3) for k, v in r["kern_ms"].items()},
-                               "distinct_experts": r["distinct"]}
-            log(f"T={Tx}: {extra[f'T{Tx}']}")
-        out["extra"] = extra
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(layers[0], sh, T)
-    if not args.no_extra:
-        c = measure_ceilings(dev)
-        c["gemv_up_frac_of_copy"] = round(achieved / c["copy_GB_s"], 4)
-        out["ceilings"] = c
-    if not args.no_prefill:
-        for m in layers:
-            m.close()
-        del layers
-        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline_stack(layers, x32)
+    for m in layers:
+        m.close()
+    del layers
+    torch.cuda.empty_cache()
+    if args.workload == "all":
+        out["large_decode"] = run_large(args, dev)
+        out["decode"] = run_decode(args, dev)
         out["prefill"] = run_prefill(args, dev)
-        if "ceilings" in out:
-            out["ceilings"]["prefill_layer_frac_of_gemm"] = round(
-                out["prefill"]["layer_TFLOP_s"] / out["ceilings"]["f16_gemm_TFLOP_s"], 4)
+        c = measure_ceilings(dev)
+        c["prefill_layer_frac_of_gemm"] = round(out["prefill"]["layer_TFLOP_s"] / c["f16_gemm_TFLOP_s"], 4)
+        c["decode_T16_gemv_up_frac_of_copy"] = round(
+            out["decode"]["T16"]["gemv_up_roofline"]["achieved"] / c["copy_GB_s"], 4)
+        out["ceilings"] = c
     print(json.dumps(out), flush=True)
 
 
