@@ -100,6 +100,16 @@ extern "C" {
 
 #define MOE_BF16 1              /* x dtype: bf16 [T, H]                           */
 #define MOE_F32  2              /* x dtype: fp32 [T, H] (e.g. a residual stream)  */
+/* Input precision and range.  The router computes its logits from x at fp32
+ * accuracy (bf16 x converts to fp16 exactly; fp32 x is split into fp16 hi and
+ * lo halves that both enter the dot products).  The expert FFNs take x rounded
+ * once to fp16 (round to nearest even; exact for bf16 x inside fp16's range),
+ * dequantize the matrix-core paths' weights to fp16 (one rounding), and store
+ * h = SiLU(Wg x) * (Wu x) in fp16; every sum is fp32.  Supported inputs are
+ * finite with |x| <= 65504 and |h| <= 65504 (fp16's largest finite value; a
+ * larger value becomes +-inf in the fp16 staging); magnitudes below 2^-14 keep
+ * an absolute precision of 2^-25 (fp16 subnormals) and below 2^-25 become 0.
+ * With MOE_F_RMSNORM the layer's input has RMS 1, so |x| <= sqrt(H). */
 
 #define MOE_F_SHARED  1u        /* config flag: an always-on shared expert exists */
 #define MOE_F_RMSNORM 2u        /* config flag: the layer runs on x / sqrt(mean(x^2) + 1e-6),

@@ -207,16 +207,19 @@ def rms_normalize(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
 
 
 def oracle_stack(layers, x0: np.ndarray, lookahead_k: int | None = None,
-                 norm: bool = False, pool=None) -> dict:
+                 norm: bool = False, pool=None, force_ids=None) -> dict:
     """r_0 = x0; y_l = layer_l(n(r_l)); r_{l+1} = r_l + y_l, with n the RMS norm
     when ``norm`` (else the identity).  With lookahead_k, also the next layer's
     router on n(r_l) (its top-lookahead_k ids), for reporting only: it never
-    feeds back into the result.  ``pool`` is passed to each layer's forward."""
+    feeds back into the result.  ``pool`` is passed to each layer's forward;
+    ``force_ids`` (one [T, k] selection per layer, or None) evaluates each
+    layer on a given selection, as forward(force_ids=...) does."""
     r = np.asarray(x0, dtype=np.float64)
     per_layer = []
     for li, layer in enumerate(layers):
         xin = rms_normalize(r) if norm else r
-        res = layer.forward(xin, pool=pool)
+        res = layer.forward(xin, pool=pool,
+                            force_ids=None if force_ids is None else force_ids[li])
         res["input"] = r
         if lookahead_k is not None and li + 1 < len(layers):
             pred, _ = select_topk(layers[li + 1].logits(xin), lookahead_k)

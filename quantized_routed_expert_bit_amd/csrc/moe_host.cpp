@@ -74,7 +74,6 @@ WsLayout ws_layout(const moe_config& c) {
   };
   L.part = take(KS * T * Epad * 4);
   L.x16 = take(T * H * 2);
-  L.x16lo = take(T * H * 2);
   L.xs = take(T * G * 8);
   L.ids = take(Tk * 4);
   L.p = take(Tk * 4);
@@ -303,7 +302,7 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
         (e = hipStreamWaitEvent(ms, ctx->fork, 0)) != hipSuccess)
       return hip_fail(ctx, e, "forking the matrix-core stream");
     mark(3, 0, ms);
-    e = launch_mfma_up(d, f32, n_tokens, ms);
+    e = launch_mfma_up(d, n_tokens, ms);
     if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core gate/up launch");
     mark(3, 1, ms);
     mark(4, 0, ms);
@@ -314,7 +313,7 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
       return hip_fail(ctx, e, "joining the matrix-core stream");
   }
   mark(1, 0, s);
-  e = launch_gemv_up(d, f32, n_tokens, s);
+  e = launch_gemv_up(d, n_tokens, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "streaming gate/up launch");
   mark(1, 1, s);
   mark(2, 0, s);

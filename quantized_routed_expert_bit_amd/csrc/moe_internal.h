@@ -64,7 +64,7 @@ enum MiscSlot {
 };
 
 struct WsLayout {
-  size_t part, x16, x16lo, xs, ids, p, offs, misc,
+  size_t part, x16, xs, ids, p, offs, misc,
       slots, items, mitems, ntiles, wunits_up, wunits_dn, pred, hbuf, hs, yslot, xn, total;
   int cap_up, cap_dn;   // entries per XCD of the wide unit lists
 };
@@ -97,10 +97,10 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
                          float* logits_out, int32_t* ids_out, float* p_out,
                          hipStream_t s);
 // The streaming launches also run the narrow (32-row) matrix-core tiles.
-hipError_t launch_gemv_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
+hipError_t launch_gemv_up(const LayerDev& d, int T, hipStream_t s);
 hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s);
 bool mfma_needed(const LayerDev& d, int T);
-hipError_t launch_mfma_up(const LayerDev& d, int x_f32, int T, hipStream_t s);
+hipError_t launch_mfma_up(const LayerDev& d, int T, hipStream_t s);
 hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s);
 hipError_t launch_combine(const LayerDev& d, int T, const float* p, const float* residual, float* y,
                           hipStream_t s);

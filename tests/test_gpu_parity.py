@@ -72,10 +72,12 @@ def test_router_logits(torch_dev, cfg):
     assert err < 4e-6
 
 
-@pytest.mark.parametrize("T", [128, 300])
+@pytest.mark.parametrize("T", [64, 128, 300])
 def test_router_logits_matrix_core(torch_dev, T):
-    """From 128 bf16 tokens the router GEMV runs on the matrix cores (128-token
-    tiles; 300 leaves a ragged last tile)."""
+    """From 64 tokens the router GEMV runs on the matrix cores (64-token tiles;
+    300 leaves a ragged last tile), for bf16 input and for fp32 input (hi and
+    lo fp16 halves, two products per step)."""
+    import torch
     wl = synth.WORKLOADS[1]
     li = synth.layer_inputs(wl)
     m = _layer(li, torch_dev, T)
@@ -84,6 +86,11 @@ def test_router_logits_matrix_core(torch_dev, T):
     lg = m.router_logits(P.bf16_tensor(xb, torch_dev)).cpu().numpy()
     err = np.abs(lg - ol.logits(oracle.bf16_bits_to_f64(xb))).max()
     P.log(f"router matrix-core T={T}: max |logit err| = {err:.3e}")
+    assert err < 4e-6
+    x32 = (np.random.default_rng(T).standard_normal((T, wl.shape.hidden)) * 3.0 + 0.5).astype(np.float32)
+    lg = m.router_logits(torch.from_numpy(x32).to(torch_dev)).cpu().numpy()
+    err = np.abs(lg - ol.logits(x32.astype(np.float64))).max()
+    P.log(f"router matrix-core T={T} fp32 input: max |logit err| = {err:.3e}")
     assert err < 4e-6
 
 

@@ -453,3 +453,27 @@ def test_concurrent_expert_evaluation_is_identical():
         b = layer.forward(x, pool=ex)
     for key in ("y", "ids", "p", "gap", "logits"):
         assert np.array_equal(a[key], b[key]), key
+
+
+def test_stack_forced_selections():
+    """oracle_stack(force_ids=...) with each layer's own selection is bitwise
+    the unforced stack; with another selection at one layer it is the
+    hand-composed stack of forward(force_ids) calls and residual adds."""
+    layers = []
+    for l in range(3):
+        router = synth.make_router(3, 92, l, 128, 8)
+        recs = [synth.make_record(3, 92, l, e, 128, 64) for e in range(8)]
+        layers.append(oracle.OracleLayer(128, 8, 2, 64, 0, router, None,
+                                         (lambda rs: (lambda e: rs[e]))(recs)))
+    x = np.random.default_rng(7).standard_normal((5, 128)) * 2.0
+    base = oracle.oracle_stack(layers, x, norm=True)
+    own = [lr["ids"] for lr in base["layers"]]
+    again = oracle.oracle_stack(layers, x, norm=True, force_ids=own)
+    assert np.array_equal(again["out"], base["out"])
+    other = [own[0], np.array([[6, 7]] * 5), own[2]]
+    forced = oracle.oracle_stack(layers, x, norm=True, force_ids=other)
+    r = x
+    for layer, sel in zip(layers, other):
+        r = r + layer.forward(oracle.rms_normalize(r), force_ids=sel)["y"]
+    assert np.array_equal(forced["out"], r)
+    assert not np.allclose(forced["out"], base["out"])
