@@ -9,12 +9,14 @@ pass of the batch through all eight layers (8 moe_forward calls: router, top-k
 and bucketing, gate/up, down, combine with the residual add).  The value is
 tokens/s through the stack.
 
-The timed region is one HIP-graph replay of K steps, bracketed by device
-synchronisation and timed with HIP events on the stream it runs on.  Per-kernel
-durations come from the library's own event pairs around each kernel in an
-eager pass over the same steps.  The other workloads (the large decode layer at
-1, 8 and 64 tokens, the decode layer at 1, 4 and 16 tokens, the 2048-token
-prefill) are reported as extra entries, each with its fraction of the roofline.
+The timed region is K eager steps, bracketed by device synchronisation and
+timed with HIP events on the stream they run on; the library's own event pairs
+around each kernel in those same steps give the per-kernel durations (a step is
+milliseconds of GPU work, so eager launches cost nothing measurable).  The
+other workloads (the large decode layer at 1, 8 and 64 tokens, the decode layer
+at 1, 4 and 16 tokens, the 2048-token prefill) are reported as extra entries,
+each with its fraction of the roofline; they are timed as graph replays, and
+their kernels in a separate eager pass.
 
 Prints ONE JSON line (one GPU).
 """
@@ -153,16 +155,22 @@ def timed_graph(step, steps):
     return e0.elapsed_time(e1) * 1e-3, host
 
 
-def profiled(layers, step, n_steps):
+def profiled(layers, step, n_steps, timed=False):
     """Average ms per launch of each kernel slot over n_steps eager steps, from
     the library's event pairs (a spin kernel first holds the GPU while the host
-    queues the steps).  Returns ({kernel: ms}, {kernel: launches per step})."""
+    queues the steps).  Returns ({kernel: ms}, {kernel: launches per step}),
+    and with timed=True also the seconds the steps took, from HIP events on the
+    current stream around them (after the spin), between synchronisations."""
     import torch
     for m in layers:
         m.profile_start(n_steps * 4)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(int(2.4e9 * 0.05))
+    e0.record()
     for i in range(n_steps):
         step(i)
+    e1.record()
     torch.cuda.synchronize()
     tot = {k: 0.0 for k in KERNELS}
     n = {k: 0 for k in KERNELS}
@@ -172,8 +180,9 @@ def profiled(layers, step, n_steps):
             if avg[k] > 0:
                 tot[k] += avg[k] * calls
                 n[k] += calls
-    return ({k: tot[k] / n[k] if n[k] else 0.0 for k in KERNELS},
-            {k: n[k] / n_steps for k in KERNELS})
+    out = ({k: tot[k] / n[k] if n[k] else 0.0 for k in KERNELS},
+           {k: n[k] / n_steps for k in KERNELS})
+    return out + (e0.elapsed_time(e1) * 1e-3,) if timed else out
 
 
 def host_info():
@@ -254,9 +263,12 @@ def run_stack(args, dev):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    el, host = timed_graph(step, args.steps)
+    # the timed region: `steps` eager steps, timed with HIP events on the
+    # stream they run on, with the library's event pairs around every kernel
+    # (each step is milliseconds of GPU work, so launching eagerly costs
+    # nothing measurable)
+    kern, per_step, el = profiled(layers, step, args.steps, timed=True)
     us_step = el * 1e6 / args.steps
-    kern, per_step = profiled(layers, step, min(args.steps, 10))
     rmin, rwide = layers[0].mfma_min_rows, layers[0].wide_min_rows
     work = [kernel_work(c, sh, T, rmin, rwide) for c in counts]
     distinct = [int((c > 0).sum()) for c in counts]
@@ -270,8 +282,7 @@ def run_stack(args, dev):
     rl = roofline(dom, b, f, kern[dom] * 1e3)
     rl["traffic"] = measured_traffic(f"{dom}_stack_hbm_traffic.md")
     res = dict(
-        tokens_s=T * args.steps / el, us_per_step=us_step, host_us_per_step=host * 1e6 / args.steps,
-        roofline=rl,
+        tokens_s=T * args.steps / el, us_per_step=us_step, roofline=rl,
         stack_hbm={"alg_bytes_per_step": int(alg), "GB_s": round(alg / (el / args.steps) / 1e9, 1),
                    "frac": round(alg / (el / args.steps) / 1e9 / HBM_PEAK_GBS, 4)},
         stack_mfma={"flops_per_step": int(flops),
@@ -583,8 +594,9 @@ def main():
                                f"experts, top-{sh.top_k}, intermediate {sh.inter}, shared expert "
                                f"{sh.shared_inter}, 4-bit g64 experts, 8-bit router, Zipf(1.1) "
                                f"router prior, 256 tokens, fp32 residual, lookahead on",
-                   "layers": 8, "tokens_per_step": 256, "launch": "hip_graph",
-                   "timing": "HIP events around one graph replay of `steps` steps"},
+                   "layers": 8, "tokens_per_step": 256, "launch": "eager",
+                   "timing": "HIP events around `steps` eager steps, the library's event pairs "
+                             "around every kernel in the same steps"},
         "roofline": res["roofline"],
         "stack": {k: v for k, v in res.items() if k not in ("roofline",)},
     }

@@ -52,7 +52,13 @@
  *       u32 magic = 0x58455251 ("QREX"), u32 version = 1,
  *       i32 expert_id (index in the bank; -1 for the shared expert),
  *       u32 hidden, u32 inter, u32 group = 64, u32 bits = 4, u32 tile_rows = 64,
- *       u64 gate_off, u64 up_off, u64 down_off, u64 end_off, rest zero.
+ *       u64 gate_off, u64 up_off, u64 down_off, u64 end_off,
+ *       u32 payload_crc32 (at byte 64): CRC-32 of bytes [gate_off, end_off)
+ *           with zlib's polynomial and conditioning (reflected 0xEDB88320,
+ *           initial value and final xor 0xFFFFFFFF),
+ *       u32 hflags (at byte 68): bit 0 set iff payload_crc32 is present (else
+ *           payload_crc32 is 0); other bits zero,
+ *       rest zero.
  *   gate: tiled 4-bit matrix I x H at gate_off = 256
  *   up:   tiled 4-bit matrix I x H at up_off   = gate_off + (I/64)(H/64)*2304
  *   down: tiled 4-bit matrix H x I at down_off = up_off   + (I/64)(H/64)*2304
@@ -114,6 +120,9 @@ extern "C" {
 #define MOE_F_SHARED  1u        /* config flag: an always-on shared expert exists */
 #define MOE_F_RMSNORM 2u        /* config flag: the layer runs on x / sqrt(mean(x^2) + 1e-6),
                                    per token (a parameter-free pre-norm, for residual stacks) */
+#define MOE_F_VERIFY  4u        /* config flag: moe_set_weights checks every record's
+                                   payload_crc32 on the GPU (WASTE page, "Disk streaming
+                                   mimarisi": a crc32 of the payload, checked on request) */
 
 #define MOE_ABI_VERSION 1
 
@@ -130,7 +139,7 @@ typedef struct moe_config {
     int32_t  group;         /* must be 64 */
     int32_t  max_tokens;    /* largest T a forward may pass, 1..65536 */
     int32_t  device;        /* HIP device ordinal the context runs on */
-    uint32_t flags;         /* MOE_F_SHARED | MOE_F_RMSNORM */
+    uint32_t flags;         /* MOE_F_SHARED | MOE_F_RMSNORM | MOE_F_VERIFY */
 } moe_config;
 
 /* Weights and workspace, all device pointers (borrowed). */
@@ -164,10 +173,14 @@ int moe_open(const moe_config *cfg, moe_ctx **out);
  * with one synchronous copy on `stream`, validates each with
  * moe_check_record_header (magic, expert id and offsets are checked before a
  * record is ever used: WASTE page, "Disk streaming mimarisi"), and initialises
- * the workspace's counters.  On any failure the context keeps no weights (a
- * later forward gives MOE_ESTATE): it refuses rather than computes from
- * unvalidated records.  Errors: MOE_EINVAL, MOE_EBADRECORD, MOE_ENOMEM
- * (workspace too small), MOE_EHIP. */
+ * the workspace's counters.  With MOE_F_VERIFY it also computes the CRC-32 of
+ * every record's payload on the GPU (moe_crc32's kernel, through the static
+ * scratch that moe_forward_noalloc uses, so it must not overlap such a call on
+ * the same GPU) and refuses a record whose checksum is absent or differs.  On
+ * any failure the context keeps no weights (a later forward gives
+ * MOE_ESTATE): it refuses rather than computes from unvalidated records.
+ * Errors: MOE_EINVAL, MOE_EBADRECORD, MOE_ENOMEM (workspace too small),
+ * MOE_EHIP. */
 int moe_set_weights(moe_ctx *ctx, const moe_weights *w, void *stream);
 
 /* Run the layer on T = n_tokens rows of x (x_dtype MOE_BF16 or MOE_F32,
@@ -259,12 +272,23 @@ const char *moe_last_error(const moe_ctx *ctx);
 /* Host-only validation of one record header (header_bytes >= 256 host bytes):
  * magic, version, expert_id == expected_id (-1 for the shared expert), hidden
  * and inter equal to the config's (inter = shared_inter when expected_id is -1),
- * group 64, bits 4, tile_rows 64, and section offsets exactly as the format
- * fixes them with end_off <= record_stride.  Returns MOE_OK or
+ * group 64, bits 4, tile_rows 64, section offsets exactly as the format fixes
+ * them with end_off <= record_stride, hflags 0 or 1 (payload_crc32 0 when 0),
+ * and the reserved bytes zero.  It cannot see a wrong payload_crc32: that is
+ * what MOE_F_VERIFY checks.  Returns MOE_OK or
  * MOE_EBADRECORD / MOE_EINVAL.  Touches no GPU. */
 int moe_check_record_header(const void *header, uint64_t header_bytes,
                             const moe_config *cfg, int32_t expected_id,
                             uint64_t record_stride);
+
+/* CRC-32 of n_bytes of device memory at dev_bytes (16-byte aligned), with
+ * zlib's polynomial and conditioning (the record payload checksum), into
+ * *crc_out (host).  Runs on the current device, ordered on `stream`, and
+ * waits for the result; its partial results use the static scratch of
+ * moe_forward_noalloc (calls that overlap one of those on the same GPU race).
+ * n_bytes 0 gives 0 without touching the device.  Errors: MOE_EINVAL (null
+ * pointer, misaligned address), MOE_EHIP. */
+int moe_crc32(const void *dev_bytes, uint64_t n_bytes, uint32_t *crc_out, void *stream);
 
 /* Test hook: dequantize a tiled matrix (bits 4 or 8) to fp32 [rows, cols] on
  * the GPU with the same decoding the kernels use. */

@@ -13,11 +13,12 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EBADRECORD, MOE_ESTATE, MO
 MOE_BF16, MOE_F32 = 1, 2
 MOE_F_SHARED = 1
 MOE_F_RMSNORM = 2
+MOE_F_VERIFY = 4
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every function include/moe.h declares
 EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
-            "moe_forward_noalloc",
+            "moe_forward_noalloc", "moe_crc32",
             "moe_router_logits", "moe_set_path_rows", "moe_close", "moe_strerror",
             "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
             "moe_profile_start", "moe_profile_read")
@@ -78,6 +79,8 @@ def load() -> ctypes.CDLL:
     lib.moe_check_record_header.restype = c_int
     lib.moe_debug_dequant.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]
     lib.moe_debug_dequant.restype = c_int
+    lib.moe_crc32.argtypes = [c_void_p, c_uint64, P(c_uint32), c_void_p]
+    lib.moe_crc32.restype = c_int
     lib.moe_profile_start.argtypes = [c_void_p, c_int32]
     lib.moe_profile_start.restype = c_int
     lib.moe_profile_read.argtypes = [c_void_p, P(c_float), P(c_int32), c_int32]
@@ -87,7 +90,8 @@ def load() -> ctypes.CDLL:
 
 
 def make_config(hidden, n_experts, top_k, inter, shared_inter=0, max_tokens=1, device=0,
-                rmsnorm=False):
+                rmsnorm=False, verify=False):
     return MoeConfig(ctypes.sizeof(MoeConfig), hidden, n_experts, top_k, inter,
                      shared_inter, 64, max_tokens, device,
-                     (MOE_F_SHARED if shared_inter else 0) | (MOE_F_RMSNORM if rmsnorm else 0))
+                     (MOE_F_SHARED if shared_inter else 0) | (MOE_F_RMSNORM if rmsnorm else 0)
+                     | (MOE_F_VERIFY if verify else 0))

@@ -110,7 +110,7 @@ static int check_config(const moe_config* c) {
   if (c->n_experts < 1 || c->n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
   if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > kMaxTopK) return MOE_EUNSUPPORTED;
   if (c->max_tokens < 1 || c->max_tokens > 65536) return MOE_EUNSUPPORTED;
-  if (c->flags & ~(MOE_F_SHARED | MOE_F_RMSNORM)) return MOE_EUNSUPPORTED;
+  if (c->flags & ~(MOE_F_SHARED | MOE_F_RMSNORM | MOE_F_VERIFY)) return MOE_EUNSUPPORTED;
   if (c->flags & MOE_F_SHARED) {
     if (c->shared_inter < 64 || c->shared_inter > 16384 || c->shared_inter % 64)
       return MOE_EUNSUPPORTED;
@@ -233,6 +233,37 @@ int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
   if (w->shared_record) {
     const int rc = moe_check_record_header(shdr.data(), 256, &c, -1, UINT64_MAX);
     if (rc != MOE_OK) return fail(ctx, rc, "shared record failed header validation");
+  }
+  if (c.flags & MOE_F_VERIFY) {
+    // payload checksums: every record must carry one, and the GPU's CRC of
+    // its payload must equal it
+    auto rd32 = [](const uint8_t* p) { uint32_t v; memcpy(&v, p, 4); return v; };
+    auto check = [&](const uint8_t* dev, const uint8_t* h, int n, uint64_t stride,
+                     const char* what) -> int {
+      for (int i = 0; i < n; ++i)
+        if (rd32(h + (size_t)i * 256 + 68) != 1u)
+          return fail(ctx, MOE_EBADRECORD, "%s %d carries no payload checksum", what, i);
+      std::vector<uint32_t> got(n);
+      uint64_t off, end;
+      memcpy(&off, h + 32, 8);
+      memcpy(&end, h + 56, 8);
+      hipError_t e2 = crc32_ranges(dev, stride, off, end - off, n,
+                                   reinterpret_cast<uint32_t*>(ctx->scratch),
+                                   kNoallocScratchBytes / 4, got.data(), s);
+      if (e2 != hipSuccess) return hip_fail(ctx, e2, "payload checksums");
+      for (int i = 0; i < n; ++i) {
+        const uint32_t want = rd32(h + (size_t)i * 256 + 64);
+        if (got[i] != want)
+          return fail(ctx, MOE_EBADRECORD, "%s %d: payload crc32 %08x, header says %08x", what, i,
+                      got[i], want);
+      }
+      return MOE_OK;
+    };
+    int rc = check(static_cast<const uint8_t*>(w->bank), hdr.data(), c.n_experts, w->record_stride,
+                   "record");
+    if (rc == MOE_OK && w->shared_record)
+      rc = check(static_cast<const uint8_t*>(w->shared_record), shdr.data(), 1, 0, "shared record");
+    if (rc != MOE_OK) return rc;
   }
   LayerDev& d = ctx->d;
   d.router = static_cast<const uint8_t*>(w->router);
@@ -482,6 +513,22 @@ const char* moe_strerror(int code) {
 }
 
 const char* moe_last_error(const moe_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+int moe_crc32(const void* dev_bytes, uint64_t n_bytes, uint32_t* crc_out, void* stream) {
+  if (!crc_out) return MOE_EINVAL;
+  if (n_bytes == 0) {   // the CRC of no bytes
+    *crc_out = 0;
+    return MOE_OK;
+  }
+  if (!dev_bytes || ((uintptr_t)dev_bytes & 15)) return MOE_EINVAL;
+  int dev = 0;
+  uint8_t* tmp = nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || noalloc_scratch(dev, &tmp) != hipSuccess) return MOE_EHIP;
+  const hipError_t e = crc32_ranges(static_cast<const uint8_t*>(dev_bytes), 0, 0, n_bytes, 1,
+                                    reinterpret_cast<uint32_t*>(tmp), kNoallocScratchBytes / 4,
+                                    crc_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
 
 int moe_debug_dequant(const void* tiles, int32_t bits, int32_t rows, int32_t cols, float* out,
                       void* stream) {

@@ -108,6 +108,11 @@ hipError_t launch_ws_init(const LayerDev& d, hipStream_t s);
 hipError_t launch_rmsnorm(const LayerDev& d, const void* x, int x_f32, int T, hipStream_t s);
 hipError_t launch_debug_dequant(const void* tiles, int bits, int rows, int cols, float* out,
                                 hipStream_t s);
+// CRC-32 (zlib's) of n byte ranges base + r * stride + off, len bytes each
+// (base 16-byte aligned, stride and off multiples of 16), into host_out[r];
+// dev_tmp holds tmp_words partial results.  Synchronizes the stream.
+hipError_t crc32_ranges(const uint8_t* base, uint64_t stride, uint64_t off, uint64_t len, int n,
+                        uint32_t* dev_tmp, size_t tmp_words, uint32_t* host_out, hipStream_t s);
 // Device address of the library's static scratch array (kNoallocScratchBytes)
 // on `device`, which must be the current device; looked up once per device.
 hipError_t noalloc_scratch(int device, uint8_t** out);

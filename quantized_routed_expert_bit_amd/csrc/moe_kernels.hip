@@ -34,7 +34,9 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 namespace qreb {
 
@@ -2524,6 +2526,137 @@ hipError_t launch_ws_init(const LayerDev& d, hipStream_t s) {
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, base,
                      (int)n, 0);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ crc32 ----
+// CRC-32 with zlib's polynomial and conditioning (reflected polynomial
+// 0xEDB88320, initial value and final xor 0xFFFFFFFF), for the optional
+// payload check of the records (the WASTE page, "Disk streaming mimarisi":
+// a crc32 of each record's payload, checked on request).  Every workgroup
+// takes one part of one range; each of its threads runs a table-driven CRC
+// (four 256-entry tables in LDS, four bytes per step) over its own chunk, and
+// the chunks are joined in order by the CRC's linearity:
+//     crc(A B) = crc(A) * x^(8 |B|) mod P  xor  crc(B)
+// (multiplication of polynomials over GF(2), reduced mod P).  Parts of a range
+// are joined the same way on the host.
+
+constexpr uint32_t kCrcPoly = 0xEDB88320u;   // P, bit-reflected
+constexpr int kCrcThreads = 256;
+
+// a * b mod P, both in the reflected representation (bit 31 is x^0)
+__host__ __device__ inline uint32_t crc_mulmod(uint32_t a, uint32_t b) {
+  if (!a) return 0;
+  uint32_t m = 1u << 31, p = 0;
+  for (;;) {
+    if (a & m) {
+      p ^= b;
+      if ((a & (m - 1)) == 0) break;
+    }
+    m >>= 1;
+    b = (b & 1) ? (b >> 1) ^ kCrcPoly : b >> 1;
+  }
+  return p;
+}
+
+// x^(8 n) mod P by square-and-multiply (x^8 is 1 << 23 reflected)
+__host__ __device__ inline uint32_t crc_xpow8n(uint64_t n) {
+  uint32_t r = 1u << 31, sq = 1u << 23;
+  while (n) {
+    if (n & 1) r = crc_mulmod(r, sq);
+    sq = crc_mulmod(sq, sq);
+    n >>= 1;
+  }
+  return r;
+}
+
+__host__ __device__ inline uint32_t crc_join(uint32_t crc_a, uint32_t crc_b, uint64_t len_b) {
+  return crc_mulmod(crc_xpow8n(len_b), crc_a) ^ crc_b;
+}
+
+// ranges: base + r * stride + off, len bytes each (base 16-byte aligned,
+// stride and off multiples of 16); part q of nparts covers
+// [q * plen, min(len, (q + 1) * plen)), plen a multiple of 16.
+// out[r * nparts + q] = crc of that part (the crc of an empty part is 0).
+__global__ __launch_bounds__(kCrcThreads) void crc32_kernel(const uint8_t* __restrict__ base,
+                                                            uint64_t stride, uint64_t off,
+                                                            uint64_t len, int nparts,
+                                                            uint64_t plen, uint32_t* __restrict__ out) {
+  __shared__ uint32_t tab[4][256];
+  __shared__ uint32_t s_crc[kCrcThreads];
+  __shared__ uint64_t s_len[kCrcThreads];
+  const int tid = threadIdx.x;
+  {   // tab[0] is the bytewise table; tab[j] advances a byte through j more zero bytes
+    uint32_t c = (uint32_t)tid;
+    for (int k = 0; k < 8; ++k) c = (c & 1) ? (c >> 1) ^ kCrcPoly : c >> 1;
+    tab[0][tid] = c;
+  }
+  __syncthreads();
+  for (int j = 1; j < 4; ++j) {
+    const uint32_t c = tab[j - 1][tid];
+    tab[j][tid] = (c >> 8) ^ tab[0][c & 0xffu];
+    __syncthreads();
+  }
+  const int r = (int)blockIdx.x / nparts, q = (int)blockIdx.x % nparts;
+  const uint8_t* src = base + (size_t)r * stride + off;
+  const uint64_t pb = min(len, (uint64_t)q * plen), pe = min(len, (uint64_t)(q + 1) * plen);
+  // this thread's chunk of the part, 16-byte aligned except the part's end
+  const uint64_t plen_q = pe - pb;
+  const uint64_t cl = ((plen_q + kCrcThreads - 1) / kCrcThreads + 15) & ~(uint64_t)15;
+  const uint64_t cb = min(pe, pb + (uint64_t)tid * cl), ce = min(pe, cb + cl);
+  uint32_t c = 0xffffffffu;
+  uint64_t i = cb;
+  for (; i + 16 <= ce; i += 16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c ^= w[k];
+      c = tab[3][c & 0xffu] ^ tab[2][(c >> 8) & 0xffu] ^ tab[1][(c >> 16) & 0xffu] ^ tab[0][c >> 24];
+    }
+  }
+  for (; i < ce; ++i) c = (c >> 8) ^ tab[0][(c ^ src[i]) & 0xffu];
+  s_crc[tid] = ce > cb ? ~c : 0u;
+  s_len[tid] = ce - cb;
+  __syncthreads();
+  // join neighbouring chunks, left to right, in a tree
+  for (int w = 1; w < kCrcThreads; w <<= 1) {
+    if ((tid & (2 * w - 1)) == 0) {
+      const uint64_t lb = s_len[tid + w];
+      if (lb) s_crc[tid] = s_len[tid] ? crc_join(s_crc[tid], s_crc[tid + w], lb) : s_crc[tid + w];
+      s_len[tid] += lb;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) out[blockIdx.x] = s_crc[0];
+}
+
+hipError_t crc32_ranges(const uint8_t* base, uint64_t stride, uint64_t off, uint64_t len, int n,
+                        uint32_t* dev_tmp, size_t tmp_words, uint32_t* host_out, hipStream_t s) {
+  // enough parts that the grid fills the device, each at least 64 KiB
+  int nparts = 1;
+  while (nparts < 64 && (uint64_t)n * nparts < 1024 && len / (uint64_t)(2 * nparts) >= 65536) nparts *= 2;
+  if ((size_t)n * nparts > tmp_words) return hipErrorInvalidValue;
+  const uint64_t plen = ((len + nparts - 1) / nparts + 15) & ~(uint64_t)15;
+  hipLaunchKernelGGL(crc32_kernel, dim3((unsigned)(n * nparts)), dim3(kCrcThreads), 0, s, base, stride,
+                     off, len, nparts, plen, dev_tmp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  std::vector<uint32_t> part((size_t)n * nparts);
+  e = hipMemcpyAsync(part.data(), dev_tmp, part.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return e;
+  for (int r = 0; r < n; ++r) {
+    uint32_t c = 0;
+    uint64_t done = 0;
+    for (int q = 0; q < nparts; ++q) {
+      const uint64_t pb = std::min(len, (uint64_t)q * plen), pe = std::min(len, (uint64_t)(q + 1) * plen);
+      if (pe <= pb) continue;
+      c = done ? crc_join(c, part[(size_t)r * nparts + q], pe - pb) : part[(size_t)r * nparts + q];
+      done += pe - pb;
+    }
+    host_out[r] = c;
+  }
+  return hipSuccess;
 }
 
 // ------------------------------------------------ allocation-free scratch ----

@@ -43,7 +43,9 @@ extern "C" int moe_check_record_header(const void* header, uint64_t header_bytes
   if (gate != 256 || up != gate + sec || down != up + sec || end != down + sec)
     return MOE_EBADRECORD;
   if (end > record_stride) return MOE_EBADRECORD;
-  for (int i = 64; i < 256; ++i)
+  const uint32_t crc = rd32(h + 64), hflags = rd32(h + 68);
+  if (hflags > 1u || (hflags == 0u && crc != 0u)) return MOE_EBADRECORD;   // checksum field
+  for (int i = 72; i < 256; ++i)
     if (h[i] != 0) return MOE_EBADRECORD;                                // reserved bytes
   return MOE_OK;
 }

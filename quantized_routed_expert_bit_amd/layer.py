@@ -27,10 +27,10 @@ class MoELayer:
     """One routed-expert layer: router (8-bit), top-k, 4-bit experts, combine."""
 
     def __init__(self, hidden, n_experts, top_k, inter, shared_inter=0, max_tokens=1,
-                 device=0, rmsnorm=False):
+                 device=0, rmsnorm=False, verify=False):
         self.lib = L.load()
         self.cfg = L.make_config(hidden, n_experts, top_k, inter, shared_inter, max_tokens,
-                                 device, rmsnorm)
+                                 device, rmsnorm, verify)
         self.hidden, self.n_experts, self.top_k = hidden, n_experts, top_k
         self.max_tokens = max_tokens
         self.device = torch.device("cuda", device)
@@ -143,6 +143,17 @@ class MoELayer:
             self.close()
         except Exception:
             pass
+
+
+def crc32(t):
+    """CRC-32 (zlib's) of a contiguous device tensor's bytes, by the library's
+    GPU kernel (moe_crc32)."""
+    lib = L.load()
+    out = ctypes.c_uint32()
+    rc = lib.moe_crc32(_ptr(t), t.numel() * t.element_size(), ctypes.byref(out), _stream())
+    if rc != 0:
+        raise MoEError(rc, "moe_crc32")
+    return out.value
 
 
 def debug_dequant(tiles, bits, rows, cols):

@@ -7,7 +7,9 @@ Storage format (normative text: ``include/moe.h``, "Record format"):
   2304 bytes: 2048 bytes of codes followed by 64 (scale, bias) fp16 pairs.
 * An 8-bit matrix uses the same tiling with 4096 code bytes per tile (4352 B).
 * An expert record is a 256-byte header, then the gate, up and down matrices,
-  padded to a multiple of 4096 bytes.
+  padded to a multiple of 4096 bytes.  Host-generated records carry the
+  payload's CRC-32 in the header; device-generated banks (``gpu_bank``) do
+  not.
 
 Value recipe (the workloads' own description of the synthetic layer):
 
@@ -27,6 +29,7 @@ without generating the bank around it.
 from __future__ import annotations
 
 import struct
+import zlib
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -35,7 +38,7 @@ __all__ = [
     "GROUP", "TILE_ROWS", "Q4_TILE_BYTES", "Q4_CODE_BYTES", "Q8_TILE_BYTES",
     "Q8_CODE_BYTES", "HEADER_BYTES", "RECORD_ALIGN", "MAGIC", "VERSION",
     "SHARED_ID", "LayerShape", "Workload", "WORKLOADS", "record_layout",
-    "record_stride", "router_bytes_len", "make_record", "make_router",
+    "record_stride", "router_bytes_len", "make_record", "set_payload_crc32", "make_router",
     "make_router_bias", "make_hidden", "bf16_bits_from_f32", "LayerInputs",
 ]
 
@@ -142,10 +145,20 @@ def _pack_header(buf: np.ndarray, expert_id: int, hidden: int, inter: int, lay: 
     buf[: len(hdr)] = np.frombuffer(hdr, dtype=np.uint8)
 
 
+def set_payload_crc32(buf: np.ndarray) -> np.ndarray:
+    """Write the header's payload checksum (CRC-32 of bytes [gate_off, end_off),
+    zlib's) and set hflags bit 0; returns buf."""
+    gate, end = struct.unpack_from("<Q", bytes(buf[32:40]))[0], struct.unpack_from("<Q", bytes(buf[56:64]))[0]
+    crc = zlib.crc32(memoryview(np.ascontiguousarray(buf[gate:end])))
+    buf[64:72] = np.frombuffer(struct.pack("<II", crc, 1), dtype=np.uint8)
+    return buf
+
+
 def make_record(seed: int, cfg: int, layer: int, expert: int, hidden: int, inter: int,
-                shared: bool = False) -> np.ndarray:
+                shared: bool = False, checksum: bool = True) -> np.ndarray:
     """One expert record (uint8, record_stride bytes).  ``shared`` selects the
-    always-on expert's stream and marks its header with expert id -1."""
+    always-on expert's stream and marks its header with expert id -1; with
+    ``checksum`` the header carries the payload's CRC-32."""
     lay = record_layout(hidden, inter)
     buf = np.zeros(lay["stride"], dtype=np.uint8)
     rng = _rng(seed, cfg, layer, _T_SHARED if shared else _T_EXPERT, 0 if shared else expert)
@@ -154,7 +167,7 @@ def make_record(seed: int, cfg: int, layer: int, expert: int, hidden: int, inter
     for off in (lay["gate"], lay["up"], lay["down"]):
         _fill_tiles(buf[off: off + sec], lay["tiles"], Q4_CODE_BYTES, Q4_TILE_BYTES,
                     rng, 8.0, 8.0)
-    return buf
+    return set_payload_crc32(buf) if checksum else buf
 
 
 def make_router(seed: int, cfg: int, layer: int, hidden: int, n_experts: int) -> np.ndarray:

@@ -96,17 +96,57 @@ def test_record_header_validation(lib):
 
 
 def test_record_header_fuzz(lib):
-    """Random byte mutations never pass unless they leave the header unchanged."""
+    """Random byte mutations never pass the header check unless they leave the
+    header unchanged or touch only the payload checksum's value (which only
+    the payload verification can judge)."""
     cfg = _cfg()
     rec = synth.make_record(0, 1, 0, 9, 2816, 704)[:256].copy()
     rng = np.random.default_rng(0)
-    for _ in range(400):
+    n_crc_only = 0
+    for _ in range(600):
         bad = rec.copy()
         n = int(rng.integers(1, 6))
         pos = rng.integers(0, 256, n)
+        if rng.random() < 0.2:
+            pos = rng.integers(64, 68, n)                     # the checksum value only
         bad[pos] = rng.integers(0, 256, n).astype(np.uint8)
         rc = _check(lib, bad, cfg, 9, 3346432)
-        if np.array_equal(bad, rec):
+        changed = np.nonzero(bad != rec)[0]
+        if changed.size == 0 or (changed.min() >= 64 and changed.max() < 68):
+            n_crc_only += changed.size > 0
             assert rc == 0
         else:
             assert rc == -4
+    assert n_crc_only > 50
+
+
+def test_checksum_field_rules(lib):
+    """hflags 0 requires a zero checksum; hflags above 1 is refused; a record
+    without a checksum (hflags 0) passes the header check."""
+    import struct
+    cfg = _cfg()
+    rec = synth.make_record(0, 1, 0, 9, 2816, 704)
+    stride = len(rec)
+    assert struct.unpack_from("<II", bytes(rec[64:72]))[1] == 1
+    plain = synth.make_record(0, 1, 0, 9, 2816, 704, checksum=False)
+    assert _check(lib, plain[:256], cfg, 9, stride) == 0
+    h = rec[:256].copy()
+    h[68:72] = 0                                          # flag cleared, checksum left
+    assert _check(lib, h, cfg, 9, stride) == -4
+    h = rec[:256].copy()
+    h[68] = 3
+    assert _check(lib, h, cfg, 9, stride) == -4
+
+
+def test_generator_checksum_is_zlib_crc32():
+    """The record generator's checksum is zlib's CRC-32 of [gate_off, end_off)."""
+    import struct
+    import zlib
+    rec = synth.make_record(0, 0, 0, 3, 512, 256)
+    lay = synth.record_layout(512, 256)
+    crc, flags = struct.unpack_from("<II", bytes(rec[64:72]))
+    assert flags == 1 and crc == zlib.crc32(bytes(rec[lay["gate"]:lay["end"]]))
+    # a single flipped payload bit changes it
+    rec2 = rec.copy()
+    rec2[lay["down"] + 1000] ^= 4
+    assert zlib.crc32(bytes(rec2[lay["gate"]:lay["end"]])) != crc
