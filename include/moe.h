@@ -255,7 +255,7 @@ int moe_set_path_rows(moe_ctx *ctx, int32_t mfma_min_rows, int32_t wide_min_rows
  * 0 router+top-k+bucketing, 1 gate/up launch of the streaming path (which
  * also carries the 32-row matrix-core tiles), 2 down launch of the same,
  * 3 matrix-core gate/up (128-row tiles), 4 matrix-core down (128-row tiles),
- * 5 combine, 6 and 7 reserved (always 0).
+ * 5 combine, 6 expert-cache plan and fill (demand), 7 reserved (always 0).
  * Errors: MOE_EINVAL, MOE_EHIP. */
 #define MOE_PROFILE_SLOTS 8
 int moe_profile_start(moe_ctx *ctx, int32_t max_calls);
@@ -280,6 +280,56 @@ const char *moe_last_error(const moe_ctx *ctx);
 int moe_check_record_header(const void *header, uint64_t header_bytes,
                             const moe_config *cfg, int32_t expected_id,
                             uint64_t record_stride);
+
+/* ---------------------------------------------------------------------------
+ * Banks larger than HBM: an expert cache per layer
+ * ---------------------------------------------------------------------------
+ * The bank given to moe_set_weights may be pinned, mapped host memory (e.g.
+ * hipHostMalloc); the kernels then read it over PCIe, unless the context has an
+ * expert cache.  With one, a forward computes only on records in a bounded
+ * set of HBM slots (TurboFieldfare page, "Token üretim süreci": the router's
+ * expert ids are compared with a 16-slot LFU cache per layer, misses are read
+ * in, then the experts run; WASTE page, "RAM bütçesi ve dar performans
+ * aralığı": the expert cache is bounded, and a budget below one token's
+ * working set is refused).  After the top-k a one-workgroup plan looks the
+ * selected experts up; missing ones take the slots that sort first by
+ * (free, then fewest forwards that selected their expert, then least recently
+ * used, then lowest slot), never a slot whose expert this forward selects;
+ * a copy kernel then reads the missing records from the bank into their
+ * slots, and the expert kernels read them there.  All of it is decided on the
+ * GPU, ordered on the caller's stream: no host synchronisation, no
+ * allocation.  The selected experts, y, ids and p are bitwise those of the
+ * same context without a cache, and each forward reads the same record bytes
+ * from HBM; what the cache adds is the copies, which moe_cache_stats counts.
+ *
+ * With MOE_CACHE_PREFETCH, a forward of the previous layer that names this
+ * context as lookahead_next prefetches this layer's predicted experts (its
+ * router run one residual ahead, WASTE page, "Önceden okuma ve router
+ * tahmini") into this cache on a copy stream this context owns, overlapping
+ * that layer's compute; this context's next forward waits for the copies
+ * before its own plan.  A prefetch never evicts for itself a slot whose expert
+ * it predicts, and a record prefetched but not used is evicted first.
+ *
+ * moe_set_cache: slots is device memory of slots_bytes >= n_slots *
+ * record_stride bytes (256-aligned, caller-owned, borrowed until the next
+ * moe_set_cache, moe_set_weights or moe_close), n_slots in [min(E,
+ * max_tokens * k), E]; slots NULL or n_slots 0 removes the cache.  The cache
+ * starts empty, its counters at zero.  It needs the bound workspace (its
+ * state lives there); moe_set_weights removes it, and moe_forward_noalloc
+ * refuses a context that has one.  Errors: MOE_ESTATE (no weights or no
+ * workspace), MOE_ENOMEM (too few slots or bytes), MOE_EINVAL, MOE_EHIP.
+ *
+ * moe_cache_stats: the counters since moe_set_cache, into out[0 .. n-1]
+ * (waits for the stream): 0 forwards, 1 experts selected, 2 demand hits,
+ * 3 demand misses, 4 bytes copied on demand, 5 records prefetched, 6 bytes
+ * prefetched, 7 prefetched records later selected, 8 prefetched records
+ * evicted unused, 9..15 zero.  Errors: MOE_ESTATE (no cache), MOE_EINVAL,
+ * MOE_EHIP. */
+#define MOE_CACHE_PREFETCH 1u
+#define MOE_CACHE_STATS 16
+int moe_set_cache(moe_ctx *ctx, void *slots, uint64_t slots_bytes, int32_t n_slots,
+                  uint32_t flags, void *stream);
+int moe_cache_stats(moe_ctx *ctx, uint64_t *out, int32_t n, void *stream);
 
 /* CRC-32 of n_bytes of device memory at dev_bytes (16-byte aligned), with
  * zlib's polynomial and conditioning (the record payload checksum), into

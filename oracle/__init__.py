@@ -5,3 +5,4 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 library never routes through it and shares no code with it.
 """
 from .moe_ref import *  # noqa: F401,F403
+from .cache_ref import *  # noqa: F401,F403

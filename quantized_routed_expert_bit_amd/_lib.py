@@ -18,13 +18,16 @@ MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every function include/moe.h declares
 EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
-            "moe_forward_noalloc", "moe_crc32",
+            "moe_forward_noalloc", "moe_crc32", "moe_set_cache", "moe_cache_stats",
             "moe_router_logits", "moe_set_path_rows", "moe_close", "moe_strerror",
             "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
             "moe_profile_start", "moe_profile_read")
 # kernel timing slots of moe_profile_read (the last two are reserved)
 PROFILE_SLOTS = ("router", "gemv_up", "gemv_down", "mfma_up", "mfma_down", "combine",
-                 "reserved6", "reserved7")
+                 "cache", "reserved7")
+MOE_CACHE_PREFETCH = 1
+CACHE_STATS = ("forwards", "selected", "demand_hits", "demand_misses", "demand_bytes",
+               "prefetched", "prefetch_bytes", "prefetch_used", "prefetch_evicted_unused")
 
 
 class MoeConfig(ctypes.Structure):
@@ -79,6 +82,10 @@ def load() -> ctypes.CDLL:
     lib.moe_check_record_header.restype = c_int
     lib.moe_debug_dequant.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]
     lib.moe_debug_dequant.restype = c_int
+    lib.moe_set_cache.argtypes = [c_void_p, c_void_p, c_uint64, c_int32, c_uint32, c_void_p]
+    lib.moe_set_cache.restype = c_int
+    lib.moe_cache_stats.argtypes = [c_void_p, P(c_uint64), c_int32, c_void_p]
+    lib.moe_cache_stats.restype = c_int
     lib.moe_crc32.argtypes = [c_void_p, c_uint64, P(c_uint32), c_void_p]
     lib.moe_crc32.restype = c_int
     lib.moe_profile_start.argtypes = [c_void_p, c_int32]

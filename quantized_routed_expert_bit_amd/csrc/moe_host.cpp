@@ -29,7 +29,33 @@ struct moe_ctx {
   hipEvent_t fork = nullptr, join = nullptr;
   // this device's copy of the library's static scratch (moe_forward_noalloc)
   uint8_t* scratch = nullptr;
+  // expert cache: the stream that prefetches into this context's slots (a
+  // lookahead from the previous layer), and the event its next forward waits on
+  hipStream_t copy = nullptr;
+  hipEvent_t pf_done = nullptr;
+  bool pf_pending = false;
+  uint32_t cache_flags = 0;
 };
+
+// The device-side address of a buffer the kernels may read: device memory as
+// it is; host memory only if it is pinned and mapped (its device alias).
+static const void* device_view(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) return p;
+  if (a.type == hipMemoryTypeHost) {
+    void* dp = nullptr;
+    if (hipHostGetDevicePointer(&dp, const_cast<void*>(p), 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return dp;
+  }
+  return nullptr;
+}
 
 static void prof_clear(moe_ctx* c) {
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
@@ -96,6 +122,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.hs = take((Tk * (I / 32) + Ts * (Is / 32)) * 8);   // (S1, S2) per 32-column half
   L.yslot = take((Tk + Ts) * H * 4);
   L.xn = take((c.flags & MOE_F_RMSNORM) ? T * H * 4 : 0);
+  L.cache = take(kCacheBytes);
   L.total = o;
   return L;
 }
@@ -192,6 +219,10 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
 
 int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
   if (!ctx) return MOE_EINVAL;
+  if (ctx->pf_pending) {   // a prefetch may still be copying into the old slots
+    (void)hipEventSynchronize(ctx->pf_done);
+    ctx->pf_pending = false;
+  }
   ctx->has_weights = false;
   const moe_config& c = ctx->cfg;
   if (!w || w->struct_size != sizeof(moe_weights))
@@ -215,8 +246,11 @@ int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
   if (e != hipSuccess) return hip_fail(ctx, e, "hipSetDevice");
   hipStream_t s = static_cast<hipStream_t>(stream);
   std::vector<uint8_t> hdr((size_t)c.n_experts * 256);
+  const void* bank_dev = device_view(w->bank);
+  if (!bank_dev)
+    return fail(ctx, MOE_EINVAL, "bank is neither device memory nor pinned, mapped host memory");
   e = hipMemcpy2DAsync(hdr.data(), 256, w->bank, w->record_stride, 256, c.n_experts,
-                       hipMemcpyDeviceToHost, s);
+                       hipMemcpyDefault, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "copying record headers");
   std::vector<uint8_t> shdr(256);
   if (w->shared_record) {
@@ -259,7 +293,7 @@ int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
       }
       return MOE_OK;
     };
-    int rc = check(static_cast<const uint8_t*>(w->bank), hdr.data(), c.n_experts, w->record_stride,
+    int rc = check(static_cast<const uint8_t*>(bank_dev), hdr.data(), c.n_experts, w->record_stride,
                    "record");
     if (rc == MOE_OK && w->shared_record)
       rc = check(static_cast<const uint8_t*>(w->shared_record), shdr.data(), 1, 0, "shared record");
@@ -268,8 +302,16 @@ int moe_set_weights(moe_ctx* ctx, const moe_weights* w, void* stream) {
   LayerDev& d = ctx->d;
   d.router = static_cast<const uint8_t*>(w->router);
   d.router_bias = w->router_bias;
-  d.bank = static_cast<const uint8_t*>(w->bank);
+  d.bank = static_cast<const uint8_t*>(bank_dev);
   d.stride = w->record_stride;
+  d.slot_of = nullptr;                       // any expert cache is unbound with the old bank
+  d.cache_src = nullptr;
+  d.cache_slots = 0;
+  {
+    uint64_t end;
+    memcpy(&end, hdr.data() + 56, 8);
+    d.rec_bytes = end;
+  }
   d.shared = static_cast<const uint8_t*>(w->shared_record);
   d.ws = static_cast<uint8_t*>(w->workspace);
   if (d.ws) {
@@ -308,8 +350,15 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
     (void)hipEventRecord(ctx->ev[((size_t)call * MOE_PROFILE_SLOTS + slot) * 2 + end], st);
     if (end) ctx->launched[(size_t)call * MOE_PROFILE_SLOTS + slot] = 1;
   };
-  mark(0, 0, s);
   hipError_t e = hipSuccess;
+  // a prefetch into this context's cache (issued by the previous layer's
+  // lookahead) must land before this forward plans its cache
+  if (ctx->pf_pending) {
+    if ((e = hipStreamWaitEvent(s, ctx->pf_done, 0)) != hipSuccess)
+      return hip_fail(ctx, e, "waiting for the prefetch");
+    ctx->pf_pending = false;
+  }
+  mark(0, 0, s);
   const void* xin = x;
   int f32 = x_dtype == MOE_F32;
   if (d.rmsnorm) {   // the layer (and a lookahead router) sees the normalized rows
@@ -321,6 +370,32 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
   e = launch_router(d, xin, f32, n_tokens, 0, nullptr, ids_out, p_out, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "router launch");
   mark(0, 1, s);
+  const int max_sel = n_tokens * d.k < d.E ? n_tokens * d.k : d.E;
+  if (d.slot_of) {   // the experts of this forward into the cache
+    mark(6, 0, s);
+    if ((e = launch_cache_plan(d, 0, 0, s)) != hipSuccess ||
+        (e = launch_cache_fill(d, 0, max_sel, s)) != hipSuccess)
+      return hip_fail(ctx, e, "expert cache");
+    mark(6, 1, s);
+  }
+  // The next layer's router on this input ("one residual ahead"): its
+  // prediction orders that layer's work and, with a cache there, prefetches
+  // its experts on that context's copy stream while this layer computes.
+  // It reads x before the combine writes y, so y may alias x.
+  if (next) {
+    e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
+    if (next->d.slot_of && (next->cache_flags & MOE_CACHE_PREFETCH)) {
+      const int nmax = n_tokens * next->d.k < next->d.E ? n_tokens * next->d.k : next->d.E;
+      if ((e = hipEventRecord(next->pf_done, s)) != hipSuccess ||
+          (e = hipStreamWaitEvent(next->copy, next->pf_done, 0)) != hipSuccess ||
+          (e = launch_cache_plan(next->d, 1, n_tokens * next->d.k, next->copy)) != hipSuccess ||
+          (e = launch_cache_fill(next->d, 1, nmax, next->copy)) != hipSuccess ||
+          (e = hipEventRecord(next->pf_done, next->copy)) != hipSuccess)
+        return hip_fail(ctx, e, "lookahead prefetch");
+      next->pf_pending = true;
+    }
+  }
   // Wide matrix-core work (experts with many rows) runs on the context's side
   // stream, concurrently with the streaming launches, which also carry the
   // narrow matrix-core tiles; the two touch disjoint slots.  Decode-sized
@@ -351,11 +426,6 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
   e = launch_gemv_down(d, n_tokens, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "streaming down launch");
   mark(2, 1, s);
-  // The lookahead reads x before the combine writes y, so y may alias x.
-  if (next) {
-    e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
-    if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
-  }
   if (mf) {
     if ((e = hipStreamWaitEvent(s, ctx->join, 0)) != hipSuccess)
       return hip_fail(ctx, e, "joining the matrix-core stream");
@@ -392,6 +462,8 @@ int moe_forward_noalloc(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_
                         const float* residual, int32_t* ids_out, float* p_out, void* stream) {
   int rc = check_forward(ctx, x, x_dtype, n_tokens, y);
   if (rc != MOE_OK) return rc;
+  if (ctx->d.slot_of)
+    return fail(ctx, MOE_EINVAL, "a context with an expert cache keeps its state in its workspace");
   if (n_tokens == 0) return MOE_OK;
   // The workspace layout for exactly this batch, placed in the static scratch.
   LayerDev d = ctx->d;
@@ -492,10 +564,13 @@ int moe_set_path_rows(moe_ctx* ctx, int32_t mfma_min_rows, int32_t wide_min_rows
 
 void moe_close(moe_ctx* ctx) {
   if (!ctx) return;
+  if (ctx->pf_pending) (void)hipEventSynchronize(ctx->pf_done);
   prof_clear(ctx);
   if (ctx->join) (void)hipEventDestroy(ctx->join);
   if (ctx->fork) (void)hipEventDestroy(ctx->fork);
   if (ctx->side) (void)hipStreamDestroy(ctx->side);
+  if (ctx->pf_done) (void)hipEventDestroy(ctx->pf_done);
+  if (ctx->copy) (void)hipStreamDestroy(ctx->copy);
   delete ctx;
 }
 
@@ -513,6 +588,73 @@ const char* moe_strerror(int code) {
 }
 
 const char* moe_last_error(const moe_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+int moe_set_cache(moe_ctx* ctx, void* slots, uint64_t slots_bytes, int32_t n_slots, uint32_t flags,
+                  void* stream) {
+  if (!ctx) return MOE_EINVAL;
+  if (!ctx->has_weights) return fail(ctx, MOE_ESTATE, "no weights bound");
+  LayerDev& d = ctx->d;
+  if (!d.ws) return fail(ctx, MOE_ESTATE, "the expert cache keeps its state in the bound workspace");
+  if (flags & ~MOE_CACHE_PREFETCH) return fail(ctx, MOE_EINVAL, "unknown cache flags");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSetDevice(ctx->cfg.device);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipSetDevice");
+  // a prefetch still copying into the old slots must finish first
+  if (ctx->pf_pending) {
+    if ((e = hipEventSynchronize(ctx->pf_done)) != hipSuccess) return hip_fail(ctx, e, "prefetch");
+    ctx->pf_pending = false;
+  }
+  const uint8_t* src = d.slot_of ? d.cache_src : d.bank;
+  if (!slots || n_slots == 0) {   // unbind: the kernels read the bank again
+    d.bank = src;
+    d.slot_of = nullptr;
+    d.cache_src = nullptr;
+    d.cache_slots = 0;
+    return MOE_OK;
+  }
+  const int need = ctx->cfg.max_tokens * d.k < d.E ? ctx->cfg.max_tokens * d.k : d.E;
+  if (n_slots < need || n_slots > d.E)
+    return fail(ctx, MOE_ENOMEM,
+                "%d cache slots: a forward of %d tokens may select %d experts (slots must be in "
+                "[%d, %d])", n_slots, ctx->cfg.max_tokens, need, need, d.E);
+  if ((uintptr_t)slots & 255) return fail(ctx, MOE_EINVAL, "slots must be 256-byte aligned");
+  if (slots_bytes < (uint64_t)n_slots * d.stride)
+    return fail(ctx, MOE_ENOMEM, "slots hold %llu bytes, %d records need %llu",
+                (unsigned long long)slots_bytes, n_slots, (unsigned long long)n_slots * d.stride);
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, slots) != hipSuccess || a.type != hipMemoryTypeDevice) {
+    (void)hipGetLastError();
+    return fail(ctx, MOE_EINVAL, "slots must be device memory");
+  }
+  if (!ctx->copy && ((e = hipStreamCreateWithFlags(&ctx->copy, hipStreamNonBlocking)) != hipSuccess ||
+                     (e = hipEventCreateWithFlags(&ctx->pf_done, hipEventDisableTiming)) != hipSuccess))
+    return hip_fail(ctx, e, "creating the prefetch stream");
+  d.cache_src = src;
+  d.cache_src_stride = d.stride;
+  d.bank = static_cast<const uint8_t*>(slots);
+  d.slot_of = reinterpret_cast<const int*>(d.ws + d.L.cache + kCacheSlotOf);
+  d.cache_slots = n_slots;
+  ctx->cache_flags = flags;
+  e = launch_cache_reset(d, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "cache reset");
+  return MOE_OK;
+}
+
+int moe_cache_stats(moe_ctx* ctx, uint64_t* out, int32_t n, void* stream) {
+  if (!ctx || !out || n < 0) return MOE_EINVAL;
+  if (!ctx->d.slot_of) return fail(ctx, MOE_ESTATE, "no expert cache");
+  const int m = n < kCacheStats ? n : kCacheStats;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (ctx->pf_pending) e = hipStreamWaitEvent(s, ctx->pf_done, 0);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(out, ctx->d.ws + ctx->d.L.cache + kCacheStatsOff, (size_t)m * 8,
+                       hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "reading the cache counters");
+  for (int i = m; i < n; ++i) out[i] = 0;
+  return MOE_OK;
+}
 
 int moe_crc32(const void* dev_bytes, uint64_t n_bytes, uint32_t* crc_out, void* stream) {
   if (!crc_out) return MOE_EINVAL;

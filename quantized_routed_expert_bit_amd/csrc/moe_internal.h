@@ -63,9 +63,25 @@ enum MiscSlot {
   kMiscInts = 64,
 };
 
+// Expert-cache state in the workspace (byte offsets inside its region; every
+// array is sized for kMaxExperts, which bounds both E and the slot count).
+constexpr int kCacheStats = 16;
+constexpr size_t kCacheSlotOf = 0;                                  // int [E]: slot or -1
+constexpr size_t kCacheOwner = kCacheSlotOf + 4 * kMaxExperts;      // int [S]: expert or -1
+constexpr size_t kCacheFreq = kCacheOwner + 4 * kMaxExperts;        // u32 [E]
+constexpr size_t kCacheStamp = kCacheFreq + 4 * kMaxExperts;        // u32 [S]
+constexpr size_t kCachePf = kCacheStamp + 4 * kMaxExperts;          // u32 [S]
+constexpr size_t kCacheCopyD = kCachePf + 4 * kMaxExperts;          // int [2 E] demand copies
+constexpr size_t kCacheCopyP = kCacheCopyD + 8 * kMaxExperts;       // int [2 E] prefetch copies
+constexpr size_t kCacheNCopyD = kCacheCopyP + 8 * kMaxExperts;
+constexpr size_t kCacheNCopyP = kCacheNCopyD + 4;
+constexpr size_t kCacheClock = kCacheNCopyP + 4;
+constexpr size_t kCacheStatsOff = kCacheClock + 8;                  // u64 [kCacheStats]
+constexpr size_t kCacheBytes = kCacheStatsOff + 8 * kCacheStats;
+
 struct WsLayout {
   size_t part, x16, xs, ids, p, offs, misc,
-      slots, items, mitems, ntiles, wunits_up, wunits_dn, pred, hbuf, hs, yslot, xn, total;
+      slots, items, mitems, ntiles, wunits_up, wunits_dn, pred, hbuf, hs, yslot, xn, cache, total;
   int cap_up, cap_dn;   // entries per XCD of the wide unit lists
 };
 
@@ -78,9 +94,15 @@ struct LayerDev {
   // weights
   const uint8_t* router;
   const float* router_bias;
-  const uint8_t* bank;
+  const uint8_t* bank;      // the records the kernels read: the bank, or the cache's slots
   uint64_t stride;
   const uint8_t* shared;
+  const int* slot_of;       // with an expert cache: expert -> slot (in the workspace), else NULL
+  // expert cache: where missing records are copied from, slot count, bytes per copy
+  const uint8_t* cache_src;
+  uint64_t cache_src_stride;
+  int cache_slots;
+  uint64_t rec_bytes;
   // shape
   int H, E, Epad, k, I, Is, has_shared, rmsnorm, max_tokens;
   int mfma_min_rows;   // rows at which an expert leaves the streaming path
@@ -108,6 +130,11 @@ hipError_t launch_ws_init(const LayerDev& d, hipStream_t s);
 hipError_t launch_rmsnorm(const LayerDev& d, const void* x, int x_f32, int T, hipStream_t s);
 hipError_t launch_debug_dequant(const void* tiles, int bits, int rows, int cols, float* out,
                                 hipStream_t s);
+// Expert cache: plan (mode 0 demand from the bucketing, 1 prefetch from the
+// npred predicted ids), fill (at most max_copies records), reset.
+hipError_t launch_cache_plan(const LayerDev& d, int mode, int npred, hipStream_t s);
+hipError_t launch_cache_fill(const LayerDev& d, int mode, int max_copies, hipStream_t s);
+hipError_t launch_cache_reset(const LayerDev& d, hipStream_t s);
 // CRC-32 (zlib's) of n byte ranges base + r * stride + off, len bytes each
 // (base 16-byte aligned, stride and off multiples of 16), into host_out[r];
 // dev_tmp holds tmp_words partial results.  Synchronizes the stream.

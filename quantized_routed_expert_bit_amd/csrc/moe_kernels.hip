@@ -1348,6 +1348,7 @@ struct MfmaArgs {
   const uint8_t* bank;
   uint64_t stride;
   const uint8_t* shared;
+  const int* slot_of;      // expert -> cache slot of the bank, or NULL (the bank is indexed by expert)
   int H, E, k, I, Is, T;
   const uint16_t* x16;
   const uint16_t* hsrc;    // down: h rows
@@ -1361,6 +1362,16 @@ struct MfmaArgs {
   const int* slots;
   float* yslot;
 };
+
+// An expert's record: the shared one, or the bank's entry for expert e; with an
+// expert cache the bank is the cache's slot array and slot_of maps experts to
+// slots (the cache plan has placed every expert of this forward).
+__device__ __forceinline__ const uint8_t* record_of(const uint8_t* bank, uint64_t stride,
+                                                    const int* slot_of, const uint8_t* shared,
+                                                    bool sh, int e) {
+  if (sh) return shared;
+  return bank + (size_t)(slot_of ? slot_of[e] : e) * stride;
+}
 
 // SwiGLU of one (gate, up) pair: g * sigmoid(g) * u, with the hardware
 // base-2 exponential and reciprocal (each within about 1 ulp).  For very
@@ -1460,7 +1471,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
     s_slot[tid] = slot;
     s_src[tid] = UP ? (size_t)(slot < Tk ? slot / a.k : slot - Tk) * a.H : h_off(slot, Tk, a.I, a.Is);
   }
-  const uint8_t* rec = sh ? a.shared : a.bank + (size_t)e * a.stride;
+  const uint8_t* rec = record_of(a.bank, a.stride, a.slot_of, a.shared, sh, e);
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
   // B sources of this lane: codes of (nb, hi, row) and, for the scale DMA,
   // lanes 0-31 carry block 0's rows and lanes 32-63 block 1's
@@ -1668,7 +1679,7 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
   const size_t a_row = UP ? (size_t)(slot < Tk ? slot / a.k : slot - Tk) * a.H
                           : h_off(slot, Tk, a.I, a.Is);
   const uint16_t* asrc = (UP ? a.x16 : a.hsrc) + a_row + hi * 32;
-  const uint8_t* rec = sh ? a.shared : a.bank + (size_t)e * a.stride;
+  const uint8_t* rec = record_of(a.bank, a.stride, a.slot_of, a.shared, sh, e);
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
   const uint8_t* bb[2];
   int brow[2];
@@ -1916,7 +1927,7 @@ void gemv_up_kernel(
   uint32_t* xl = dyn;                              // [mt][xrow]
   float2* xsl = reinterpret_cast<float2*>(dyn + mt * xrow);   // [mt][G] (S1, S2)
   const size_t sec = (size_t)(inter >> 6) * G * kQ4TileBytes;
-  const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
+  const uint8_t* rec = record_of(bank, stride, ma.slot_of, shared, sh, e);
   // SPLIT: half the waves stream gate, half up (fewer registers per wave,
   // more workgroups per CU).  Else every wave streams both matrices.  The
   // waves of a matrix split the groups.
@@ -2062,7 +2073,7 @@ void gemv_down_kernel(
   uint32_t* hl = dyn;                                        // [mt][hrow]
   float2* hsl = reinterpret_cast<float2*>(dyn + mt * hrow);    // [mt][G2] (S1, S2)
   const size_t sec = (size_t)G2 * G * kQ4TileBytes;
-  const uint8_t* rec = sh ? shared : bank + (size_t)e * stride;
+  const uint8_t* rec = record_of(bank, stride, ma.slot_of, shared, sh, e);
   GemvStream<1, kGemvP> st;
   st.mat[0] = rec + kHeaderBytes + 2 * sec + (size_t)min(rb, nrb - 1) * G2 * kQ4TileBytes;
   st.gbeg = (G2 * wq) / wpr;
@@ -2452,6 +2463,7 @@ static MfmaArgs mfma_args(const LayerDev& d, int T) {
   m.bank = d.bank;
   m.stride = d.stride;
   m.shared = d.shared;
+  m.slot_of = d.slot_of;
   m.H = d.H;
   m.E = d.E;
   m.k = d.k;
@@ -2525,6 +2537,229 @@ hipError_t launch_ws_init(const LayerDev& d, hipStream_t s) {
   const size_t n = kMiscInts;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, base,
                      (int)n, 0);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- expert cache --
+// A bank larger than HBM stays in host memory; each layer keeps a bounded set
+// of records in HBM slots and reads only those (the TurboFieldfare page,
+// "Token üretim süreci": the selected expert ids are compared with a 16-slot
+// LFU cache per layer and misses are filled before the experts run; the WASTE
+// page, "RAM bütçesi ve dar performans aralığı": a bounded expert cache, and
+// "Önceden okuma ve router tahmini": the next layer's router run one residual
+// ahead prefetches its experts, which raises the demand hit rate while the
+// real router still decides).  Everything is decided on the device, so a
+// forward needs no host round trip.
+//
+// cache_plan_kernel (one workgroup): the experts of this forward (demand: the
+// bucketing's per-expert counts) or of the lookahead's prediction (prefetch)
+// are looked up in slot_of.  Missing ones take the slots that sort first by
+// (occupied, freq of the occupant, stamp, slot): free slots, then the least
+// frequently used, the least recently used among equal counts, the lowest
+// slot among equal stamps; a slot whose expert is in the current set is never
+// taken.  freq counts the forwards that selected an expert; stamps are a
+// forward clock.  The copies (expert, slot) go to a list for cache_fill_kernel.
+constexpr int kCacheThreads = 1024;
+constexpr uint32_t kFreqMax = (1u << 23) - 1;
+constexpr uint32_t kStampMask = (1u << 30) - 1;
+
+struct CacheArgs {
+  int E, S, mode;                 // mode 0: demand (offs), 1: prefetch (pred)
+  const int* offs;                // [E + 1] bucketing offsets (demand)
+  const int* pred;                // [npred] predicted expert ids (prefetch)
+  int npred;
+  uint64_t rec_bytes;             // bytes copied per record
+  int* slot_of;                   // [E]
+  int* owner;                     // [S]
+  uint32_t* freq;                 // [E]
+  uint32_t* stamp;                // [S]
+  uint32_t* pf_flag;              // [S] holds a prefetched record not used yet
+  uint32_t* clock;                // [1]
+  int* copy;                      // [2 * E] (expert, slot) of this plan
+  int* n_copy;                    // [1]
+  unsigned long long* stats;      // [kCacheStats]
+};
+
+__global__ __launch_bounds__(kCacheThreads) void cache_plan_kernel(CacheArgs c) {
+  __shared__ unsigned long long key[kCacheThreads];
+  __shared__ unsigned char s_sel[kMaxExperts];
+  __shared__ int s_rank[kMaxExperts];
+  __shared__ int s_scan[2 * kCacheThreads / 64];
+  __shared__ unsigned s_cnt[4];   // selected, hits, useful prefetches, wasted prefetches
+  const int tid = threadIdx.x;
+  const bool demand = c.mode == 0;
+  for (int e = tid; e < c.E; e += kCacheThreads) s_sel[e] = demand ? (c.offs[e + 1] > c.offs[e]) : 0;
+  if (tid < 4) s_cnt[tid] = 0;
+  __syncthreads();
+  if (!demand)
+    for (int i = tid; i < c.npred; i += kCacheThreads) {
+      const int e = c.pred[i];
+      if (e >= 0 && e < c.E) s_sel[e] = 1;
+    }
+  __syncthreads();
+  const uint32_t now = (c.clock[0] + (demand ? 1u : 0u)) & kStampMask;
+  // eviction keys, pinned slots (their expert is in the current set) last
+  {
+    unsigned long long k = ~0ull;
+    if (tid < c.S) {
+      const int o = c.owner[tid];
+      if (o < 0) {
+        k = (unsigned long long)tid;
+      } else if (!s_sel[o]) {
+        const uint32_t f = min(c.freq[o], kFreqMax);
+        k = (1ull << 63) | ((unsigned long long)f << 40) |
+            ((unsigned long long)(c.stamp[tid] & kStampMask) << 10) | (unsigned long long)tid;
+      }
+    }
+    key[tid] = k;
+  }
+  // hits and the rank of each missing expert among the missing (expert order)
+  for (int e = tid; e < kMaxExperts; e += kCacheThreads) {
+    int miss = 0;
+    if (e < c.E && s_sel[e]) {
+      const int sl = c.slot_of[e];
+      if (sl < 0) {
+        miss = 1;
+      } else {
+        atomicAdd(&s_cnt[1], 1u);
+        if (demand) {
+          c.stamp[sl] = now;
+          if (c.pf_flag[sl]) {
+            c.pf_flag[sl] = 0;
+            atomicAdd(&s_cnt[2], 1u);
+          }
+        }
+      }
+      atomicAdd(&s_cnt[0], 1u);
+      if (demand) c.freq[e] = min(c.freq[e] + 1u, kFreqMax);
+    }
+    s_rank[e] = miss;
+  }
+  __syncthreads();
+  const int n_miss = block_excl_scan<kCacheThreads>(s_rank, kMaxExperts, s_scan);
+  // bitonic sort of the 1024 keys, ascending
+  for (int k = 2; k <= kCacheThreads; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = tid ^ j;
+      if (p > tid) {
+        const unsigned long long a = key[tid], b = key[p];
+        const bool up = (tid & k) == 0;
+        if ((a > b) == up) {
+          key[tid] = b;
+          key[p] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // the r-th missing expert takes the r-th slot in key order
+  for (int e = tid; e < c.E; e += kCacheThreads) {
+    if (!s_sel[e] || c.slot_of[e] >= 0) continue;
+    const int r = s_rank[e];
+    const unsigned long long k = key[r];
+    if (k == ~0ull) continue;   // no slot left: the capacity check at set-up rules this out
+    const int v = (int)(k & 1023ull);
+    const int o = c.owner[v];
+    if (o >= 0) c.slot_of[o] = -1;
+    if (c.pf_flag[v]) atomicAdd(&s_cnt[3], 1u);
+    c.owner[v] = e;
+    c.slot_of[e] = v;
+    c.stamp[v] = now;
+    c.pf_flag[v] = demand ? 0u : 1u;
+    c.copy[2 * r] = e;
+    c.copy[2 * r + 1] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    c.n_copy[0] = n_miss;
+    if (demand) {
+      c.clock[0] = now;
+      c.stats[0] += 1;                                   // forwards
+      c.stats[1] += s_cnt[0];                            // experts selected
+      c.stats[2] += s_cnt[1];                            // demand hits
+      c.stats[3] += (unsigned long long)n_miss;          // demand misses
+      c.stats[4] += (unsigned long long)n_miss * c.rec_bytes;
+      c.stats[7] += s_cnt[2];                            // prefetched records used
+    } else {
+      c.stats[5] += (unsigned long long)n_miss;          // records prefetched
+      c.stats[6] += (unsigned long long)n_miss * c.rec_bytes;
+    }
+    c.stats[8] += s_cnt[3];                              // prefetched records evicted unused
+  }
+}
+
+// Copy the planned records: workgroup b takes chunk b % chunks of copy b / chunks.
+constexpr int kFillChunk = 65536;
+__global__ __launch_bounds__(256) void cache_fill_kernel(const uint8_t* __restrict__ src,
+                                                         uint64_t src_stride, uint8_t* __restrict__ slots,
+                                                         uint64_t stride, uint64_t rec_bytes,
+                                                         const int* __restrict__ copy,
+                                                         const int* __restrict__ n_copy, int chunks) {
+  const int r = (int)blockIdx.x / chunks, ch = (int)blockIdx.x % chunks;
+  if (r >= n_copy[0]) return;
+  const int e = copy[2 * r], v = copy[2 * r + 1];
+  const uint8_t* s = src + (size_t)e * src_stride;
+  uint8_t* d = slots + (size_t)v * stride;
+  const uint64_t beg = (uint64_t)ch * kFillChunk, end = min(rec_bytes, beg + kFillChunk);
+  for (uint64_t i = beg + threadIdx.x * 16; i < end; i += 256 * 16)
+    *reinterpret_cast<uint4*>(d + i) = ld16_nt(s + i);
+}
+
+hipError_t launch_cache_plan(const LayerDev& d, int mode, int npred, hipStream_t s) {
+  CacheArgs c{};
+  c.E = d.E;
+  c.S = d.cache_slots;
+  c.mode = mode;
+  c.offs = reinterpret_cast<const int*>(d.ws + d.L.offs);
+  c.pred = reinterpret_cast<const int*>(d.ws + d.L.pred);
+  c.npred = npred;
+  c.rec_bytes = d.rec_bytes;
+  uint8_t* cs = d.ws + d.L.cache;
+  c.slot_of = reinterpret_cast<int*>(cs + kCacheSlotOf);
+  c.owner = reinterpret_cast<int*>(cs + kCacheOwner);
+  c.freq = reinterpret_cast<uint32_t*>(cs + kCacheFreq);
+  c.stamp = reinterpret_cast<uint32_t*>(cs + kCacheStamp);
+  c.pf_flag = reinterpret_cast<uint32_t*>(cs + kCachePf);
+  c.clock = reinterpret_cast<uint32_t*>(cs + kCacheClock);
+  c.copy = reinterpret_cast<int*>(cs + (mode ? kCacheCopyP : kCacheCopyD));
+  c.n_copy = reinterpret_cast<int*>(cs + (mode ? kCacheNCopyP : kCacheNCopyD));
+  c.stats = reinterpret_cast<unsigned long long*>(cs + kCacheStatsOff);
+  hipLaunchKernelGGL(cache_plan_kernel, dim3(1), dim3(kCacheThreads), 0, s, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_fill(const LayerDev& d, int mode, int max_copies, hipStream_t s) {
+  if (max_copies <= 0) return hipSuccess;
+  const int chunks = (int)((d.rec_bytes + kFillChunk - 1) / kFillChunk);
+  uint8_t* cs = d.ws + d.L.cache;
+  hipLaunchKernelGGL(cache_fill_kernel, dim3((unsigned)(max_copies * chunks)), dim3(256), 0, s,
+                     d.cache_src, d.cache_src_stride, const_cast<uint8_t*>(d.bank), d.stride,
+                     d.rec_bytes, reinterpret_cast<const int*>(cs + (mode ? kCacheCopyP : kCacheCopyD)),
+                     reinterpret_cast<const int*>(cs + (mode ? kCacheNCopyP : kCacheNCopyD)), chunks);
+  return hipGetLastError();
+}
+
+// Empty cache: every expert absent, every slot free, counters zero.
+__global__ void cache_reset_kernel(uint8_t* cs, int E) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < E) {
+    reinterpret_cast<int*>(cs + kCacheSlotOf)[i] = -1;
+    reinterpret_cast<int*>(cs + kCacheOwner)[i] = -1;
+    reinterpret_cast<uint32_t*>(cs + kCacheFreq)[i] = 0;
+    reinterpret_cast<uint32_t*>(cs + kCacheStamp)[i] = 0;
+    reinterpret_cast<uint32_t*>(cs + kCachePf)[i] = 0;
+  }
+  if (i < kCacheStats) reinterpret_cast<unsigned long long*>(cs + kCacheStatsOff)[i] = 0;
+  if (i == 0) {
+    reinterpret_cast<uint32_t*>(cs + kCacheClock)[0] = 0;
+    reinterpret_cast<int*>(cs + kCacheNCopyD)[0] = 0;
+    reinterpret_cast<int*>(cs + kCacheNCopyP)[0] = 0;
+  }
+}
+
+hipError_t launch_cache_reset(const LayerDev& d, hipStream_t s) {
+  const int n = d.E > kCacheStats ? d.E : kCacheStats;
+  hipLaunchKernelGGL(cache_reset_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d.ws + d.L.cache, d.E);
   return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ class MoELayer:
                          _ptr(bank), record_stride, _ptr(shared), _ptr(workspace),
                          0 if workspace is None else workspace.numel())
         self._keep = (router, bank, shared, router_bias, workspace)
+        self._stride = record_stride
         self._check(self.lib.moe_set_weights(self.ctx, ctypes.byref(w), _stream()),
                     "moe_set_weights")
         return self
@@ -125,6 +126,24 @@ class MoELayer:
                     "moe_profile_read")
         return ({k: v for k, v in zip(L.PROFILE_SLOTS, list(arr)) if not k.startswith("reserved")},
                 calls.value)
+
+    def set_cache(self, n_slots, prefetch=False, slots=None):
+        """Give the layer an expert cache of n_slots records in HBM (a new
+        device tensor unless `slots` is given); 0 removes it."""
+        if n_slots and slots is None:
+            slots = torch.empty(n_slots * self._stride, dtype=torch.uint8, device=self.device)
+        self._slots = slots
+        self._check(self.lib.moe_set_cache(self.ctx, _ptr(slots) if n_slots else None,
+                                           0 if slots is None else slots.numel(), n_slots,
+                                           L.MOE_CACHE_PREFETCH if prefetch else 0, _stream()),
+                    "moe_set_cache")
+        return self
+
+    def cache_stats(self):
+        """{counter name: value} of the expert cache (moe_cache_stats)."""
+        arr = (ctypes.c_uint64 * 16)()
+        self._check(self.lib.moe_cache_stats(self.ctx, arr, 16, _stream()), "moe_cache_stats")
+        return dict(zip(L.CACHE_STATS, list(arr)))
 
     def set_path_rows(self, mfma_min_rows, wide_min_rows=None):
         if wide_min_rows is None:

@@ -1,0 +1,143 @@
+"""Banks larger than HBM: the expert cache on the GPU.
+
+A 4-layer residual stack at the decode layer's shape (hidden 2816, 128
+experts, top-8, intermediate 704, shared expert 2112), its banks in pinned
+host memory and a 16-slot cache per layer (the TurboFieldfare setting), run
+token by token with the next layer's router one residual ahead prefetching
+into the next layer's cache.  Against the same layers on resident device
+banks: every output, id and weight bitwise equal.  The cache counters (hits,
+misses, bytes, prefetches used and wasted) equal those of the plain model in
+oracle/cache_ref.py driven by the same selections and predictions."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.WORKLOADS[1]
+SH = WL.shape
+N_LAYERS = 4
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _pair(dev, layer, max_tokens, host_bank=True):
+    """(resident context, context over a copy of the bank in pinned host
+    memory or a second device bank)."""
+    import torch
+    from quantized_routed_expert_bit_amd import MoELayer
+    li = synth.LayerInputs(0, 1, layer, SH, None)
+    w = synth.upload_layer(li, dev)
+    res = MoELayer(SH.hidden, SH.n_experts, SH.top_k, SH.inter, SH.shared_inter, max_tokens,
+                   rmsnorm=True)
+    res.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
+    if host_bank:
+        bank = torch.empty(w["bank"].numel(), dtype=torch.uint8, pin_memory=True)
+        bank.copy_(w["bank"])
+    else:
+        bank = w["bank"].clone()
+    cac = MoELayer(SH.hidden, SH.n_experts, SH.top_k, SH.inter, SH.shared_inter, max_tokens,
+                   rmsnorm=True)
+    cac.set_weights(w["router"], bank, w["stride"], w["shared"], w["bias"])
+    res._w, cac._bank = w, bank
+    return res, cac
+
+
+def _model(w):
+    lay = synth.record_layout(SH.hidden, SH.inter)
+    return lambda n_slots: oracle.OracleExpertCache(SH.n_experts, n_slots, lay["end"])
+
+
+def test_cached_stack_matches_resident_bitwise_with_lfu_counts(torch_dev):
+    import torch
+    from oracle import select_topk
+    pairs = [_pair(torch_dev, l, 1) for l in range(N_LAYERS)]
+    n_slots = 16
+    for l, (_, cac) in enumerate(pairs):
+        cac.set_cache(n_slots, prefetch=l > 0)
+    models = [_model(None)(n_slots) for _ in range(N_LAYERS)]
+    n_tok = 24
+    for t in range(n_tok):
+        x = P.bf16_tensor(synth.make_hidden(0, 1, 1, SH.hidden, tag=700 + t), torch_dev).float()
+        ra, rb = x.clone(), x.clone()
+        for l in range(N_LAYERS):
+            res, cac = pairs[l]
+            nxt_r = pairs[l + 1][0] if l + 1 < N_LAYERS else None
+            nxt_c = pairs[l + 1][1] if l + 1 < N_LAYERS else None
+            if nxt_r is not None:   # the prediction the lookahead will make for layer l + 1
+                lg = nxt_r.router_logits(ra).cpu().numpy().astype(np.float64)
+                pred = select_topk(lg, SH.top_k)[0].reshape(-1)
+            _, ia, pa = res.forward(ra, return_selection=True, y=ra, residual=ra, lookahead=nxt_r)
+            _, ib, pb = cac.forward(rb, return_selection=True, y=rb, residual=rb, lookahead=nxt_c)
+            torch.cuda.synchronize()
+            assert torch.equal(ia, ib) and torch.equal(pa, pb), f"token {t} layer {l}: selection differs"
+            assert torch.equal(ra, rb), f"token {t} layer {l}: output differs"
+            models[l].demand(ia.cpu().numpy().reshape(-1))
+            if nxt_r is not None:
+                models[l + 1].prefetch(pred)
+    for l, (_, cac) in enumerate(pairs):
+        got = cac.cache_stats()
+        want = models[l].stats
+        P.log(f"layer {l}: {got}")
+        for k, v in want.items():
+            assert got[k] == v, f"layer {l} {k}: gpu {got[k]} model {v}"
+    hits = sum(m.stats["demand_hits"] for m in models[1:])
+    P.log(f"layers 1-3 demand hit rate with the lookahead prefetch: "
+          f"{hits / sum(m.stats['selected'] for m in models[1:]):.2f}; layer 0 (no prefetch): "
+          f"{models[0].stats['demand_hits'] / models[0].stats['selected']:.2f}")
+    for r, c in pairs:
+        r.close()
+        c.close()
+
+
+def test_cached_batches_and_device_backing(torch_dev):
+    """4-token batches through one layer with a cache of exactly one forward's
+    working set (32 slots), once over a pinned host bank and once over a
+    device bank: bitwise equal to the resident layer, counters equal to the
+    model's."""
+    import torch
+    for host in (True, False):
+        res, cac = _pair(torch_dev, 2, 4, host_bank=host)
+        cac.set_cache(32)
+        model = _model(None)(32)
+        for b in range(10):
+            x = P.bf16_tensor(synth.make_hidden(0, 1, 4, SH.hidden, tag=800 + b), torch_dev).float()
+            ya, ia, pa = res.forward(x, return_selection=True)
+            yb, ib, pb = cac.forward(x, return_selection=True)
+            torch.cuda.synchronize()
+            assert torch.equal(ya, yb) and torch.equal(ia, ib) and torch.equal(pa, pb)
+            model.demand(ia.cpu().numpy().reshape(-1))
+        got = cac.cache_stats()
+        assert all(got[k] == v for k, v in model.stats.items()), (got, model.stats)
+        P.log(f"batches of 4, {'host' if host else 'device'} bank: {got}")
+        res.close()
+        cac.close()
+
+
+def test_cache_refusals(torch_dev):
+    from quantized_routed_expert_bit_amd import MoEError
+    res, cac = _pair(torch_dev, 3, 4, host_bank=False)
+    for n in (31, 129):                 # below one forward's working set (4 x 8), above E
+        with pytest.raises(MoEError) as ei:
+            cac.set_cache(n)
+        assert ei.value.code == -3
+    cac.set_cache(32)
+    x = P.bf16_tensor(synth.make_hidden(0, 1, 4, SH.hidden, tag=900), torch_dev)
+    with pytest.raises(MoEError) as ei:
+        cac.forward_noalloc(x)
+    assert ei.value.code == -1
+    cac.set_weights(cac._keep[0], cac._keep[1], cac._stride, cac._keep[2])   # rebinding drops the cache
+    with pytest.raises(MoEError) as ei:
+        cac.cache_stats()
+    assert ei.value.code == -5
+    res.close()
+    cac.close()
