@@ -400,7 +400,83 @@ def run_large(args, dev, n_inputs=4):
     return out
 
 
-def run_decode(args, dev, batches=(1, 4, 16), copies=6):
+def run_cache(args, dev, decode_layers, n_slots=16, n_tokens=32):
+    """Banks larger than HBM: the decode layers as a residual stack whose banks
+    sit in pinned host memory, each layer with an n_slots-record HBM cache
+    (the TurboFieldfare setting: 16 slots for a top-8 router over 128
+    experts), run token by token.  Against the same stack on resident banks;
+    with the next layer's router one residual ahead prefetching into the next
+    layer's cache, and without."""
+    import torch
+    import synth
+    from quantized_routed_expert_bit_amd import MoELayer
+    sh = synth.WORKLOADS[1].shape
+    L = len(decode_layers)
+    res, cac = [], []
+    for mm in decode_layers:
+        w = mm._w
+        hb = torch.empty(w["bank"].numel(), dtype=torch.uint8, pin_memory=True)
+        hb.copy_(w["bank"])
+        for lst, bank in ((res, w["bank"]), (cac, hb)):
+            m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, 1, rmsnorm=True)
+            m.set_weights(w["router"], bank, w["stride"], w["shared"], w["bias"])
+            m._hb = bank
+            lst.append(m)
+    xs = [synth.bf16_tensor(synth.make_hidden(0, 1, 1, sh.hidden, tag=900 + t), dev).float()
+          for t in range(n_tokens)]
+    r = torch.empty_like(xs[0])
+    rec = synth.record_layout(sh.hidden, sh.inter)["end"]
+
+    def tok(layers, t, la):
+        r.copy_(xs[t % n_tokens])
+        for l, m in enumerate(layers):
+            m.forward(r, y=r, residual=r, lookahead=layers[l + 1] if la and l + 1 < L else None)
+
+    out = {}
+    for mode, layers, la in (("resident", res, True), ("cache_prefetch", cac, True),
+                             ("cache_no_prefetch", cac, False)):
+        if layers is cac:
+            for l, m in enumerate(layers):
+                m.set_cache(n_slots, prefetch=la and l > 0)
+        for t in range(4):
+            tok(layers, t, la)
+        torch.cuda.synchronize()
+        if layers is cac:   # count the timed tokens only
+            for l, m in enumerate(layers):
+                m.set_cache(n_slots, prefetch=la and l > 0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(n_tokens):
+            tok(layers, t, la)
+        e1.record()
+        torch.cuda.synchronize()
+        el = e0.elapsed_time(e1) * 1e-3
+        ent = {"tokens_s": round(n_tokens / el, 1), "us_per_token": round(el * 1e6 / n_tokens, 1)}
+        if layers is cac:
+            st = [m.cache_stats() for m in layers]
+            sel = sum(x["selected"] for x in st)
+            hits = sum(x["demand_hits"] for x in st)
+            moved = sum(x["demand_bytes"] + x["prefetch_bytes"] for x in st)
+            ent.update({"demand_hit_rate": round(hits / sel, 4),
+                        "hit_rate_layer0": round(st[0]["demand_hits"] / st[0]["selected"], 4),
+                        "hit_rate_layers_1_on": round(sum(x["demand_hits"] for x in st[1:]) /
+                                                      sum(x["selected"] for x in st[1:]), 4),
+                        "records_copied_per_token": round(moved / rec / n_tokens, 2),
+                        "bytes_copied_per_token": int(moved / n_tokens),
+                        "copy_GB_s": round(moved / el / 1e9, 2),
+                        "prefetched": sum(x["prefetched"] for x in st),
+                        "prefetch_used": sum(x["prefetch_used"] for x in st)})
+        out[mode] = ent
+        log(f"cache {mode}: {ent}")
+    out["setup"] = (f"{L}-layer residual stack of the decode layer (hidden {sh.hidden}, {sh.n_experts} "
+                    f"experts, top-{sh.top_k}), banks in pinned host memory, {n_slots} HBM slots per "
+                    f"layer, one token per forward, {n_tokens} tokens timed (eager, HIP events)")
+    for m in res + cac:
+        m.close()
+    return out
+
+
+def run_decode(args, dev, batches=(1, 4, 16), copies=6, keep=False):
     """The decode layer (hidden 2816, 128 experts, top-8, intermediate 704,
     shared expert 2112) at 1, 4 and 16 tokens; forwards rotate over `copies`
     layer copies (2.6 GB of weights), so each streams its experts from HBM."""
@@ -452,6 +528,8 @@ def run_decode(args, dev, batches=(1, 4, 16), copies=6):
         if T == 16:
             out["T16"]["gemv_up_roofline"]["traffic"] = measured_traffic("gemv_up_decode_T16_hbm_traffic.md")
         log(f"decode T={T}: {out[f'T{T}']}")
+    if keep:
+        return out, layers
     for mm in layers:
         mm.close()
     del layers
@@ -550,10 +628,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("all", "stack", "large", "decode", "prefill"),
+    ap.add_argument("--workload", choices=("all", "stack", "large", "decode", "prefill", "cache"),
                     default="all",
                     help="all: the stack headline plus every extra entry; stack: the headline "
-                         "only; large / decode / prefill: that workload only")
+                         "only; large / decode / prefill / cache: that workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -570,6 +648,10 @@ def main():
         return
     if args.workload == "decode":
         print(json.dumps({"decode": run_decode(args, dev)}), flush=True)
+        return
+    if args.workload == "cache":
+        dec, layers = run_decode(args, dev, batches=(1,), keep=True)
+        print(json.dumps({"expert_cache": run_cache(args, dev, layers)}), flush=True)
         return
     if args.workload == "prefill":
         print(json.dumps({"prefill": run_prefill(args, dev)}), flush=True)
@@ -608,7 +690,12 @@ def main():
     torch.cuda.empty_cache()
     if args.workload == "all":
         out["large_decode"] = run_large(args, dev)
-        out["decode"] = run_decode(args, dev)
+        out["decode"], dec_layers = run_decode(args, dev, keep=True)
+        out["expert_cache"] = run_cache(args, dev, dec_layers)
+        for mm in dec_layers:
+            mm.close()
+        del dec_layers
+        torch.cuda.empty_cache()
         out["prefill"] = run_prefill(args, dev)
         c = measure_ceilings(dev)
         c["prefill_layer_frac_of_gemm"] = round(out["prefill"]["layer_TFLOP_s"] / c["f16_gemm_TFLOP_s"], 4)
