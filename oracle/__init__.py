@@ -6,3 +6,4 @@ library never routes through it and shares no code with it.
 """
 from .moe_ref import *  # noqa: F401,F403
 from .cache_ref import *  # noqa: F401,F403
+from .rvq_ref import *  # noqa: F401,F403

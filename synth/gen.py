@@ -290,3 +290,35 @@ def gpu_bank(seed: int, cfg: int, layer: int, hidden: int, inter: int, n_records
 
 
 __all__.append("gpu_bank")
+
+
+# ---------------------------------------------------------------------------
+# 3-bit residual-VQ matrices (the WASTE page's expert codec): indices are
+# uniform random bytes; the three codebooks hold N(0, sigma_s) entries with
+# sigma = 0.02, 0.005, 0.00125 (each stage refines the one before), as fp16.
+# ---------------------------------------------------------------------------
+
+RVQ_TILE_BYTES = 1536
+_T_RVQ = 5
+
+
+def rvq_bytes(rows: int, cols: int) -> int:
+    """Bytes of a tiled RVQ matrix: three 8-bit indices per 8 weights."""
+    return (rows // 64) * (cols // 64) * RVQ_TILE_BYTES
+
+
+def make_rvq_codebooks(seed: int, tag: int = 0) -> np.ndarray:
+    """fp16 bit patterns [3, 256, 8]."""
+    rng = _rng(seed, 0, 0, _T_RVQ, 1000 + tag)
+    sig = np.array([0.02, 0.005, 0.00125])[:, None, None]
+    return (rng.standard_normal((3, 256, 8)) * sig).astype(np.float16).view(np.uint16)
+
+
+def make_rvq_matrix(seed: int, rows: int, cols: int, tag: int = 0) -> np.ndarray:
+    """Tiled RVQ matrix bytes (uniform random indices)."""
+    rng = _rng(seed, 0, 0, _T_RVQ, tag)
+    return np.frombuffer(rng.bytes(rvq_bytes(rows, cols)), dtype=np.uint8).copy()
+
+
+__all__ += ["RVQ_TILE_BYTES", "rvq_bytes", "make_rvq_codebooks", "make_rvq_matrix"]
+
