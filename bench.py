@@ -476,6 +476,54 @@ def run_cache(args, dev, decode_layers, n_slots=16, n_tokens=32):
     return out
 
 
+def run_rvq(args, dev, n_mats=16, R=4096, K=7168, copies=4, batches=(1, 2, 4, 8)):
+    """The 3-bit residual-VQ product (the WASTE page's expert codec) on the
+    large layer's gate/up shape: n_mats matrices of R x K (16 experts' gate
+    and up rows at one decode token), rotating over `copies` banks so each
+    call streams its indices from HBM.  Bytes: the indices, 3 bits per
+    weight (the 12 KB of codebooks and the per-token tables are not
+    counted)."""
+    import torch
+    import synth
+    from quantized_routed_expert_bit_amd import rvq_gemv
+    mb = synth.rvq_bytes(R, K)
+    stride = -(-mb // 4096) * 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    banks = [torch.randint(0, 256, (n_mats * stride,), dtype=torch.uint8, device=dev, generator=g)
+             for _ in range(copies)]
+    cb = torch.from_numpy(synth.make_rvq_codebooks(0).view(np.int16)).to(dev)
+    out = {}
+    for T in batches:
+        x = synth.bf16_tensor(synth.make_hidden(0, 3, T, K, tag=600), dev)
+        y = torch.empty((n_mats, T, R), dtype=torch.float32, device=dev)
+        ws = torch.empty(int(rvq_gemv.__globals__["L"].load().moe_rvq_workspace_bytes(T, K, R, n_mats)),
+                         dtype=torch.uint8, device=dev)
+        call = lambda i: rvq_gemv(x, banks[i % copies], R, cb, n_mats, stride, ws, y)  # noqa: E731
+        for i in range(args.warmup):
+            call(i)
+        torch.cuda.synchronize()
+        n = max(args.steps, 20)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        b = n_mats * mb
+        out[f"T{T}"] = {"us_per_call": round(us, 2), "index_bytes": int(b),
+                        "GB_s": round(b / (us * 1e-6) / 1e9, 1),
+                        "frac_hbm_peak": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "weights_per_s_T": round(n_mats * R * K / (us * 1e-6) / 1e12, 3)}
+        log(f"rvq T={T}: {out[f'T{T}']}")
+    out["setup"] = (f"{n_mats} matrices of {R} x {K} at 3 bits per weight ({n_mats * mb / 1e6:.0f} MB), "
+                    f"{copies} rotating copies, one call = tables + lookups + slice reduction")
+    del banks
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_decode(args, dev, batches=(1, 4, 16), copies=6, keep=False):
     """The decode layer (hidden 2816, 128 experts, top-8, intermediate 704,
     shared expert 2112) at 1, 4 and 16 tokens; forwards rotate over `copies`
@@ -628,10 +676,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("all", "stack", "large", "decode", "prefill", "cache"),
+    ap.add_argument("--workload", choices=("all", "stack", "large", "decode", "prefill", "cache", "rvq"),
                     default="all",
                     help="all: the stack headline plus every extra entry; stack: the headline "
-                         "only; large / decode / prefill / cache: that workload only")
+                         "only; large / decode / prefill / cache / rvq: that workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -648,6 +696,9 @@ def main():
         return
     if args.workload == "decode":
         print(json.dumps({"decode": run_decode(args, dev)}), flush=True)
+        return
+    if args.workload == "rvq":
+        print(json.dumps({"rvq_gemv": run_rvq(args, dev)}), flush=True)
         return
     if args.workload == "cache":
         dec, layers = run_decode(args, dev, batches=(1,), keep=True)
@@ -697,6 +748,7 @@ def main():
         del dec_layers
         torch.cuda.empty_cache()
         out["prefill"] = run_prefill(args, dev)
+        out["rvq_gemv"] = run_rvq(args, dev)
         c = measure_ceilings(dev)
         c["prefill_layer_frac_of_gemm"] = round(out["prefill"]["layer_TFLOP_s"] / c["f16_gemm_TFLOP_s"], 4)
         c["decode_T16_gemv_up_frac_of_copy"] = round(

@@ -331,6 +331,44 @@ int moe_set_cache(moe_ctx *ctx, void *slots, uint64_t slots_bytes, int32_t n_slo
                   uint32_t flags, void *stream);
 int moe_cache_stats(moe_ctx *ctx, uint64_t *out, int32_t n, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * 3-bit residual-VQ matrices (WASTE page, "Quantization ve doğruluk")
+ * ---------------------------------------------------------------------------
+ * The WASTE engine's expert codec: every run of 8 consecutive weights of a
+ * row is the sum of one 8-vector from each of three 256-entry codebooks
+ * (residual vector quantization in three stages), so a weight costs 3.00 bits
+ * (three 8-bit indices per 8 weights).  The product never rebuilds the
+ * matrix: it builds per-input-row tables of the inner products of every
+ * codebook entry with every 8-column run of x, and sums three table lookups
+ * per run of each row: the three lookups and two additions per run of 8
+ * weights that the page counts.
+ *
+ * Matrix layout: R rows by K columns (multiples of 64), (R/64) * (K/64) tiles
+ * of MOE_RVQ_TILE_BYTES in row-block-major order; byte s*512 + r*8 + j of tile
+ * (rb, g) is the stage-s index (0..255) of row rb*64 + r's run j, i.e. of its
+ * columns g*64 + 8j .. g*64 + 8j + 7.  Codebooks: fp16 [3][256][8] (stage,
+ * entry, dimension), 16-byte aligned:
+ *     W[r, 8j' + d] = C[0][i0][d] + C[1][i1][d] + C[2][i2][d]
+ * for run j' of row r with stage indices i0, i1, i2.
+ *
+ * moe_rvq_gemv: y[m][t][r] = sum_c W_m[r, c] x[t, c] for n_mats matrices at
+ * mats + m * mat_stride (16-byte aligned; mat_stride a multiple of 16 and at
+ * least one matrix when n_mats > 1), x bf16 or fp32 [T, K] (MOE_BF16 /
+ * MOE_F32, 4-byte aligned), y fp32 [n_mats][T][R] (4-byte aligned), all
+ * device memory; the per-group partial sums (fp32, summed over K groups of
+ * 256 columns in group order) live in the caller's workspace of
+ * moe_rvq_workspace_bytes (256-byte aligned); the tables are built in LDS.  Stream-ordered, no allocation, no host synchronisation; T = 0 is
+ * a no-op.  Errors: MOE_EINVAL (shapes, dtype, pointers, alignment),
+ * MOE_ENOMEM (workspace too small), MOE_EHIP.  moe_rvq_workspace_bytes
+ * returns 0 for an invalid shape (T outside 1..65535, K or R not a positive
+ * multiple of 64, n_mats < 1). */
+#define MOE_RVQ_TILE_BYTES 1536
+uint64_t moe_rvq_workspace_bytes(int32_t n_tokens, int32_t k_cols, int32_t rows, int32_t n_mats);
+int moe_rvq_gemv(const void *x, int32_t x_dtype, int32_t n_tokens, int32_t k_cols,
+                 const void *mats, uint64_t mat_stride, int32_t n_mats, int32_t rows,
+                 const void *codebooks, float *y, void *workspace, uint64_t workspace_bytes,
+                 void *stream);
+
 /* CRC-32 of n_bytes of device memory at dev_bytes (16-byte aligned), with
  * zlib's polynomial and conditioning (the record payload checksum), into
  * *crc_out (host).  Runs on the current device, ordered on `stream`, and

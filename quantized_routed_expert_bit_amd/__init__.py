@@ -8,4 +8,4 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_F_SHARED, MOE_F_RMSNORM, MOE_F_VERIFY,
                    MOE_EINVAL,
                    MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EBADRECORD, MOE_ESTATE, MOE_EHIP,
                    LIB_PATH, load, make_config)
-from .layer import MoELayer, MoEError, crc32, debug_dequant  # noqa: F401
+from .layer import MoELayer, MoEError, crc32, debug_dequant, rvq_gemv  # noqa: F401

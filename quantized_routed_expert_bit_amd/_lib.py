@@ -19,6 +19,7 @@ MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 # every function include/moe.h declares
 EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
             "moe_forward_noalloc", "moe_crc32", "moe_set_cache", "moe_cache_stats",
+            "moe_rvq_workspace_bytes", "moe_rvq_gemv",
             "moe_router_logits", "moe_set_path_rows", "moe_close", "moe_strerror",
             "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
             "moe_profile_start", "moe_profile_read")
@@ -86,6 +87,11 @@ def load() -> ctypes.CDLL:
     lib.moe_set_cache.restype = c_int
     lib.moe_cache_stats.argtypes = [c_void_p, P(c_uint64), c_int32, c_void_p]
     lib.moe_cache_stats.restype = c_int
+    lib.moe_rvq_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, c_int32]
+    lib.moe_rvq_workspace_bytes.restype = c_uint64
+    lib.moe_rvq_gemv.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_uint64, c_int32,
+                                 c_int32, c_void_p, c_void_p, c_void_p, c_uint64, c_void_p]
+    lib.moe_rvq_gemv.restype = c_int
     lib.moe_crc32.argtypes = [c_void_p, c_uint64, P(c_uint32), c_void_p]
     lib.moe_crc32.restype = c_int
     lib.moe_profile_start.argtypes = [c_void_p, c_int32]

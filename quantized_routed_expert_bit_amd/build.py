@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqreb_moe.so")
-SOURCES = ["moe_kernels.hip", "moe_host.cpp", "moe_validate.cpp"]
+SOURCES = ["moe_kernels.hip", "moe_rvq.hip", "moe_host.cpp", "moe_validate.cpp"]
 
 # Packed fp32 VALU ops are disabled on the device pass; the host pass warns
 # that it does not know the feature, which is harmless.

@@ -656,6 +656,36 @@ int moe_cache_stats(moe_ctx* ctx, uint64_t* out, int32_t n, void* stream) {
   return MOE_OK;
 }
 
+uint64_t moe_rvq_workspace_bytes(int32_t n_tokens, int32_t k_cols, int32_t rows, int32_t n_mats) {
+  if (n_tokens < 1 || n_tokens > 65535 || k_cols < 64 || k_cols % 64 || rows < 64 || rows % 64 ||
+      n_mats < 1)
+    return 0;
+  return rvq_workspace(n_tokens, k_cols, rows, n_mats);
+}
+
+int moe_rvq_gemv(const void* x, int32_t x_dtype, int32_t n_tokens, int32_t k_cols,
+                 const void* mats, uint64_t mat_stride, int32_t n_mats, int32_t rows,
+                 const void* codebooks, float* y, void* workspace, uint64_t workspace_bytes,
+                 void* stream) {
+  if (n_tokens == 0) return MOE_OK;
+  const uint64_t need = moe_rvq_workspace_bytes(n_tokens, k_cols, rows, n_mats);
+  if (need == 0 || n_tokens < 0 || (x_dtype != MOE_BF16 && x_dtype != MOE_F32)) return MOE_EINVAL;
+  if (!x || !mats || !codebooks || !y || !workspace) return MOE_EINVAL;
+  if (((uintptr_t)mats & 15) || (mat_stride & 15) ||
+      (n_mats > 1 && mat_stride < (uint64_t)(rows / 64) * (k_cols / 64) * 1536))
+    return MOE_EINVAL;
+  if (((uintptr_t)workspace & 255) || ((uintptr_t)codebooks & 15) || ((uintptr_t)x & 3) ||
+      ((uintptr_t)y & 3))
+    return MOE_EINVAL;
+  if (workspace_bytes < need) return MOE_ENOMEM;
+  const hipError_t e = launch_rvq_gemv(x, x_dtype == MOE_F32, n_tokens, k_cols,
+                                       static_cast<const uint8_t*>(mats), mat_stride, n_mats, rows,
+                                       static_cast<const uint16_t*>(codebooks), y,
+                                       static_cast<uint8_t*>(workspace),
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 int moe_crc32(const void* dev_bytes, uint64_t n_bytes, uint32_t* crc_out, void* stream) {
   if (!crc_out) return MOE_EINVAL;
   if (n_bytes == 0) {   // the CRC of no bytes

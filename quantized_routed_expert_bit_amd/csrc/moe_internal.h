@@ -140,6 +140,12 @@ hipError_t launch_cache_reset(const LayerDev& d, hipStream_t s);
 // dev_tmp holds tmp_words partial results.  Synchronizes the stream.
 hipError_t crc32_ranges(const uint8_t* base, uint64_t stride, uint64_t off, uint64_t len, int n,
                         uint32_t* dev_tmp, size_t tmp_words, uint32_t* host_out, hipStream_t s);
+// 3-bit residual-VQ products (moe_rvq.hip): workspace bytes, and the
+// tables -> lookups -> slice reduction sequence.
+size_t rvq_workspace(int T, int K, int R, int n_mats);
+hipError_t launch_rvq_gemv(const void* x, int x_f32, int T, int K, const uint8_t* mats,
+                           uint64_t mat_stride, int n_mats, int R, const uint16_t* cb, float* y,
+                           uint8_t* ws, hipStream_t s);
 // Device address of the library's static scratch array (kNoallocScratchBytes)
 // on `device`, which must be the current device; looked up once per device.
 hipError_t noalloc_scratch(int device, uint8_t** out);

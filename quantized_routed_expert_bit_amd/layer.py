@@ -164,6 +164,27 @@ class MoELayer:
             pass
 
 
+def rvq_gemv(x, mats, rows, codebooks, n_mats=1, mat_stride=0, workspace=None, y=None):
+    """y [n_mats, T, rows] = W_m x for 3-bit residual-VQ matrices (moe_rvq_gemv).
+    x: bf16 or fp32 [T, K] device tensor; mats: uint8 device tensor holding the
+    n_mats tiled matrices at mat_stride bytes; codebooks: fp16 [3, 256, 8]."""
+    lib = L.load()
+    T, K = x.shape
+    x = x.contiguous()
+    need = int(lib.moe_rvq_workspace_bytes(T, K, rows, n_mats))
+    if need == 0:
+        raise MoEError(L.MOE_EINVAL, "moe_rvq_workspace_bytes: invalid shape")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((n_mats, T, rows), dtype=torch.float32, device=x.device)
+    rc = lib.moe_rvq_gemv(_ptr(x), MoELayer._dtype(x), T, K, _ptr(mats), mat_stride, n_mats, rows,
+                          _ptr(codebooks), _ptr(y), _ptr(workspace), workspace.numel(), _stream())
+    if rc != 0:
+        raise MoEError(rc, "moe_rvq_gemv")
+    return y
+
+
 def crc32(t):
     """CRC-32 (zlib's) of a contiguous device tensor's bytes, by the library's
     GPU kernel (moe_crc32)."""

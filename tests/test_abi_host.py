@@ -150,3 +150,15 @@ def test_generator_checksum_is_zlib_crc32():
     rec2 = rec.copy()
     rec2[lay["down"] + 1000] ^= 4
     assert zlib.crc32(bytes(rec2[lay["gate"]:lay["end"]])) != crc
+
+
+def test_rvq_workspace_bytes(lib):
+    """The residual-VQ workspace holds the fp32 partial outputs of every K
+    group of 256 columns; invalid shapes size 0."""
+    T, K, R, n = 3, 7168, 4096, 16
+    ws = lib.moe_rvq_workspace_bytes(T, K, R, n)
+    assert ws % 256 == 0
+    assert ws >= (K // 256) * n * T * R * 4
+    for bad in ((1, 96, 64, 1), (1, 64, 96, 1), (1, 0, 64, 1), (1, 64, 0, 1), (-1, 64, 64, 1),
+                (1, 64, 64, 0), (65536, 64, 64, 1)):
+        assert lib.moe_rvq_workspace_bytes(*bad) == 0, bad
