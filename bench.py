@@ -616,6 +616,18 @@ def run_prefill(args, dev, copies=2):
     el, _ = timed_graph(step, n)
     kern, _ = profiled(layers, step, min(n, 8))
     us = el * 1e6 / n
+    # the same tokens as 16 sequential forwards of 128 (chunked prefill)
+    C = 128
+
+    def chunked(i):
+        mm, x, y = layers[i % copies], xs[i % copies], ys[i % copies]
+        for c in range(T // C):
+            mm.forward(x[c * C:(c + 1) * C], y=y[c * C:(c + 1) * C])
+    for i in range(2):
+        chunked(i)
+    torch.cuda.synchronize()
+    el_c, _ = timed_graph(chunked, n)
+    us_c = el_c * 1e6 / n
     m0 = layers[0]
     work = [kernel_work(c, sh, T, m0.mfma_min_rows, m0.wide_min_rows) for c in counts]
     wf = float(np.mean([w["mfma_up"][1] + w["mfma_down"][1] for w in work]))
@@ -629,6 +641,8 @@ def run_prefill(args, dev, copies=2):
            "mfma_up_roofline": roofline("mfma_up", float(np.mean([w["mfma_up"][0] for w in work])),
                                         float(np.mean([w["mfma_up"][1] for w in work])),
                                         kern["mfma_up"] * 1e3) if kern["mfma_up"] else None,
+           "chunked_16x128": {"tokens_s": round(T / (us_c * 1e-6), 1), "us_per_step": round(us_c, 2),
+                              "what": "the same 2048 tokens as 16 sequential forwards of 128"},
            "rows_per_expert": {"min": int(counts[0].min()), "median": float(np.median(counts[0])),
                                "max": int(counts[0].max())},
            "distinct_experts": float(np.mean([(c > 0).sum() for c in counts])),

@@ -169,44 +169,58 @@ def test_stack_full_layer_on_gpu_residual(torch_dev, stack, layer):
                         f"stack layer {layer}, 256 tokens", pool=pool)
 
 
-@pytest.mark.timeout(900)
-def test_stack_16_tokens_through_8_layers(torch_dev, stack):
-    """16 tokens (every 16th of the batch) through all 8 layers.
-
-    Asserted, for every layer: the layer's output, ids and weights on the
-    input the GPU's stack fed it (the 256-token forward of that layer, the
-    sampled rows), against the oracle's layer on the same input, by the same
-    rules as every other forward (ids where the gap exceeds 1e-3, y to the
-    output tolerances).
-
-    Reported: the stack end to end against the oracle's own fp64 stack.  The
-    stack amplifies any per-layer difference (the residual grows to |r| ~ 900
-    by layer 5; a relative residual drift of a few 1e-4 moves logits by a few
-    1e-2 and grows layer by layer), so r_8 is logged with the drift per layer,
-    both on the oracle's own selections and on the GPU's."""
+@pytest.fixture(scope="module")
+def stack16(stack):
+    """The stack's 256-token run without lookahead and 16 sampled tokens
+    (every 16th of the batch)."""
     r_off, ids_off, rs = _run_stack(stack, False)
-    sample = list(range(0, stack["T"], 16))
-    layers = [ol for _, ol in stack["layers"]]
+    return dict(r_off=r_off, ids_off=ids_off, rs=rs, sample=list(range(0, stack["T"], 16)))
+
+
+@pytest.mark.parametrize("l", range(8))
+def test_stack_16_tokens_layer(torch_dev, stack, stack16, l):
+    """16 tokens through all 8 layers, one layer per test: the layer's
+    output, ids and weights on the input the GPU's stack fed it (the
+    256-token forward of that layer, the sampled rows), against the oracle's
+    layer on the same input, by the same rules as every other forward (ids
+    where the gap exceeds 1e-3, y to the output tolerances)."""
+    m, ol = stack["layers"][l]
+    sample = stack16["sample"]
+    y, ids, p = m.forward(stack16["rs"][l], return_selection=True)
+    xin = oracle.rms_normalize(stack16["rs"][l].cpu().numpy()[sample].astype(np.float64))
     with P.oracle_pool() as pool:
-        for l, (m, ol) in enumerate(stack["layers"]):
-            y, ids, p = m.forward(rs[l], return_selection=True)
-            xin = oracle.rms_normalize(rs[l].cpu().numpy()[sample].astype(np.float64))
-            P.check_forward(ol, xin, y.cpu().numpy()[sample], ids.cpu().numpy()[sample],
-                            p.cpu().numpy()[sample], f"stack layer {l}, 16 tokens", pool=pool)
-        gpu_ids = [ids_off[l].cpu().numpy()[sample] for l in range(len(layers))]
-        x0 = oracle.bf16_bits_to_f64(stack["xb"])[sample]
-        own = oracle.oracle_stack(layers, x0, norm=True, pool=pool)
-        forced = oracle.oracle_stack(layers, x0, norm=True, pool=pool, force_ids=gpu_ids)
+        P.check_forward(ol, xin, y.cpu().numpy()[sample], ids.cpu().numpy()[sample],
+                        p.cpu().numpy()[sample], f"stack layer {l}, 16 tokens", pool=pool)
+
+
+@pytest.mark.parametrize("sel", ["own", "gpu"])
+def test_stack_16_tokens_end_to_end(torch_dev, stack, stack16, sel):
+    """The stack end to end against the oracle's own fp64 stack, on the
+    oracle's own selections or forced onto the GPU's.  Reported, with the
+    drift per layer; the per-layer bar is held by test_stack_16_tokens_layer.
+    The stack amplifies any per-layer difference (the residual grows to
+    |r| ~ 900 by layer 5; a relative residual drift of a few 1e-4 moves logits
+    by a few 1e-2 and grows layer by layer), so only a loose sanity bound is
+    asserted here: r_8 within 5e-2 relative (measured a few 1e-3)."""
+    sample = stack16["sample"]
+    layers = [ol for _, ol in stack["layers"]]
+    gpu_ids = [stack16["ids_off"][l].cpu().numpy()[sample] for l in range(len(layers))]
+    x0 = oracle.bf16_bits_to_f64(stack["xb"])[sample]
+    with P.oracle_pool() as pool:
+        ref = oracle.oracle_stack(layers, x0, norm=True, pool=pool,
+                                  force_ids=gpu_ids if sel == "gpu" else None)
     n_diff = 0
-    for l, lr in enumerate(own["layers"]):
-        rd = np.linalg.norm(rs[l].cpu().numpy()[sample] - lr["input"]) / np.linalg.norm(lr["input"])
+    for l, lr in enumerate(ref["layers"]):
+        rl = stack16["rs"][l].cpu().numpy()[sample]
+        rd = np.linalg.norm(rl - lr["input"]) / np.linalg.norm(lr["input"])
         diff = [(sample[i], round(float(lr["gap"][i]), 4)) for i in range(len(sample))
                 if lr["gap"][i] > P.GAP and set(gpu_ids[l][i].tolist()) != set(lr["ids"][i].tolist())]
         n_diff += len(diff)
-        P.log(f"  layer {l}: residual drift from the oracle's own stack {rd:.2e}; "
+        P.log(f"  layer {l}: residual drift from the oracle's stack ({sel} selections) {rd:.2e}; "
               f"selections that differ there (token, gap): {diff}")
-    for name, ref in (("own selections", own["out"]), ("the GPU's selections", forced["out"])):
-        err = r_off.cpu().numpy()[sample] - ref
-        P.log(f"stack end to end, oracle on {name}: r_8 rel {np.linalg.norm(err) / np.linalg.norm(ref):.3e}, "
-              f"max/rms {np.abs(err).max() / np.sqrt(np.mean(ref ** 2)):.3e}")
-    P.log(f"stack: {n_diff} token-layers select differently along the oracle's own stack")
+    err = stack16["r_off"].cpu().numpy()[sample] - ref["out"]
+    rel = np.linalg.norm(err) / np.linalg.norm(ref["out"])
+    P.log(f"stack end to end, oracle on {sel} selections: r_8 rel {rel:.3e}, "
+          f"max/rms {np.abs(err).max() / np.sqrt(np.mean(ref['out'] ** 2)):.3e}; "
+          f"{n_diff} token-layers select differently")
+    assert np.isfinite(err).all() and rel < 5e-2

@@ -344,6 +344,30 @@ def test_prefill_2048_tokens(torch_dev):
                     p.cpu().numpy(), "prefill T=2048")
 
 
+def test_prefill_chunked_sequential(torch_dev):
+    """The prefill workload as 16 sequential forwards of 128 tokens, the
+    chunked prefill the TurboFieldfare page runs ("Token üretim süreci"):
+    every chunk's tokens match the oracle (routing is per token, so the
+    chunks compute what the grouped 2048-token forward does)."""
+    import torch
+    wl = synth.WORKLOADS[2]
+    li = synth.layer_inputs(wl)
+    T, C = wl.batches[0], 128
+    m = _layer(li, torch_dev, T)
+    ol = P.oracle_layer(li)
+    xb = synth.make_hidden(0, 2, T, wl.shape.hidden)
+    x = P.bf16_tensor(xb, torch_dev)
+    y = torch.empty((T, wl.shape.hidden), dtype=torch.float32, device=torch_dev)
+    ids = torch.empty((T, wl.shape.top_k), dtype=torch.int32, device=torch_dev)
+    p = torch.empty((T, wl.shape.top_k), dtype=torch.float32, device=torch_dev)
+    for c in range(T // C):
+        yc, ic, pc = m.forward(x[c * C:(c + 1) * C], return_selection=True, y=y[c * C:(c + 1) * C])
+        ids[c * C:(c + 1) * C] = ic
+        p[c * C:(c + 1) * C] = pc
+    with P.oracle_pool() as pool:
+        P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                        p.cpu().numpy(), "prefill 16 x 128 sequential", pool=pool)
+
 def test_rmsnorm_input(torch_dev):
     """MOE_F_RMSNORM: the layer runs on x / sqrt(mean(x^2) + 1e-6)."""
     import torch
@@ -359,3 +383,24 @@ def test_rmsnorm_input(torch_dev):
     y, ids, p = m.forward(torch.from_numpy(x32).to(torch_dev), return_selection=True)
     P.check_forward(ol, oracle.rms_normalize(x32.astype(np.float64)), y.cpu().numpy(),
                     ids.cpu().numpy(), p.cpu().numpy(), "rmsnorm input")
+
+
+@pytest.mark.parametrize("scale", [2.0 ** 20, 2.0 ** -12])
+def test_rmsnorm_input_far_from_unit_scale(torch_dev, scale):
+    """fp32 inputs far outside fp16's range (2^20 times unit scale) or deep in
+    its subnormals (2^-12) are handled by MOE_F_RMSNORM, which normalizes in
+    fp32 before any fp16 staging: the layer matches the oracle on the same
+    normalized rows."""
+    import torch
+    from quantized_routed_expert_bit_amd import MoELayer
+    wl = synth.WORKLOADS[1]
+    li = synth.layer_inputs(wl)
+    sh = wl.shape
+    w = P.upload_layer(li, torch_dev)
+    m = MoELayer(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter, 16, rmsnorm=True)
+    m.set_weights(w["router"], w["bank"], w["stride"], w["shared"], w["bias"])
+    ol = P.oracle_layer(li)
+    x32 = (np.random.default_rng(9).standard_normal((16, sh.hidden)) * scale).astype(np.float32)
+    y, ids, p = m.forward(torch.from_numpy(x32).to(torch_dev), return_selection=True)
+    P.check_forward(ol, oracle.rms_normalize(x32.astype(np.float64)), y.cpu().numpy(),
+                    ids.cpu().numpy(), p.cpu().numpy(), f"rmsnorm input x{scale:g}")
