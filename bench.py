@@ -518,7 +518,7 @@ def run_rvq(args, dev, n_mats=16, R=4096, K=7168, copies=4, batches=(1, 2, 4, 8)
                         "weights_per_s_T": round(n_mats * R * K / (us * 1e-6) / 1e12, 3)}
         log(f"rvq T={T}: {out[f'T{T}']}")
     out["setup"] = (f"{n_mats} matrices of {R} x {K} at 3 bits per weight ({n_mats * mb / 1e6:.0f} MB), "
-                    f"{copies} rotating copies, one call = tables + lookups + slice reduction")
+                    f"{copies} rotating copies, one call = lookups over tables built in LDS + the K-group reduction")
     del banks
     torch.cuda.empty_cache()
     return out
@@ -575,6 +575,7 @@ def run_decode(args, dev, batches=(1, 4, 16), copies=6, keep=False):
                         "kernel_us": {k: round(v * 1e3, 3) for k, v in kern.items()}}
         if T == 16:
             out["T16"]["gemv_up_roofline"]["traffic"] = measured_traffic("gemv_up_decode_T16_hbm_traffic.md")
+            out["T16"]["gemv_down_roofline"]["traffic"] = measured_traffic("gemv_down_decode_T16_hbm_traffic.md")
         log(f"decode T={T}: {out[f'T{T}']}")
     if keep:
         return out, layers

@@ -98,7 +98,7 @@ def test_record_header_validation(lib):
 def test_record_header_fuzz(lib):
     """Random byte mutations never pass the header check unless they leave the
     header unchanged or touch only the payload checksum's value (which only
-    the payload verification can judge)."""
+    the payload verification can decide)."""
     cfg = _cfg()
     rec = synth.make_record(0, 1, 0, 9, 2816, 704)[:256].copy()
     rng = np.random.default_rng(0)
