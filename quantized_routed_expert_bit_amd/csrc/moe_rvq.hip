@@ -4,11 +4,12 @@
 // three 256-entry codebooks of 8-vectors: three 8-bit indices per 8 weights,
 // 3.00 bits per weight.  The product never rebuilds the matrix: per input row
 // x_t, partial inner-product tables
-//     tab[t][j][s][c] = <C_s[c], x_t[8j .. 8j+7]>
+//     tab_t[j][s][c] = <C_s[c], x_t[8j .. 8j+7]>
 // are built in LDS by every workgroup for the 64 columns it is working on,
-// and a row's output is the sum over its runs j of three table lookups, tab[t][j][0][i0] + tab[t][j][1][i1] +
-// tab[t][j][2][i2] (rvq_gemv_kernel): three lookups and two additions per
-// run of 8 weights, as the page counts them.  Tables are fp32 and every sum
+// and a row's output is the sum over its runs j of three table lookups,
+// tab_t[j][0][i0] + tab_t[j][1][i1] + tab_t[j][2][i2] (rvq_gemv_kernel):
+// three lookups and two additions per run of 8 weights, as the page counts
+// them.  Tables are fp32 and every sum
 // fp32; the K groups' partial sums are added in group order
 // (rvq_reduce_kernel).
 //
@@ -28,30 +29,47 @@ constexpr int kRvqTileBytes = 1536;
 constexpr int kRvqThreads = 1024;
 constexpr int kRvqRowsPerThread = 4;
 constexpr int kRvqRows = kRvqThreads * kRvqRowsPerThread;   // rows per workgroup
-constexpr int kRvqTokMax = 3;      // tokens per pass (one tile's tables: 24 KiB per token)
+constexpr int kRvqTokMax = 4;      // tokens per pass (one tile's tables: 24 KiB per token)
 constexpr int kRvqTilesPerGroup = 4;   // 64-column tiles per K group of a workgroup
 
 __device__ __forceinline__ float rvq_f16(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// The TP tokens' table values of one entry, read as one 4-, 8- or 16-byte LDS load.
+template <int TP> struct RvqVec;
+template <> struct RvqVec<1> {
+  using type = float;
+  __device__ static float at(float v, int) { return v; }
+};
+template <> struct RvqVec<2> {
+  using type = float2;
+  __device__ static float at(float2 v, int i) { return i ? v.y : v.x; }
+};
+template <> struct RvqVec<4> {
+  using type = float4;
+  __device__ static float at(float4 v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+};
+
 // Workgroup = (K group kg of up to kRvqTilesPerGroup tiles, matrix m, block
-// rb of kRvqRows rows), for the TP tokens t0 .. t0+TP-1.  Per tile the
-// workgroup builds the tile's tables for its TP tokens in LDS: thread tid
-// owns codebook entry c = tid % 256 of all three stages (in registers) and
-// runs tid / 256 and tid / 256 + 4 of the tile.  Each thread then adds, for
-// its kRvqRowsPerThread rows, three lookups per run, with the row's indices
-// loaded once per tile; after the group's last tile it writes the partial
-// outputs part[kg][m][t][r].  Work items are numbered K-group major and dealt
-// to the eight XCDs in contiguous ranges (workgroup b runs on XCD b mod 8),
-// so the workgroups that share a K group's x and indices' neighbours share an
-// L2.
+// rb of kRvqRows rows), for the TP tokens t0 .. t0+TP-1 (TP = 1, 2 or 4).
+// Per tile the workgroup builds the tile's tables in LDS, laid out
+// [run j][stage s][entry c][token], so that the TP tokens' values of one
+// entry are adjacent: thread tid owns codebook entry c = tid % 256 of all
+// three stages (in registers) and the runs tid / 256 and tid / 256 + 4 of
+// the tile.  Each thread then adds, for its kRvqRowsPerThread rows, three
+// lookups per run, each one 4-, 8- or 16-byte LDS read serving every token
+// of the pass, with the row's indices loaded once per tile; after the
+// group's last tile it writes the partial outputs part[kg][m][t][r].  Work
+// items are numbered K-group major and dealt to the eight XCDs in contiguous
+// ranges (workgroup b runs on XCD b mod 8).
 template <int TP>
 __global__ __launch_bounds__(kRvqThreads) void rvq_gemv_kernel(
     const uint8_t* __restrict__ mats, uint64_t mat_stride, int R, int K, int T, int t0,
     const void* __restrict__ x, int x_f32, const uint16_t* __restrict__ cb,
     float* __restrict__ part, int n_rb, int n_mats, int n_work, int per_xcd) {
-  extern __shared__ float lt[];   // [TP][8 runs][3][256] tables, then [TP][group columns] x
+  extern __shared__ float4 lt4[];   // [8 runs][3][256][TP] tables, then [TP][group columns] x
+  float* lt = reinterpret_cast<float*>(lt4);
   const int w = (int)(blockIdx.x & 7u) * per_xcd + (int)(blockIdx.x >> 3);
   if (w >= n_work) return;
   const int kg = w / (n_mats * n_rb), mr = w % (n_mats * n_rb);
@@ -119,27 +137,27 @@ __global__ __launch_bounds__(kRvqThreads) void rvq_gemv_kernel(
           float d = 0.f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) d = fmaf(e[st][k], xv[k], d);
-          lt[((tt * 8 + j) * 3 + st) * 256 + c] = d;
+          lt[(((j * 3 + st) * 256) + c) * TP + tt] = d;
         }
       }
     }
     __syncthreads();
-    // row by row: one row's 24 table offsets serve every token
+    // row by row: one row's 24 table offsets serve every token; the TP
+    // tokens' values of an entry are adjacent, so each lookup is one LDS read
+    using VT = typename RvqVec<TP>::type;
+    const VT* tv = reinterpret_cast<const VT*>(lt);
 #pragma unroll
     for (int q = 0; q < kRvqRowsPerThread; ++q) {
 #pragma unroll
-      for (int tt = 0; tt < TP; ++tt) {
-        const float* tl = lt + tt * 8 * 768;
-        float a_ = acc[q][tt];
+      for (int jj = 0; jj < 8; ++jj) {
+        const VT* row = tv + jj * 768;
+        const uint32_t a = (uint32_t)(ix[q][0] >> (8 * jj)) & 0xffu;
+        const uint32_t b = (uint32_t)(ix[q][1] >> (8 * jj)) & 0xffu;
+        const uint32_t cc = (uint32_t)(ix[q][2] >> (8 * jj)) & 0xffu;
+        const VT va = row[a], vb = row[256 + b], vc = row[512 + cc];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float* row = tl + jj * 768;
-          const uint32_t a = (uint32_t)(ix[q][0] >> (8 * jj)) & 0xffu;
-          const uint32_t b = (uint32_t)(ix[q][1] >> (8 * jj)) & 0xffu;
-          const uint32_t cc = (uint32_t)(ix[q][2] >> (8 * jj)) & 0xffu;
-          a_ += row[a] + row[256 + b] + row[512 + cc];
-        }
-        acc[q][tt] = a_;
+        for (int tt = 0; tt < TP; ++tt)
+          acc[q][tt] += (RvqVec<TP>::at(va, tt) + RvqVec<TP>::at(vb, tt)) + RvqVec<TP>::at(vc, tt);
       }
       // keeps the scheduler from hoisting every row's lookups at once
       __builtin_amdgcn_sched_barrier(0);
@@ -193,23 +211,23 @@ hipError_t launch_rvq_gemv(const void* x, int x_f32, int T, int K, const uint8_t
   const int n_rb = (R + kRvqRows - 1) / kRvqRows;
   const int n_work = KG * n_mats * n_rb, per_xcd = (n_work + 7) / 8;
   const int ncol = (K / 64 < kRvqTilesPerGroup ? K / 64 : kRvqTilesPerGroup) * 64;
-  // passes of up to kRvqTokMax tokens; each holds TP x (24 KiB of tables +
-  // the group's x) in LDS
+  // passes of 4, 2 or 1 tokens; each holds TP x (24 KiB of tables + the
+  // group's x) in LDS
   hipError_t e;
   static bool lds_set = false;
   if (!lds_set) {
-    const void* fns[kRvqTokMax] = {reinterpret_cast<const void*>(rvq_gemv_kernel<1>),
-                                   reinterpret_cast<const void*>(rvq_gemv_kernel<2>),
-                                   reinterpret_cast<const void*>(rvq_gemv_kernel<3>)};
-    for (int i = 0; i < kRvqTokMax; ++i) {
+    const void* fns[3] = {reinterpret_cast<const void*>(rvq_gemv_kernel<1>),
+                          reinterpret_cast<const void*>(rvq_gemv_kernel<2>),
+                          reinterpret_cast<const void*>(rvq_gemv_kernel<4>)};
+    for (int i = 0; i < 3; ++i) {
       e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (i + 1) * (8 * 768 + kRvqTilesPerGroup * 64) * 4);
+                              (1 << i) * (8 * 768 + kRvqTilesPerGroup * 64) * 4);
       if (e != hipSuccess) return e;
     }
     lds_set = true;
   }
-  for (int t0 = 0; t0 < T; t0 += kRvqTokMax) {
-    const int tp = T - t0 < kRvqTokMax ? T - t0 : kRvqTokMax;
+  for (int t0 = 0; t0 < T;) {
+    const int tp = T - t0 >= 4 ? 4 : T - t0 >= 2 ? 2 : 1;
     const size_t lds = (size_t)tp * (8 * 768 + ncol) * 4;
     const dim3 grid(per_xcd * 8), block(kRvqThreads);
     if (tp == 1)
@@ -219,10 +237,11 @@ hipError_t launch_rvq_gemv(const void* x, int x_f32, int T, int K, const uint8_t
       hipLaunchKernelGGL(rvq_gemv_kernel<2>, grid, block, lds, s, mats, mat_stride, R, K, T, t0, x,
                          x_f32, cb, part, n_rb, n_mats, n_work, per_xcd);
     else
-      hipLaunchKernelGGL(rvq_gemv_kernel<3>, grid, block, lds, s, mats, mat_stride, R, K, T, t0, x,
+      hipLaunchKernelGGL(rvq_gemv_kernel<4>, grid, block, lds, s, mats, mat_stride, R, K, T, t0, x,
                          x_f32, cb, part, n_rb, n_mats, n_work, per_xcd);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    t0 += tp;
   }
   const size_t n = (size_t)n_mats * T * R;
   hipLaunchKernelGGL(rvq_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, KG, n, y);
