@@ -189,10 +189,11 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
   d.rmsnorm = (cfg->flags & MOE_F_RMSNORM) ? 1 : 0;
   d.max_tokens = cfg->max_tokens;
   // Experts with 2 or 3 rows stream at hidden 2816 (16 tokens: 77.7 against
-  // 83 us per forward when they take 32-row matrix-core tiles) but take the
-  // tiles at hidden 7168, where each tile wave's K chain is long (8 tokens:
-  // 501 against 551 us; 64 tokens: 2218 against 3040 us).
-  d.mfma_min_rows = cfg->hidden >= 4096 ? 2 : 4;
+  // 83 us per forward when they take 32-row matrix-core tiles).  At hidden
+  // 7168 the streaming path (fp16 token rows, one product per row) beats the
+  // tiles for 2-row experts: 64 tokens 2003 against 2165 us per forward
+  // (3 or more rows on the tiles), the 256-token stack 7.79 against 7.97 ms.
+  d.mfma_min_rows = cfg->hidden >= 4096 ? 3 : 4;
   d.wide_min_rows = 32;
   d.L = ws_layout(*cfg);
   if (hipSetDevice(cfg->device) != hipSuccess ||
