@@ -184,7 +184,7 @@ int moe_open(const moe_config *cfg, moe_ctx **out);
 int moe_set_weights(moe_ctx *ctx, const moe_weights *w, void *stream);
 
 /* Run the layer on T = n_tokens rows of x (x_dtype MOE_BF16 or MOE_F32,
- * row-major [T, H]): the "generate" step of the engine API, one layer of it
+ * row-major [T, H], 16-byte aligned): the "generate" step of the engine API, one layer of it
  * (router on the GPU from resident weights, top-k, routed and shared experts,
  * combine: TurboFieldfare page, "Token üretim süreci").  Two arguments go
  * beyond the layer itself: `residual` fuses the residual add of a stack, and
@@ -199,9 +199,9 @@ int moe_set_weights(moe_ctx *ctx, const moe_weights *w, void *stream);
  * context of the same hidden size and flags with weights bound, its router also
  * runs on this x ("one residual ahead") and its next forward orders expert work by
  * that prediction; the selected experts and every output are unchanged by it.
- * T = 0 is a no-op.  Errors: MOE_EINVAL (null x/y, T < 0 or > max_tokens, bad
- * dtype, mismatched lookahead context), MOE_ESTATE (no weights), MOE_EHIP
- * (launch failure). */
+ * T = 0 is a no-op.  Errors: MOE_EINVAL (null x/y, misaligned x, T < 0 or >
+ * max_tokens, bad dtype, mismatched lookahead context), MOE_ESTATE (no
+ * weights), MOE_EHIP (launch failure). */
 int moe_forward(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_tokens,
                 float *y, const float *residual, int32_t *ids_out, float *p_out,
                 moe_ctx *lookahead_next, void *stream);
@@ -357,9 +357,10 @@ int moe_cache_stats(moe_ctx *ctx, uint64_t *out, int32_t n, void *stream);
  * MOE_F32, 4-byte aligned), y fp32 [n_mats][T][R] (4-byte aligned), all
  * device memory; the per-group partial sums (fp32, summed over K groups of
  * 256 columns in group order) live in the caller's workspace of
- * moe_rvq_workspace_bytes (256-byte aligned); the tables are built in LDS.  Stream-ordered, no allocation, no host synchronisation; T = 0 is
- * a no-op.  Errors: MOE_EINVAL (shapes, dtype, pointers, alignment),
- * MOE_ENOMEM (workspace too small), MOE_EHIP.  moe_rvq_workspace_bytes
+ * moe_rvq_workspace_bytes (256-byte aligned); the tables are built in LDS.
+ * Stream-ordered, no allocation, no host synchronisation; T = 0 is a no-op.
+ * Errors: MOE_EINVAL (shapes, dtype, pointers, alignment), MOE_ENOMEM
+ * (workspace too small), MOE_EHIP.  moe_rvq_workspace_bytes
  * returns 0 for an invalid shape (T outside 1..65535, K or R not a positive
  * multiple of 64, n_mats < 1). */
 #define MOE_RVQ_TILE_BYTES 1536

@@ -332,6 +332,9 @@ static int check_forward(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n
   if (n_tokens < 0 || n_tokens > ctx->cfg.max_tokens)
     return fail(ctx, MOE_EINVAL, "n_tokens %d outside [0, %d]", n_tokens, ctx->cfg.max_tokens);
   if (n_tokens > 0 && (!x || !out)) return fail(ctx, MOE_EINVAL, "x and output must be non-NULL");
+  // the kernels read x rows in 16-byte pieces (rows are H * 2 or H * 4 bytes,
+  // multiples of 128, so every row is then aligned as well)
+  if (n_tokens > 0 && ((uintptr_t)x & 15)) return fail(ctx, MOE_EINVAL, "x must be 16-byte aligned");
   return MOE_OK;
 }
 
@@ -382,11 +385,16 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
   // The next layer's router on this input ("one residual ahead"): its
   // prediction orders that layer's work and, with a cache there, prefetches
   // its experts on that context's copy stream while this layer computes.
-  // It reads x before the combine writes y, so y may alias x.
-  if (next) {
+  // It reads x before the combine writes y, so y may alias x.  Without a
+  // prefetch to start it runs after this layer's streaming launches, where
+  // the main stream waits for the matrix-core stream anyway, instead of
+  // ahead of the experts (the stack: about 40 us per layer off the critical
+  // path).
+  const bool la_early = next && next->d.slot_of && (next->cache_flags & MOE_CACHE_PREFETCH);
+  if (la_early) {
     e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
-    if (next->d.slot_of && (next->cache_flags & MOE_CACHE_PREFETCH)) {
+    {
       const int nmax = n_tokens * next->d.k < next->d.E ? n_tokens * next->d.k : next->d.E;
       if ((e = hipEventRecord(next->pf_done, s)) != hipSuccess ||
           (e = hipStreamWaitEvent(next->copy, next->pf_done, 0)) != hipSuccess ||
@@ -427,6 +435,10 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
   e = launch_gemv_down(d, n_tokens, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "streaming down launch");
   mark(2, 1, s);
+  if (next && !la_early) {
+    e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
+  }
   if (mf) {
     if ((e = hipStreamWaitEvent(s, ctx->join, 0)) != hipSuccess)
       return hip_fail(ctx, e, "joining the matrix-core stream");

@@ -2165,27 +2165,45 @@ constexpr float kRmsEps = 1e-6f;
 
 // xn[t] = x[t] / sqrt(mean(x[t]^2) + eps), fp32; one workgroup per token, the
 // sum of squares reduced in a fixed order (deterministic).
+__device__ __forceinline__ float4 rms_load4(const void* x, int x_f32, size_t i4) {
+  if (x_f32) return static_cast<const float4*>(x)[i4];
+  const uint2 w = static_cast<const uint2*>(x)[i4];   // four bf16
+  return make_float4(bf16f((uint16_t)(w.x & 0xffffu)), bf16f((uint16_t)(w.x >> 16)),
+                     bf16f((uint16_t)(w.y & 0xffffu)), bf16f((uint16_t)(w.y >> 16)));
+}
+// One workgroup per token, one pass over x: each thread keeps its (at most
+// 16) four-element pieces of the row in registers (hidden <= 16384), the
+// sum of squares is reduced per wave and then over the four waves, and the
+// scaled row is written from the registers.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x, int x_f32, int H,
                                                       float* __restrict__ xn) {
-  __shared__ float red[256];
+  constexpr int kPer = 16;
+  __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
-  const float* xf = static_cast<const float*>(x) + (size_t)t * H;
-  const uint16_t* xb = static_cast<const uint16_t*>(x) + (size_t)t * H;
+  const int n4 = H >> 2;
+  const size_t base = (size_t)t * n4;
+  float4 v[kPer];
   float ss = 0.f;
-  for (int c = tid; c < H; c += 256) {
-    const float v = x_f32 ? xf[c] : bf16f(xb[c]);
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = tid + r * 256;
+    if (i < n4) {
+      v[r] = rms_load4(x, x_f32, base + i);
+      ss = fmaf(v[r].x, v[r].x, ss);
+      ss = fmaf(v[r].y, v[r].y, ss);
+      ss = fmaf(v[r].z, v[r].z, ss);
+      ss = fmaf(v[r].w, v[r].w, ss);
+    }
   }
-  red[tid] = ss;
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float inv = 1.f / sqrtf(red[0] / (float)H + kRmsEps);
-  for (int c = tid; c < H; c += 256) {
-    const float v = x_f32 ? xf[c] : bf16f(xb[c]);
-    xn[(size_t)t * H + c] = v * inv;
+  const float inv = 1.f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + kRmsEps);
+  float4* out = reinterpret_cast<float4*>(xn) + base;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = tid + r * 256;
+    if (i < n4) out[i] = make_float4(v[r].x * inv, v[r].y * inv, v[r].z * inv, v[r].w * inv);
   }
 }
 

@@ -275,6 +275,11 @@ def test_error_paths(torch_dev):
     assert ei.value.code == -1                                     # T > max_tokens
     y = torch.full((0, 512), 7.0, device=torch_dev)
     m.forward(x[:0], y=y)                                          # T = 0: no-op
+    xm = torch.empty(4 * 512 + 8, dtype=x.dtype, device=torch_dev)[2:2 + 4 * 512].view(4, 512)
+    xm.copy_(x)
+    with pytest.raises(MoEError) as ei:
+        m.forward(xm)
+    assert ei.value.code == -1                                     # x not 16-byte aligned
     with pytest.raises(MoEError) as ei:
         m.set_weights(w["router"], w["bank"], w["stride"], shared=w["bank"][:4096])
     assert ei.value.code == -1                                     # shared without the flag
