@@ -259,6 +259,12 @@ int moe_set_path_rows(moe_ctx *ctx, int32_t mfma_min_rows, int32_t wide_min_rows
  * Errors: MOE_EINVAL, MOE_EHIP. */
 #define MOE_PROFILE_SLOTS 8
 int moe_profile_start(moe_ctx *ctx, int32_t max_calls);
+/* moe_profile_start for the slots whose bit is set in slot_mask only (bit i =
+ * slot i): the others record no events, so a timed region carries event pairs
+ * only around the kernels it measures (moe_profile_read gives 0 for them).
+ * moe_profile_start profiles every slot.  Errors: MOE_EINVAL (also for a
+ * mask of 0 or with bits past MOE_PROFILE_SLOTS), MOE_EHIP. */
+int moe_profile_start_slots(moe_ctx *ctx, int32_t max_calls, uint32_t slot_mask);
 int moe_profile_read(moe_ctx *ctx, float *avg_ms, int32_t *n_calls, int32_t n_slots);
 
 /* Free the context (NULL is a no-op): the "close" step of the engine API

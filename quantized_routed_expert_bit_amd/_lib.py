@@ -22,8 +22,8 @@ EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
             "moe_rvq_workspace_bytes", "moe_rvq_gemv",
             "moe_router_logits", "moe_set_path_rows", "moe_close", "moe_strerror",
             "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
-            "moe_profile_start", "moe_profile_read")
-# kernel timing slots of moe_profile_read (the last two are reserved)
+            "moe_profile_start", "moe_profile_start_slots", "moe_profile_read")
+# kernel timing slots of moe_profile_read (the last one is reserved)
 PROFILE_SLOTS = ("router", "gemv_up", "gemv_down", "mfma_up", "mfma_down", "combine",
                  "cache", "reserved7")
 MOE_CACHE_PREFETCH = 1
@@ -96,6 +96,8 @@ def load() -> ctypes.CDLL:
     lib.moe_crc32.restype = c_int
     lib.moe_profile_start.argtypes = [c_void_p, c_int32]
     lib.moe_profile_start.restype = c_int
+    lib.moe_profile_start_slots.argtypes = [c_void_p, c_int32, c_uint32]
+    lib.moe_profile_start_slots.restype = c_int
     lib.moe_profile_read.argtypes = [c_void_p, P(c_float), P(c_int32), c_int32]
     lib.moe_profile_read.restype = c_int
     _lib = lib

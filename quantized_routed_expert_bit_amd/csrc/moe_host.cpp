@@ -23,6 +23,7 @@ struct moe_ctx {
   std::vector<hipEvent_t> ev;
   std::vector<uint8_t> launched;  // [call][slot]
   int prof_max = 0, prof_calls = 0;
+  uint32_t prof_mask = 0xffu;   // slots that get event pairs
   // matrix-core work runs on this stream, forked from and joined back into the
   // caller's stream with two events (created at open, default priority)
   hipStream_t side = nullptr;
@@ -350,7 +351,7 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
   const bool prof = ctx->prof_calls < ctx->prof_max && cap == hipStreamCaptureStatusNone;
   const int call = ctx->prof_calls;
   auto mark = [&](int slot, int end, hipStream_t st) {
-    if (!prof) return;
+    if (!prof || !((ctx->prof_mask >> slot) & 1u)) return;
     (void)hipEventRecord(ctx->ev[((size_t)call * MOE_PROFILE_SLOTS + slot) * 2 + end], st);
     if (end) ctx->launched[(size_t)call * MOE_PROFILE_SLOTS + slot] = 1;
   };
@@ -498,8 +499,15 @@ int moe_forward_noalloc(moe_ctx* ctx, const void* x, int32_t x_dtype, int32_t n_
 }
 
 int moe_profile_start(moe_ctx* ctx, int32_t max_calls) {
-  if (!ctx || max_calls < 1 || max_calls > 100000) return MOE_EINVAL;
+  return moe_profile_start_slots(ctx, max_calls, 0xffu);
+}
+
+int moe_profile_start_slots(moe_ctx* ctx, int32_t max_calls, uint32_t slot_mask) {
+  if (!ctx || max_calls < 1 || max_calls > 100000 || slot_mask == 0 ||
+      (slot_mask >> MOE_PROFILE_SLOTS))
+    return MOE_EINVAL;
   prof_clear(ctx);
+  ctx->prof_mask = slot_mask;
   ctx->ev.resize((size_t)max_calls * MOE_PROFILE_SLOTS * 2);
   for (auto& e : ctx->ev) {
     // timing-only events: no system-scope fence (cache writeback and

@@ -2320,6 +2320,10 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   int tpw = 4096 / d.Epad;
   if (tpw < 1) tpw = 1;
   if (tpw > kRouterTokMax) tpw = kRouterTokMax;
+  // batches the matrix-core router takes (and a separate bucketing pass
+  // follows anyway): at least T / 128 workgroups, so the partial logits load
+  // on enough CUs (256 tokens x 512 experts: 32 -> 128 workgroups, 23 -> 15 us)
+  if (T >= kRmTok && tpw > T / 128) tpw = T / 128 > 1 ? T / 128 : 1;
   const int n_wg = (T + tpw - 1) / tpw;
   // a 16-lane group per token where the logits fit 8 per lane and the k
   // winners fit the group's lanes; else the whole wave

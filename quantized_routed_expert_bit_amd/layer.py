@@ -114,8 +114,17 @@ class MoELayer:
                                                _stream()), "moe_router_logits")
         return out
 
-    def profile_start(self, max_calls):
-        self._check(self.lib.moe_profile_start(self.ctx, max_calls), "moe_profile_start")
+    def profile_start(self, max_calls, slots=None):
+        """Kernel timing for the next max_calls forwards: every slot, or only
+        the named ones (L.PROFILE_SLOTS names)."""
+        if slots is None:
+            self._check(self.lib.moe_profile_start(self.ctx, max_calls), "moe_profile_start")
+            return
+        mask = 0
+        for n in slots:
+            mask |= 1 << L.PROFILE_SLOTS.index(n)
+        self._check(self.lib.moe_profile_start_slots(self.ctx, max_calls, mask),
+                    "moe_profile_start_slots")
 
     def profile_read(self):
         """-> ({slot name: average ms per launch}, number of profiled forwards)."""

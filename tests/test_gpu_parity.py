@@ -285,6 +285,27 @@ def test_error_paths(torch_dev):
     assert ei.value.code == -1                                     # shared without the flag
 
 
+def test_profile_slot_mask(torch_dev):
+    """Kernel timing restricted to some slots records only those."""
+    wl = synth.WORKLOADS[1]
+    li = synth.layer_inputs(wl)
+    m = _layer(li, torch_dev, 16)
+    x = P.bf16_tensor(synth.make_hidden(0, 1, 16, 2816, tag=9), torch_dev)
+    m.profile_start(4, ("gemv_up", "combine"))
+    for _ in range(3):
+        m.forward(x)
+    avg, calls = m.profile_read()
+    assert calls == 3
+    assert avg["gemv_up"] > 0 and avg["combine"] > 0
+    assert avg["router"] == 0 and avg["gemv_down"] == 0
+    m.profile_start(4)
+    m.forward(x)
+    avg, _ = m.profile_read()
+    assert avg["router"] > 0 and avg["gemv_down"] > 0
+    assert m.lib.moe_profile_start_slots(m.ctx, 4, 0) == -1         # empty mask
+    assert m.lib.moe_profile_start_slots(m.ctx, 4, 1 << 8) == -1    # no such slot
+
+
 @pytest.mark.parametrize("cfg,min_rows,wide_rows", [(0, 1, 1), (1, 1, 1), (0, 1, 64), (1, 1, 64),
                                                     (1, 4, 64), (1, 2, 8)])
 def test_layer_parity_matrix_core(torch_dev, cfg, min_rows, wide_rows):
