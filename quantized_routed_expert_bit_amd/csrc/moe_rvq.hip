@@ -80,6 +80,11 @@ __global__ __launch_bounds__(kRvqThreads) void rvq_gemv_kernel(
   const int ncol = (g1 - g0) * 64;
   float* xs = lt + TP * 8 * 768;   // [TP][ncol]
   for (int i = tid; i < TP * ncol; i += kRvqThreads) {
+    // a pass of 4 may carry 3 tokens (a fourth pass slot of zeros, not written)
+    if (t0 + i / ncol >= T) {
+      xs[i] = 0.f;
+      continue;
+    }
     const size_t src = (size_t)(t0 + i / ncol) * K + (size_t)g0 * 64 + i % ncol;
     xs[i] = x_f32 ? static_cast<const float*>(x)[src]
                   : __builtin_bit_cast(float, (uint32_t)static_cast<const uint16_t*>(x)[src] << 16);
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(kRvqThreads) void rvq_gemv_kernel(
 #pragma unroll
     for (int q = 0; q < kRvqRowsPerThread; ++q) {
       const int r = rb * kRvqRows + q * kRvqThreads + tid;
-      if (r < R) part[(((size_t)kg * n_mats + m) * T + t0 + tt) * R + r] = acc[q][tt];
+      if (r < R && t0 + tt < T) part[(((size_t)kg * n_mats + m) * T + t0 + tt) * R + r] = acc[q][tt];
     }
   }
 }
@@ -227,7 +232,9 @@ hipError_t launch_rvq_gemv(const void* x, int x_f32, int T, int K, const uint8_t
     lds_set = true;
   }
   for (int t0 = 0; t0 < T;) {
-    const int tp = T - t0 >= 4 ? 4 : T - t0 >= 2 ? 2 : 1;
+    // passes of 4 tokens (3 remaining run as a pass of 4: one 4-token pass
+    // costs less than passes of 2 and 1), then 2, then 1
+    const int tp = T - t0 >= 3 ? 4 : T - t0 >= 2 ? 2 : 1;
     const size_t lds = (size_t)tp * (8 * 768 + ncol) * 4;
     const dim3 grid(per_xcd * 8), block(kRvqThreads);
     if (tp == 1)
@@ -241,7 +248,7 @@ hipError_t launch_rvq_gemv(const void* x, int x_f32, int T, int K, const uint8_t
                          x_f32, cb, part, n_rb, n_mats, n_work, per_xcd);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    t0 += tp;
+    t0 += tp;   // (may pass T: the last pass of 4 carried 3 tokens)
   }
   const size_t n = (size_t)n_mats * T * R;
   hipLaunchKernelGGL(rvq_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, KG, n, y);

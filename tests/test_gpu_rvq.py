@@ -1,9 +1,9 @@
 """The 3-bit residual-VQ product on the GPU (tables of partial inner
 products, three lookups per 8-weight run) against the oracle, which
 reconstructs the matrix and multiplies in fp64.  Shapes cover one tile, a
-row count past a workgroup's 1024 rows with a half K slice at the end,
-several matrices at a stride, more tokens than one pass holds, fp32 input,
-and the large layer's gate/up and down shapes.
+row count past a workgroup's rows with a short last K group, several
+matrices at a stride, every kind of token pass (1, 2, 4, and 4 carrying 3),
+fp32 input, and the large layer's gate/up and the decode layer's down shapes.
 
 Tolerance: the GPU's tables and sums are fp32 (x converts exactly, codebook
 entries are fp16, products and sums round once each); with K/8 runs of three
@@ -29,10 +29,13 @@ def torch_dev():
 
 CASES = [
     dict(R=64, K=64, T=1, n=1, f32=False),
-    dict(R=1088, K=192, T=2, n=3, f32=False),     # ragged row block, half last K slice
-    dict(R=320, K=640, T=5, n=2, f32=True),       # two token passes (3 + 2), fp32 input
+    dict(R=1088, K=192, T=2, n=3, f32=False),     # ragged row block, a group of 3 tiles
+    dict(R=320, K=640, T=5, n=2, f32=True),       # passes of 4 and 1 tokens, fp32 input
     dict(R=2816, K=704, T=4, n=1, f32=False),     # the decode layer's down shape
     dict(R=4096, K=7168, T=1, n=2, f32=False),    # the large layer's gate+up rows
+    dict(R=192, K=256, T=3, n=1, f32=False),      # 3 tokens: one pass of 4 with a zero slot
+    dict(R=128, K=320, T=6, n=2, f32=True),       # passes of 4 and 2
+    dict(R=64, K=128, T=7, n=1, f32=False),       # passes of 4 and 4 (the second with 3)
 ]
 
 
