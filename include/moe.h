@@ -368,7 +368,8 @@ int moe_cache_stats(moe_ctx *ctx, uint64_t *out, int32_t n, void *stream);
  * Errors: MOE_EINVAL (shapes, dtype, pointers, alignment), MOE_ENOMEM
  * (workspace too small), MOE_EHIP.  moe_rvq_workspace_bytes
  * returns 0 for an invalid shape (T outside 1..65535, K or R not a positive
- * multiple of 64, n_mats < 1). */
+ * multiple of 64, n_mats < 1, more than 2^31 outputs n_mats * T * R, or more
+ * than 2^20 work items of 256 columns by 4096 rows). */
 #define MOE_RVQ_TILE_BYTES 1536
 uint64_t moe_rvq_workspace_bytes(int32_t n_tokens, int32_t k_cols, int32_t rows, int32_t n_mats);
 int moe_rvq_gemv(const void *x, int32_t x_dtype, int32_t n_tokens, int32_t k_cols,

@@ -681,7 +681,7 @@ uint64_t moe_rvq_workspace_bytes(int32_t n_tokens, int32_t k_cols, int32_t rows,
   if (n_tokens < 1 || n_tokens > 65535 || k_cols < 64 || k_cols % 64 || rows < 64 || rows % 64 ||
       n_mats < 1)
     return 0;
-  return rvq_workspace(n_tokens, k_cols, rows, n_mats);
+  return rvq_workspace(n_tokens, k_cols, rows, n_mats);   // 0 past the launch limits
 }
 
 int moe_rvq_gemv(const void* x, int32_t x_dtype, int32_t n_tokens, int32_t k_cols,

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace qreb {
@@ -205,6 +207,11 @@ static int rvq_groups(int K) {
 }
 
 size_t rvq_workspace(int T, int K, int R, int n_mats) {
+  // launch limits: at most 2^20 workgroups and 2^31 outputs
+  const uint64_t n_rb = ((uint64_t)R + kRvqRows - 1) / kRvqRows;
+  if ((uint64_t)rvq_groups(K) * (uint64_t)n_mats * n_rb > (1u << 20) ||
+      (uint64_t)n_mats * (uint64_t)T * (uint64_t)R > (1ull << 31))
+    return 0;
   return rvq_al((size_t)rvq_groups(K) * n_mats * T * R * 4);
 }
 
@@ -218,18 +225,26 @@ hipError_t launch_rvq_gemv(const void* x, int x_f32, int T, int K, const uint8_t
   const int ncol = (K / 64 < kRvqTilesPerGroup ? K / 64 : kRvqTilesPerGroup) * 64;
   // passes of 4, 2 or 1 tokens; each holds TP x (24 KiB of tables + the
   // group's x) in LDS
+  // the LDS limit of the 2- and 4-token kernels, once per device
   hipError_t e;
-  static bool lds_set = false;
-  if (!lds_set) {
-    const void* fns[3] = {reinterpret_cast<const void*>(rvq_gemv_kernel<1>),
-                          reinterpret_cast<const void*>(rvq_gemv_kernel<2>),
-                          reinterpret_cast<const void*>(rvq_gemv_kernel<4>)};
-    for (int i = 0; i < 3; ++i) {
-      e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (1 << i) * (8 * 768 + kRvqTilesPerGroup * 64) * 4);
-      if (e != hipSuccess) return e;
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  {
+    static std::mutex mu;
+    static bool lds_set[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!lds_set[dev]) {
+      const void* fns[3] = {reinterpret_cast<const void*>(rvq_gemv_kernel<1>),
+                            reinterpret_cast<const void*>(rvq_gemv_kernel<2>),
+                            reinterpret_cast<const void*>(rvq_gemv_kernel<4>)};
+      for (int i = 0; i < 3; ++i) {
+        e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (1 << i) * (8 * 768 + kRvqTilesPerGroup * 64) * 4);
+        if (e != hipSuccess) return e;
+      }
+      lds_set[dev] = true;
     }
-    lds_set = true;
   }
   for (int t0 = 0; t0 < T;) {
     // passes of 4 tokens (3 remaining run as a pass of 4: one 4-token pass

@@ -160,5 +160,6 @@ def test_rvq_workspace_bytes(lib):
     assert ws % 256 == 0
     assert ws >= (K // 256) * n * T * R * 4
     for bad in ((1, 96, 64, 1), (1, 64, 96, 1), (1, 0, 64, 1), (1, 64, 0, 1), (-1, 64, 64, 1),
-                (1, 64, 64, 0), (65536, 64, 64, 1)):
+                (1, 64, 64, 0), (65536, 64, 64, 1), (64, 64, 1 << 20, 1 << 12),
+                (1, 1 << 24, 1 << 14, 1 << 10)):
         assert lib.moe_rvq_workspace_bytes(*bad) == 0, bad
