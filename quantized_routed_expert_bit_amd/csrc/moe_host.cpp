@@ -631,6 +631,7 @@ int moe_set_cache(moe_ctx* ctx, void* slots, uint64_t slots_bytes, int32_t n_slo
     d.slot_of = nullptr;
     d.cache_src = nullptr;
     d.cache_slots = 0;
+    ctx->cache_flags = 0;
     return MOE_OK;
   }
   const int need = ctx->cfg.max_tokens * d.k < d.E ? ctx->cfg.max_tokens * d.k : d.E;
@@ -647,9 +648,14 @@ int moe_set_cache(moe_ctx* ctx, void* slots, uint64_t slots_bytes, int32_t n_slo
     (void)hipGetLastError();
     return fail(ctx, MOE_EINVAL, "slots must be device memory");
   }
-  if (!ctx->copy && ((e = hipStreamCreateWithFlags(&ctx->copy, hipStreamNonBlocking)) != hipSuccess ||
-                     (e = hipEventCreateWithFlags(&ctx->pf_done, hipEventDisableTiming)) != hipSuccess))
+  if (!ctx->copy && (e = hipStreamCreateWithFlags(&ctx->copy, hipStreamNonBlocking)) != hipSuccess) {
+    ctx->copy = nullptr;
     return hip_fail(ctx, e, "creating the prefetch stream");
+  }
+  if (!ctx->pf_done && (e = hipEventCreateWithFlags(&ctx->pf_done, hipEventDisableTiming)) != hipSuccess) {
+    ctx->pf_done = nullptr;
+    return hip_fail(ctx, e, "creating the prefetch event");
+  }
   d.cache_src = src;
   d.cache_src_stride = d.stride;
   d.bank = static_cast<const uint8_t*>(slots);
