@@ -107,11 +107,38 @@ def roofline(kernel, bytes_, flops, us):
             "flops_per_launch": int(flops), "avg_launch_us": round(us, 3)}
 
 
+def _code_only(text):
+    """C/C++ source without its comments and blank lines, trailing blanks
+    stripped (string and character literals kept whole), so that a change to
+    the comments alone does not count as a change of the kernels."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_sha256():
+    """Hash of the kernel sources' code (comments excluded)."""
     h = hashlib.sha256()
     for f in ("moe_kernels.hip", "moe_internal.h"):
-        with open(os.path.join(ROOT, "quantized_routed_expert_bit_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_routed_expert_bit_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -3,10 +3,11 @@
 // Layer definition and record format: include/moe.h.  Kernels, in forward order:
 //   rmsnorm_kernel        optional per-token RMS normalization (stacked layers).
 //   router_gemv_kernel    8-bit router GEMV on the VALU -> fp32 partial logits
-//                         per k-split; also writes x as fp16 (hi [+ lo]) and
-//                         per-64 group sums.
-//   router_mfma_kernel    the same on the matrix cores, for bf16 batches of 64
-//                         tokens or more.
+//                         per k-split (fp32 input as fp16 hi + lo, both
+//                         multiplied); also writes x as fp16 (the hi half, the
+//                         experts' input) and per-64 group sums.
+//   router_mfma_kernel    the same on the matrix cores, for batches of 64
+//                         tokens or more (bf16 or fp32 input).
 //   router_topk_kernel    sums the partials in fixed order, adds the logit bias,
 //                         top-k by (logit desc, index asc) with DPP reductions,
 //                         softmax over the k; when one workgroup covers the
