@@ -238,12 +238,25 @@ int moe_router_logits(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_to
  * tokens routed to it in one forward (T for the shared expert).  Rows below
  * mfma_min_rows take the streaming dot-product path; rows in
  * [mfma_min_rows, wide_min_rows) take the matrix-core path in 32-row tiles;
- * rows >= wide_min_rows take it in 128-row tiles.  Defaults: 4 and 32, or 2
+ * rows >= wide_min_rows take it in 128-row tiles.  Defaults: 4 and 32, or 3
  * and 32 when hidden >= 4096.
  * mfma_min_rows = 1 sends every expert to the matrix cores; values above
  * max_tokens keep them all on the streaming path.  Never changes the selected
  * experts.  Errors: MOE_EINVAL unless 1 <= mfma_min_rows <= wide_min_rows. */
 int moe_set_path_rows(moe_ctx *ctx, int32_t mfma_min_rows, int32_t wide_min_rows);
+
+/* Tuning knob for the 32-row tiles.  A tile can be split over workgroups by K
+ * (each of a workgroup's four waves takes a quarter of the K groups of the
+ * same 32 or 64 columns, and the partial sums are added in a fixed order) or
+ * by columns (each wave takes its own columns over all K groups, so the
+ * waves share the token rows and a workgroup covers four times the weights).
+ * A forward takes the column split when the most 32-row tiles its batch size
+ * allows would give min_workgroups workgroups or more that way (for each of
+ * the gate/up and the down launch).  Default: four times the device's
+ * compute-unit count.  0 always splits by columns; INT32_MAX never.
+ * Both splits give the same outputs up to the order of the fp32 sums over K
+ * (the selection is unchanged).  Errors: MOE_EINVAL if min_workgroups < 0. */
+int moe_set_narrow_split(moe_ctx *ctx, int32_t min_workgroups);
 
 /* Kernel timing (measurement aid).  moe_profile_start creates event pairs for
  * up to max_calls forwards; each later moe_forward on a stream that is not

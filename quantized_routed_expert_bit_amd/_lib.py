@@ -20,8 +20,8 @@ MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
             "moe_forward_noalloc", "moe_crc32", "moe_set_cache", "moe_cache_stats",
             "moe_rvq_workspace_bytes", "moe_rvq_gemv",
-            "moe_router_logits", "moe_set_path_rows", "moe_close", "moe_strerror",
-            "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
+            "moe_router_logits", "moe_set_path_rows", "moe_set_narrow_split", "moe_close",
+            "moe_strerror", "moe_last_error", "moe_check_record_header", "moe_debug_dequant",
             "moe_profile_start", "moe_profile_start_slots", "moe_profile_read")
 # kernel timing slots of moe_profile_read (the last one is reserved)
 PROFILE_SLOTS = ("router", "gemv_up", "gemv_down", "mfma_up", "mfma_down", "combine",
@@ -73,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.moe_router_logits.restype = c_int
     lib.moe_set_path_rows.argtypes = [c_void_p, c_int32, c_int32]
     lib.moe_set_path_rows.restype = c_int
+    lib.moe_set_narrow_split.argtypes = [c_void_p, c_int32]
+    lib.moe_set_narrow_split.restype = c_int
     lib.moe_close.argtypes = [c_void_p]
     lib.moe_close.restype = None
     lib.moe_strerror.argtypes = [c_int]

@@ -107,6 +107,7 @@ struct LayerDev {
   int H, E, Epad, k, I, Is, has_shared, rmsnorm, max_tokens;
   int mfma_min_rows;   // rows at which an expert leaves the streaming path
   int wide_min_rows;   // rows at which it uses 128-row instead of 32-row tiles
+  int narrow_cs_min_wgs;   // 32-row tiles split columns, not K, from this many workgroups
   int n_cu;            // compute units of the device
   // workspace
   uint8_t* ws;

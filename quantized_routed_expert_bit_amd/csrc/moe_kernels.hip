@@ -1401,7 +1401,10 @@ __device__ __forceinline__ f16x8 dequant8(const Lift& L, uint32_t dw, f16x2 s2, 
 // instruction fills a contiguous 1 KiB (256 B) block.  Issued through inline
 // assembly so the compiler neither waits for these loads on its own (the
 // kernel waits with explicit vmcnt counts) nor reorders LDS accesses across
-// them ("memory" clobber).
+// them ("memory" clobber).  m0 is reserved to the compiler, which warns that
+// it may not keep a value of its own in m0 across these statements; in these
+// kernels nothing but these two statements writes or reads m0 (checked in the
+// gfx950 assembly), so there is nothing for them to clobber.
 __device__ __forceinline__ void lds_dma16(const void* g, const void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"((uint32_t)(uintptr_t)lds_base) : "memory", "m0");
@@ -1643,17 +1646,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   }
 }
 
-// Narrow matrix-core kernel, for experts with a few tens of rows: one
-// workgroup = one 32-row tile x 32 gate+up columns (or 64 down columns); the
-// 4 waves split the K groups, so each wave streams a quarter of the weights
-// with a PN-deep register ring for both operands (A straight from global, no
-// LDS, no barriers in the loop) and the partial accumulators are summed across
-// waves in fixed order at the end.
+// Narrow matrix-core kernel, for experts with a few tens of rows: 32-row
+// tiles, each wave with 32 gate+up columns (or 64 down columns) and a PN-deep
+// register ring for both operands (A straight from global, no LDS, no
+// barriers in the loop).  Two ways to split a tile over workgroups:
+//  - CS false: one workgroup = 32 (64) columns; the 4 waves split the K
+//    groups and their partial accumulators are summed across waves in fixed
+//    order at the end (four times the workgroups: for few tiles);
+//  - CS true: one workgroup = 128 (256) columns, wave w the w-th quarter over
+//    all K groups (the four waves read the same token rows, so those are
+//    fetched once per 128 (256) columns instead of once per 32 (64), and
+//    each workgroup's fixed costs cover four times the weights: for many
+//    tiles).
 // The body works on tile tile_i, column block cblk, with red (16 KiB, one
 // [16][64] plane per wave) and s_slot (32 ints) in LDS; the first workgroups
 // of the streaming kernels run it (one launch for both expert paths).
 typedef float NarrowRed[16][64];
-template <bool UP>
+template <bool UP, bool CS>
 __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int cblk,
                                             NarrowRed* red, int* s_slot) {
   constexpr int PN = 2;
@@ -1666,15 +1675,18 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
   const int inter = sh ? a.Is : a.I;
   const int G = a.H >> 6;
   const int Kg = UP ? G : inter >> 6;
-  constexpr int CB = UP ? 32 : 64;
+  constexpr int CB = UP ? 32 : 64;           // columns per wave
   const int ncols = UP ? inter : a.H;
-  const int n0 = cblk * CB;
-  if (n0 >= ncols) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = CS ? (cblk * kMfmaWaves + wave) * CB : cblk * CB;
+  if ((CS ? cblk * kMfmaWaves * CB : n0) >= ncols) return;
   const int hi = lane >> 5, l32 = lane & 31;
   const int Tk = a.T * a.k;
   if (tid < 32) s_slot[tid] = a.slots[loff + m0 + (tid < mrows ? tid : 0)];
   __syncthreads();
+  // (CS: the last workgroup of a tile may hold waves past the last column;
+  // no barrier follows)
+  if (CS && n0 >= ncols) return;
   // this lane's A row (row l32 of the tile; rows past the tile repeat row 0)
   const int slot = s_slot[l32];
   const size_t a_row = UP ? (size_t)(slot < Tk ? slot / a.k : slot - Tk) * a.H
@@ -1691,7 +1703,7 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
     bb[nb] = mat + (size_t)(r >> 6) * Kg * kQ4TileBytes;
     brow[nb] = (r & 63) + l32;
   }
-  const int gbeg = (Kg * wave) / kMfmaWaves, gend = (Kg * (wave + 1)) / kMfmaWaves;
+  const int gbeg = CS ? 0 : (Kg * wave) / kMfmaWaves, gend = CS ? Kg : (Kg * (wave + 1)) / kMfmaWaves;
   f32x16 acc[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
@@ -1745,6 +1757,25 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
     }
 #undef QREB_NARROW_LOAD
   }
+  if (CS) {
+    // the wave's own columns, all K: lane holds rows 8 (j / 4) + 4 hi + j % 4
+    // of column n0 (+ 32) + l32
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = 8 * (j >> 2) + 4 * hi + (j & 3);
+      if (row < mrows) {
+        const int sl = s_slot[row];
+        if (UP) {
+          const float hv = swiglu(acc[0][j], acc[1][j]);
+          a.hdst[h_off(sl, Tk, a.I, a.Is) + pair_pos4(n0 + l32)] = f16bits((_Float16)hv);
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) a.yslot[(size_t)sl * a.H + n0 + nb * 32 + l32] = acc[nb][j];
+        }
+      }
+    }
+    return;
+  }
   // wave w finishes rows j in {4w .. 4w+3} of each lane's 16 (fixed-order
   // sum over the waves), one 32-column block at a time through the same LDS
   float v[2][4];
@@ -1782,6 +1813,13 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
 
 // --------------------------------------------- streaming path kernels --
 
+// How the narrow tiles of a streaming launch are laid over its workgroups:
+// the shared expert's tile count, column blocks per shared and per routed
+// tile, and the split (cs: by columns, else by K).
+struct NarrowGrid {
+  int nsht, ncbs, ncbr, cs;
+};
+
 // Which narrow matrix-core tile a workgroup of a streaming launch runs.  The
 // tiles of this forward (misc[kNNarrow] of them, the shared expert's nsht
 // tiles last in the list) take the first workgroups of the grid, compacted:
@@ -1789,9 +1827,10 @@ __device__ __forceinline__ void narrow_tile(const MfmaArgs& a, int tile_i, int c
 // then the routed ones (ncbr each).  Returns true with (tile, cblk) set for a
 // narrow workgroup; else rebases b onto the streaming units, so the
 // workgroups past this forward's work all sit at the end of the grid.
-__device__ __forceinline__ bool narrow_work(const int* misc, int nsht, int ncbs, int ncbr, int& b,
+__device__ __forceinline__ bool narrow_work(const int* misc, const NarrowGrid& ng, int& b,
                                             int& tile, int& cblk) {
   const int nreal = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNNarrow];
+  const int nsht = ng.nsht, ncbs = ng.ncbs, ncbr = ng.ncbr;
   const int nrt = max(nreal - nsht, 0);
   const int nsw = nsht * ncbs;
   if (b < nsw) {
@@ -1901,14 +1940,18 @@ void gemv_up_kernel(
     const float* __restrict__ xs,
     const int4* __restrict__ items, const int* __restrict__ misc, const int* __restrict__ slots,
     uint16_t* __restrict__ hbuf, float* __restrict__ hs, int nsh, int nunits, int mt,
-    MfmaArgs ma, int nsht, int ncbs, int ncbr) {
+    MfmaArgs ma, NarrowGrid ng) {
   extern __shared__ uint32_t dyn[];
   // the narrow matrix-core tiles run in the first workgroups, so both
   // expert paths share one launch
   int b = (int)blockIdx.x, tile, cblk;
-  if (narrow_work(misc, nsht, ncbs, ncbr, b, tile, cblk)) {
-    narrow_tile<true>(ma, tile, cblk, reinterpret_cast<NarrowRed*>(dyn),
-                          reinterpret_cast<int*>(dyn) + kMfmaWaves * 16 * 64);
+  if (narrow_work(misc, ng, b, tile, cblk)) {
+    NarrowRed* red = reinterpret_cast<NarrowRed*>(dyn);
+    int* s_slot = reinterpret_cast<int*>(dyn) + kMfmaWaves * 16 * 64;
+    if (ng.cs)
+      narrow_tile<true, true>(ma, tile, cblk, red, s_slot);
+    else
+      narrow_tile<true, false>(ma, tile, cblk, red, s_slot);
     return;
   }
   // per-wave partial sums, in LDS over the staged rows once they are consumed
@@ -2047,12 +2090,16 @@ void gemv_down_kernel(
     int H, int E, int k, int I, int Is, int T, const int4* __restrict__ items,
     const int* __restrict__ misc, const int* __restrict__ slots,
     const uint32_t* __restrict__ hbuf32, const float* __restrict__ hs,
-    float* __restrict__ yslot, int nsh, int rpu, int mt, MfmaArgs ma, int nsht, int ncb) {
+    float* __restrict__ yslot, int nsh, int rpu, int mt, MfmaArgs ma, NarrowGrid ng) {
   extern __shared__ uint32_t dyn[];
   int b = (int)blockIdx.x, tile, cblk;
-  if (narrow_work(misc, nsht, ncb, ncb, b, tile, cblk)) {   // as in gemv_up_kernel
-    narrow_tile<false>(ma, tile, cblk, reinterpret_cast<NarrowRed*>(dyn),
-                              reinterpret_cast<int*>(dyn) + kMfmaWaves * 16 * 64);
+  if (narrow_work(misc, ng, b, tile, cblk)) {   // as in gemv_up_kernel
+    NarrowRed* red = reinterpret_cast<NarrowRed*>(dyn);
+    int* s_slot = reinterpret_cast<int*>(dyn) + kMfmaWaves * 16 * 64;
+    if (ng.cs)
+      narrow_tile<false, true>(ma, tile, cblk, red, s_slot);
+    else
+      narrow_tile<false, false>(ma, tile, cblk, red, s_slot);
     return;
   }
   float (*red)[kGemvTokV2][64] = reinterpret_cast<float (*)[kGemvTokV2][64]>(dyn);   // over the rows
@@ -2403,6 +2450,25 @@ static int narrow_shared_tiles(const LayerDev& d, int T) {
   return narrow ? (T + kNarrowBM - 1) / kNarrowBM : 0;
 }
 
+// Narrow tile layout of a streaming launch over ncols columns per routed
+// tile (ncols_s for the shared expert's), cw columns per wave, and its
+// workgroup count (*nn, for the most tiles T tokens can give).  The column
+// split is taken when that bound reaches narrow_cs_min_wgs workgroups; the
+// grid then holds a quarter of the K split's workgroups.
+static NarrowGrid narrow_grid(const LayerDev& d, int T, int ncols, int ncols_s, int cw, int* nn) {
+  NarrowGrid g;
+  const int cwc = cw * kMfmaWaves;
+  const int ntm = narrow_tiles_max(d, T);
+  g.nsht = narrow_shared_tiles(d, T);
+  const int ncs_c = (ncols_s + cwc - 1) / cwc, ncr_c = (ncols + cwc - 1) / cwc;
+  const int nn_c = g.nsht * ncs_c + (ntm - g.nsht) * ncr_c;
+  g.cs = nn_c >= d.narrow_cs_min_wgs ? 1 : 0;
+  g.ncbs = g.cs ? ncs_c : ncols_s / cw;
+  g.ncbr = g.cs ? ncr_c : ncols / cw;
+  *nn = g.nsht * g.ncbs + (ntm - g.nsht) * g.ncbr;
+  return g;
+}
+
 hipError_t launch_gemv_up(const LayerDev& d, int T, hipStream_t s) {
   const ExpertPtrs p = expert_ptrs(d, T);
   const int mt = gemv_tokens_per_pass(d, T);
@@ -2418,16 +2484,16 @@ hipError_t launch_gemv_up(const LayerDev& d, int T, hipStream_t s) {
   const int nsh = shared_streams(d, T) ? d.Is / rpu : 0, nunits = d.I / rpu;
   const int units = nsh + routed_stream_items(d, T) * nunits;
   // narrow matrix-core tiles (experts with a few tens of rows) in the same
-  // launch: 32 gate+up columns per workgroup
-  const int nsht = narrow_shared_tiles(d, T), ncbs = d.Is / 32, ncbr = d.I / 32;
-  const int nn = nsht * ncbs + (narrow_tiles_max(d, T) - nsht) * ncbr;
+  // launch: 32 gate+up columns per wave
+  int nn;
+  const NarrowGrid ng = narrow_grid(d, T, d.I, d.Is, 32, &nn);
   if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
   const size_t red_bytes = (size_t)(split ? 1 : 2) * kGemvWaves * kGemvTokV2 * 64 * 4;
   if (lds < red_bytes) lds = red_bytes;
   auto* kern = split ? gemv_up_kernel<true, false> : gemv_up_kernel<false, true>;
   hipLaunchKernelGGL(kern, dim3(nn + units), dim3(kGemvThreads), lds, s, d.bank, d.stride,
                      d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.x16, p.xs, p.items, p.misc,
-                     p.slots, p.hbuf, p.hs, nsh, nunits, mt, mfma_args(d, T), nsht, ncbs, ncbr);
+                     p.slots, p.hbuf, p.hs, nsh, nunits, mt, mfma_args(d, T), ng);
   return hipGetLastError();
 }
 
@@ -2448,12 +2514,14 @@ hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
   const bool many = two > 8 * d.n_cu && T * d.k < 4 * d.E;
   const int rpu = G2 > 24 ? 1 : many ? kGemvWaves : kGemvWaves / 2;
   const int units = nsh + routed_stream_items(d, T) * ((nrb + rpu - 1) / rpu);
-  const int ncb = d.H / 64, nn = ncb * narrow_tiles_max(d, T);   // narrow down tiles, 64 columns
+  // narrow down tiles: 64 columns per wave
+  int nn;
+  const NarrowGrid ng = narrow_grid(d, T, d.H, d.H, 64, &nn);
   if (nn > 0 && lds < kNarrowLds) lds = kNarrowLds;
   hipLaunchKernelGGL(gemv_down_kernel, dim3(nn + units), dim3(kGemvThreads), lds, s, d.bank,
                      d.stride, d.shared, d.H, d.E, d.k, d.I, d.Is, T, p.items, p.misc, p.slots,
                      reinterpret_cast<const uint32_t*>(p.hbuf), p.hs, p.yslot, nsh, rpu, mt,
-                     mfma_args(d, T), narrow_shared_tiles(d, T), ncb);
+                     mfma_args(d, T), ng);
   return hipGetLastError();
 }
 

@@ -161,6 +161,11 @@ class MoELayer:
                     "moe_set_path_rows")
         self.mfma_min_rows, self.wide_min_rows = mfma_min_rows, wide_min_rows
 
+    def set_narrow_split(self, min_workgroups):
+        """32-row tiles split by columns from min_workgroups workgroups on
+        (0: always, 2**31 - 1: never), else by K."""
+        self._check(self.lib.moe_set_narrow_split(self.ctx, min_workgroups), "moe_set_narrow_split")
+
     def close(self):
         if self.ctx:
             self.lib.moe_close(self.ctx)

@@ -283,6 +283,9 @@ def test_error_paths(torch_dev):
     with pytest.raises(MoEError) as ei:
         m.set_weights(w["router"], w["bank"], w["stride"], shared=w["bank"][:4096])
     assert ei.value.code == -1                                     # shared without the flag
+    with pytest.raises(MoEError) as ei:
+        m.set_narrow_split(-1)
+    assert ei.value.code == -1
 
 
 def test_profile_slot_mask(torch_dev):
@@ -323,6 +326,34 @@ def test_layer_parity_matrix_core(torch_dev, cfg, min_rows, wide_rows):
                         p.cpu().numpy(), f"cfg{cfg} mfma>={min_rows} T={T}")
 
 
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_narrow_tile_splits(torch_dev, cfg):
+    """Every expert (and the shared one) on the 32-row tiles, split over
+    workgroups by K and by columns (forced both ways): each against the oracle,
+    and the two against each other (same selection; outputs equal up to the
+    order of the fp32 sums over K)."""
+    import torch
+    wl = synth.WORKLOADS[cfg]
+    li = synth.layer_inputs(wl)
+    ol = P.oracle_layer(li)
+    ms = {}
+    for name, split in (("k", 2 ** 31 - 1), ("cols", 0)):
+        ms[name] = _layer(li, torch_dev, 40, mfma_min_rows=1, wide_min_rows=64)
+        ms[name].set_narrow_split(split)
+    for T in (1, 5, 16, 40):
+        xb = synth.make_hidden(0, cfg, T, wl.shape.hidden, tag=11)
+        out = {}
+        for name, m in ms.items():
+            P.log(f"cfg{cfg} narrow split by {name}, T={T}")
+            y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+            P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
+                            p.cpu().numpy(), f"cfg{cfg} split {name} T={T}")
+            out[name] = (y, ids)
+        assert torch.equal(out["k"][1], out["cols"][1])
+        d = (out["k"][0] - out["cols"][0]).abs().max().item()
+        assert d <= 1e-3 * out["k"][0].abs().max().item(), d   # (h is rounded to fp16 after either sum)
+
+
 @pytest.mark.parametrize("shape", [
     dict(H=320, E=65, k=3, I=192, Is=0, T=200),      # partial 128-column blocks, ragged tiles
     dict(H=192, E=8, k=2, I=64, Is=320, T=300),      # >128 rows per expert: several row tiles
@@ -333,11 +364,13 @@ def test_matrix_core_edge_shapes(torch_dev, shape):
     li = synth.LayerInputs(13, 91, 0, synth.LayerShape(H, E, k, I, Is), "normal0.5")
     ol = P.oracle_layer(li)
     xb = synth.make_hidden(13, 91, T, H)
-    for wide in (2, 40):
+    for wide, split in ((2, None), (40, 0), (40, 2 ** 31 - 1)):
         m = _layer(li, torch_dev, T, mfma_min_rows=2, wide_min_rows=wide)
+        if split is not None:   # 32-row tiles split by columns (partial last blocks), or by K
+            m.set_narrow_split(split)
         y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
         P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
-                        p.cpu().numpy(), f"mfma edge wide>={wide}")
+                        p.cpu().numpy(), f"mfma edge wide>={wide} split {split}")
     m = _layer(li, torch_dev, T, mfma_min_rows=2)
     y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
     P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids.cpu().numpy(),
