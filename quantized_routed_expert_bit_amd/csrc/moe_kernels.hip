@@ -2507,12 +2507,17 @@ hipError_t launch_gemv_down(const LayerDev& d, int T, hipStream_t s) {
   // routed experts: several row blocks per workgroup, one or two waves per
   // block, so a workgroup's fixed costs cover more weights; four blocks (one
   // wave each) once two-block units would exceed what the CUs hold at once
-  // while most routed experts stream (fewer than 4 rows on average)
+  // while most routed experts stream (fewer than 4 rows on average).  A long
+  // K (more than 24 groups) takes one block per workgroup, unless the grid's
+  // bound (every expert streaming) passes 16 workgroups per CU: then four,
+  // since the bound's empty workgroups cost their dispatch (256-token stack
+  // at hidden 7168: the down launch 384 -> 323 us per layer)
   const int nrb = d.H / 64, nsh = shared_streams(d, T) ? nrb : 0;
   const int G2 = d.I / 64;
   const int two = routed_stream_items(d, T) * ((nrb + 1) / 2);
   const bool many = two > 8 * d.n_cu && T * d.k < 4 * d.E;
-  const int rpu = G2 > 24 ? 1 : many ? kGemvWaves : kGemvWaves / 2;
+  const bool big = routed_stream_items(d, T) * nrb > 16 * d.n_cu;
+  const int rpu = G2 > 24 ? (big ? kGemvWaves : 1) : many ? kGemvWaves : kGemvWaves / 2;
   const int units = nsh + routed_stream_items(d, T) * ((nrb + rpu - 1) / rpu);
   // narrow down tiles: 64 columns per wave
   int nn;
