@@ -375,8 +375,10 @@ int moe_cache_stats(moe_ctx *ctx, uint64_t *out, int32_t n, void *stream);
  * least one matrix when n_mats > 1), x bf16 or fp32 [T, K] (MOE_BF16 /
  * MOE_F32, 4-byte aligned), y fp32 [n_mats][T][R] (4-byte aligned), all
  * device memory; the per-group partial sums (fp32, summed over K groups of
- * 256 columns in group order) live in the caller's workspace of
- * moe_rvq_workspace_bytes (256-byte aligned); the tables are built in LDS.
+ * 4 to 8 tiles in group order; the group size follows the shape and the
+ * device's CU count, so results can differ in the last bits between devices)
+ * live in the caller's workspace of moe_rvq_workspace_bytes (256-byte
+ * aligned, sized for groups of 4 tiles); the tables are built in LDS.
  * Stream-ordered, no allocation, no host synchronisation; T = 0 is a no-op.
  * Errors: MOE_EINVAL (shapes, dtype, pointers, alignment), MOE_ENOMEM
  * (workspace too small), MOE_EHIP.  moe_rvq_workspace_bytes

@@ -32,7 +32,9 @@ constexpr int kRvqThreads = 1024;
 constexpr int kRvqRowsPerThread = 4;
 constexpr int kRvqRows = kRvqThreads * kRvqRowsPerThread;   // rows per workgroup
 constexpr int kRvqTokMax = 4;      // tokens per pass (one tile's tables: 24 KiB per token)
-constexpr int kRvqTilesPerGroup = 4;   // 64-column tiles per K group of a workgroup
+// 64-column tiles per K group of a workgroup: chosen per shape in this range
+constexpr int kRvqTilesMin = 4;
+constexpr int kRvqTilesMax = 8;
 
 __device__ __forceinline__ float rvq_f16(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
@@ -53,7 +55,7 @@ template <> struct RvqVec<4> {
   __device__ static float at(float4 v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 };
 
-// Workgroup = (K group kg of up to kRvqTilesPerGroup tiles, matrix m, block
+// Workgroup = (K group kg of up to tpg tiles, matrix m, block
 // rb of kRvqRows rows), for the TP tokens t0 .. t0+TP-1 (TP = 1, 2 or 4).
 // Per tile the workgroup builds the tile's tables in LDS, laid out
 // [run j][stage s][entry c][token], so that the TP tokens' values of one
@@ -69,7 +71,7 @@ template <int TP>
 __global__ __launch_bounds__(kRvqThreads) void rvq_gemv_kernel(
     const uint8_t* __restrict__ mats, uint64_t mat_stride, int R, int K, int T, int t0,
     const void* __restrict__ x, int x_f32, const uint16_t* __restrict__ cb,
-    float* __restrict__ part, int n_rb, int n_mats, int n_work, int per_xcd) {
+    float* __restrict__ part, int n_rb, int n_mats, int n_work, int per_xcd, int tpg) {
   extern __shared__ float4 lt4[];   // [8 runs][3][256][TP] tables, then [TP][group columns] x
   float* lt = reinterpret_cast<float*>(lt4);
   const int w = (int)(blockIdx.x & 7u) * per_xcd + (int)(blockIdx.x >> 3);
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kRvqThreads) void rvq_gemv_kernel(
   const int m = mr / n_rb, rb = mr % n_rb;
   const int tid = threadIdx.x;
   const int G = K / 64;
-  const int g0 = kg * kRvqTilesPerGroup, g1 = min(G, g0 + kRvqTilesPerGroup);
+  const int g0 = kg * tpg, g1 = min(G, g0 + tpg);
   const int ncol = (g1 - g0) * 64;
   float* xs = lt + TP * 8 * 768;   // [TP][ncol]
   for (int i = tid; i < TP * ncol; i += kRvqThreads) {
@@ -201,51 +203,82 @@ __global__ __launch_bounds__(256) void rvq_reduce_kernel(const float* __restrict
 
 static size_t rvq_al(size_t v) { return (v + 255) & ~size_t(255); }
 
-static int rvq_groups(int K) {
+static int rvq_groups(int K, int tpg) {
   const int G = K / 64;
-  return (G + kRvqTilesPerGroup - 1) / kRvqTilesPerGroup;
+  return (G + tpg - 1) / tpg;
+}
+
+// Tiles per K group: the workgroups (one per CU at a time: 16 waves of 84 or
+// more registers) run in ceil(work / CUs) rounds of a time proportional to
+// the group's tiles, so the size with the fewest rounds x tiles is taken, the
+// larger on a tie (fewer partial sums to add).  16 matrices of 4096 x 7168 on
+// 256 CUs: 7 tiles, one round of 256 workgroups (one token 58 -> 48 us against
+// 4 tiles, 448 workgroups in two rounds).
+static int rvq_tiles_per_group(int K, int n_mats, int n_rb, int n_cu) {
+  int best = kRvqTilesMin;
+  long best_cost = -1;
+  for (int tpg = kRvqTilesMin; tpg <= kRvqTilesMax; ++tpg) {
+    const long work = (long)rvq_groups(K, tpg) * n_mats * n_rb;
+    const long cost = (work + n_cu - 1) / n_cu * tpg;
+    if (best_cost < 0 || cost <= best_cost) {
+      best = tpg;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 size_t rvq_workspace(int T, int K, int R, int n_mats) {
-  // launch limits: at most 2^20 workgroups and 2^31 outputs
+  // launch limits: at most 2^20 workgroups and 2^31 outputs; partial sums
+  // for the most K groups (the smallest group size)
   const uint64_t n_rb = ((uint64_t)R + kRvqRows - 1) / kRvqRows;
-  if ((uint64_t)rvq_groups(K) * (uint64_t)n_mats * n_rb > (1u << 20) ||
+  if ((uint64_t)rvq_groups(K, kRvqTilesMin) * (uint64_t)n_mats * n_rb > (1u << 20) ||
       (uint64_t)n_mats * (uint64_t)T * (uint64_t)R > (1ull << 31))
     return 0;
-  return rvq_al((size_t)rvq_groups(K) * n_mats * T * R * 4);
+  return rvq_al((size_t)rvq_groups(K, kRvqTilesMin) * n_mats * T * R * 4);
 }
 
 hipError_t launch_rvq_gemv(const void* x, int x_f32, int T, int K, const uint8_t* mats,
                            uint64_t mat_stride, int n_mats, int R, const uint16_t* cb, float* y,
                            uint8_t* ws, hipStream_t s) {
-  const int KG = rvq_groups(K);
-  float* part = reinterpret_cast<float*>(ws);
-  const int n_rb = (R + kRvqRows - 1) / kRvqRows;
-  const int n_work = KG * n_mats * n_rb, per_xcd = (n_work + 7) / 8;
-  const int ncol = (K / 64 < kRvqTilesPerGroup ? K / 64 : kRvqTilesPerGroup) * 64;
-  // passes of 4, 2 or 1 tokens; each holds TP x (24 KiB of tables + the
-  // group's x) in LDS
-  // the LDS limit of the 2- and 4-token kernels, once per device
+  // the LDS limit of the 2- and 4-token kernels and the CU count, once per
+  // device
   hipError_t e;
   int dev = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static int n_cus[kMaxDevices] = {};
+  int n_cu;
   {
     static std::mutex mu;
     static bool lds_set[kMaxDevices] = {};
     std::lock_guard<std::mutex> lock(mu);
     if (!lds_set[dev]) {
+      int v = 0;
+      e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      if (v < 1) return hipErrorInvalidDevice;
+      n_cus[dev] = v;
       const void* fns[3] = {reinterpret_cast<const void*>(rvq_gemv_kernel<1>),
                             reinterpret_cast<const void*>(rvq_gemv_kernel<2>),
                             reinterpret_cast<const void*>(rvq_gemv_kernel<4>)};
       for (int i = 0; i < 3; ++i) {
         e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (1 << i) * (8 * 768 + kRvqTilesPerGroup * 64) * 4);
+                                (1 << i) * (8 * 768 + kRvqTilesMax * 64) * 4);
         if (e != hipSuccess) return e;
       }
       lds_set[dev] = true;
     }
+    n_cu = n_cus[dev];
   }
+  float* part = reinterpret_cast<float*>(ws);
+  const int n_rb = (R + kRvqRows - 1) / kRvqRows;
+  const int tpg = rvq_tiles_per_group(K, n_mats, n_rb, n_cu);
+  const int KG = rvq_groups(K, tpg);
+  const int n_work = KG * n_mats * n_rb, per_xcd = (n_work + 7) / 8;
+  const int ncol = (K / 64 < tpg ? K / 64 : tpg) * 64;
+  // passes of 4, 2 or 1 tokens; each holds TP x (24 KiB of tables + the
+  // group's x) in LDS
   for (int t0 = 0; t0 < T;) {
     // passes of 4 tokens (3 remaining run as a pass of 4: one 4-token pass
     // costs less than passes of 2 and 1), then 2, then 1
@@ -254,13 +287,13 @@ hipError_t launch_rvq_gemv(const void* x, int x_f32, int T, int K, const uint8_t
     const dim3 grid(per_xcd * 8), block(kRvqThreads);
     if (tp == 1)
       hipLaunchKernelGGL(rvq_gemv_kernel<1>, grid, block, lds, s, mats, mat_stride, R, K, T, t0, x,
-                         x_f32, cb, part, n_rb, n_mats, n_work, per_xcd);
+                         x_f32, cb, part, n_rb, n_mats, n_work, per_xcd, tpg);
     else if (tp == 2)
       hipLaunchKernelGGL(rvq_gemv_kernel<2>, grid, block, lds, s, mats, mat_stride, R, K, T, t0, x,
-                         x_f32, cb, part, n_rb, n_mats, n_work, per_xcd);
+                         x_f32, cb, part, n_rb, n_mats, n_work, per_xcd, tpg);
     else
       hipLaunchKernelGGL(rvq_gemv_kernel<4>, grid, block, lds, s, mats, mat_stride, R, K, T, t0, x,
-                         x_f32, cb, part, n_rb, n_mats, n_work, per_xcd);
+                         x_f32, cb, part, n_rb, n_mats, n_work, per_xcd, tpg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     t0 += tp;   // (may pass T: the last pass of 4 carried 3 tokens)

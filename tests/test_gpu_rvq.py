@@ -3,7 +3,8 @@ products, three lookups per 8-weight run) against the oracle, which
 reconstructs the matrix and multiplies in fp64.  Shapes cover one tile, a
 row count past a workgroup's rows with a short last K group, several
 matrices at a stride, every kind of token pass (1, 2, 4, and 4 carrying 3),
-fp32 input, and the large layer's gate/up and the decode layer's down shapes.
+fp32 input, the large layer's gate/up and the decode layer's down shapes,
+and enough matrices for K groups larger than 4 tiles.
 
 Tolerance: the GPU's tables and sums are fp32 (x converts exactly, codebook
 entries are fp16, products and sums round once each); with K/8 runs of three
@@ -36,6 +37,9 @@ CASES = [
     dict(R=192, K=256, T=3, n=1, f32=False),      # 3 tokens: one pass of 4 with a zero slot
     dict(R=128, K=320, T=6, n=2, f32=True),       # passes of 4 and 2
     dict(R=64, K=128, T=7, n=1, f32=False),       # passes of 4 and 4 (the second with 3)
+    # 16 matrices: on 256 CUs the K groups take 7 tiles (one round of 240
+    # workgroups), the last group 2 tiles
+    dict(R=256, K=6400, T=2, n=16, f32=False),
 ]
 
 
