@@ -439,7 +439,8 @@ def run_cache(args, dev, decode_layers, n_slots=16, n_tokens=32):
     (the TurboFieldfare setting: 16 slots for a top-8 router over 128
     experts), run token by token.  Against the same stack on resident banks;
     with the next layer's router one residual ahead prefetching into the next
-    layer's cache, and without."""
+    layer's cache (each token's k predicted experts, or its top 6 as the
+    WASTE page prefetches), and without."""
     import torch
     import synth
     from quantized_routed_expert_bit_amd import MoELayer
@@ -466,17 +467,18 @@ def run_cache(args, dev, decode_layers, n_slots=16, n_tokens=32):
             m.forward(r, y=r, residual=r, lookahead=layers[l + 1] if la and l + 1 < L else None)
 
     out = {}
-    for mode, layers, la in (("resident", res, True), ("cache_prefetch", cac, True),
-                             ("cache_no_prefetch", cac, False)):
+    for mode, layers, la, top in (("resident", res, True, None), ("cache_prefetch", cac, True, None),
+                                  ("cache_prefetch_top6", cac, True, 6),
+                                  ("cache_no_prefetch", cac, False, None)):
         if layers is cac:
             for l, m in enumerate(layers):
-                m.set_cache(n_slots, prefetch=la and l > 0)
+                m.set_cache(n_slots, prefetch=la and l > 0, prefetch_top=top if la and l > 0 else None)
         for t in range(4):
             tok(layers, t, la)
         torch.cuda.synchronize()
         if layers is cac:   # count the timed tokens only
             for l, m in enumerate(layers):
-                m.set_cache(n_slots, prefetch=la and l > 0)
+                m.set_cache(n_slots, prefetch=la and l > 0, prefetch_top=top if la and l > 0 else None)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for t in range(n_tokens):

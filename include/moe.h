@@ -328,15 +328,20 @@ int moe_check_record_header(const void *header, uint64_t header_bytes,
  * that layer's compute; this context's next forward waits for the copies
  * before its own plan.  A prefetch never evicts for itself a slot whose expert
  * it predicts, and a record prefetched but not used is evicted first.
+ * MOE_CACHE_PREFETCH_TOP(p) (with MOE_CACHE_PREFETCH, 1 <= p <= k) prefetches
+ * only the p highest-ranked of each token's k predicted experts (the WASTE
+ * page prefetches the top 6 of its router's 8); without it, all k.
  *
- * moe_set_cache: slots is device memory of slots_bytes >= n_slots *
- * record_stride bytes (256-aligned, caller-owned, borrowed until the next
+ * moe_set_cache: flags is 0 or MOE_CACHE_PREFETCH, optionally with
+ * MOE_CACHE_PREFETCH_TOP(p); slots is device memory of slots_bytes >=
+ * n_slots * record_stride bytes (256-aligned, caller-owned, borrowed until the next
  * moe_set_cache, moe_set_weights or moe_close), n_slots in [min(E,
  * max_tokens * k), E]; slots NULL or n_slots 0 removes the cache.  The cache
  * starts empty, its counters at zero.  It needs the bound workspace (its
  * state lives there); moe_set_weights removes it, and moe_forward_noalloc
  * refuses a context that has one.  Errors: MOE_ESTATE (no weights or no
- * workspace), MOE_ENOMEM (too few slots or bytes), MOE_EINVAL, MOE_EHIP.
+ * workspace), MOE_ENOMEM (too few slots or bytes), MOE_EINVAL (also unknown
+ * flags, or a prefetch depth without MOE_CACHE_PREFETCH or above k), MOE_EHIP.
  *
  * moe_cache_stats: the counters since moe_set_cache, into out[0 .. n-1]
  * (waits for the stream): 0 forwards, 1 experts selected, 2 demand hits,
@@ -345,6 +350,7 @@ int moe_check_record_header(const void *header, uint64_t header_bytes,
  * evicted unused, 9..15 zero.  Errors: MOE_ESTATE (no cache), MOE_EINVAL,
  * MOE_EHIP. */
 #define MOE_CACHE_PREFETCH 1u
+#define MOE_CACHE_PREFETCH_TOP(p) ((((uint32_t)(p)) & 0xffu) << 8)
 #define MOE_CACHE_STATS 16
 int moe_set_cache(moe_ctx *ctx, void *slots, uint64_t slots_bytes, int32_t n_slots,
                   uint32_t flags, void *stream);

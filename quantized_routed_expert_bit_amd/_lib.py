@@ -27,6 +27,11 @@ EXPORTED = ("moe_workspace_bytes", "moe_open", "moe_set_weights", "moe_forward",
 PROFILE_SLOTS = ("router", "gemv_up", "gemv_down", "mfma_up", "mfma_down", "combine",
                  "cache", "reserved7")
 MOE_CACHE_PREFETCH = 1
+
+
+def cache_prefetch_top(p):
+    """MOE_CACHE_PREFETCH_TOP(p): prefetch depth in bits 8-15 of the cache flags."""
+    return (int(p) & 0xFF) << 8
 CACHE_STATS = ("forwards", "selected", "demand_hits", "demand_misses", "demand_bytes",
                "prefetched", "prefetch_bytes", "prefetch_used", "prefetch_evicted_unused")
 

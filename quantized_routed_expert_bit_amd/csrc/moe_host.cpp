@@ -383,7 +383,7 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
   const int max_sel = n_tokens * d.k < d.E ? n_tokens * d.k : d.E;
   if (d.slot_of) {   // the experts of this forward into the cache
     mark(6, 0, s);
-    if ((e = launch_cache_plan(d, 0, 0, s)) != hipSuccess ||
+    if ((e = launch_cache_plan(d, 0, 0, 0, s)) != hipSuccess ||
         (e = launch_cache_fill(d, 0, max_sel, s)) != hipSuccess)
       return hip_fail(ctx, e, "expert cache");
     mark(6, 1, s);
@@ -404,7 +404,8 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
       const int nmax = n_tokens * next->d.k < next->d.E ? n_tokens * next->d.k : next->d.E;
       if ((e = hipEventRecord(next->pf_done, s)) != hipSuccess ||
           (e = hipStreamWaitEvent(next->copy, next->pf_done, 0)) != hipSuccess ||
-          (e = launch_cache_plan(next->d, 1, n_tokens * next->d.k, next->copy)) != hipSuccess ||
+          (e = launch_cache_plan(next->d, 1, n_tokens * next->d.k, (int)((next->cache_flags >> 8) & 0xffu),
+                                 next->copy)) != hipSuccess ||
           (e = launch_cache_fill(next->d, 1, nmax, next->copy)) != hipSuccess ||
           (e = hipEventRecord(next->pf_done, next->copy)) != hipSuccess)
         return hip_fail(ctx, e, "lookahead prefetch");
@@ -628,7 +629,11 @@ int moe_set_cache(moe_ctx* ctx, void* slots, uint64_t slots_bytes, int32_t n_slo
   if (!ctx->has_weights) return fail(ctx, MOE_ESTATE, "no weights bound");
   LayerDev& d = ctx->d;
   if (!d.ws) return fail(ctx, MOE_ESTATE, "the expert cache keeps its state in the bound workspace");
-  if (flags & ~MOE_CACHE_PREFETCH) return fail(ctx, MOE_EINVAL, "unknown cache flags");
+  if (flags & ~(MOE_CACHE_PREFETCH | MOE_CACHE_PREFETCH_TOP(0xff)))
+    return fail(ctx, MOE_EINVAL, "unknown cache flags");
+  const uint32_t top = (flags >> 8) & 0xffu;
+  if (top && (!(flags & MOE_CACHE_PREFETCH) || top > (uint32_t)d.k))
+    return fail(ctx, MOE_EINVAL, "a prefetch depth needs MOE_CACHE_PREFETCH and at most k (%d)", d.k);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSetDevice(ctx->cfg.device);
   if (e != hipSuccess) return hip_fail(ctx, e, "hipSetDevice");

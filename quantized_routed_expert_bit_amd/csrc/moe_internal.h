@@ -133,7 +133,9 @@ hipError_t launch_debug_dequant(const void* tiles, int bits, int rows, int cols,
                                 hipStream_t s);
 // Expert cache: plan (mode 0 demand from the bucketing, 1 prefetch from the
 // npred predicted ids), fill (at most max_copies records), reset.
-hipError_t launch_cache_plan(const LayerDev& d, int mode, int npred, hipStream_t s);
+// mode 0: this forward's experts; 1: prefetch of the first `top` (0: all k)
+// predicted experts of each token
+hipError_t launch_cache_plan(const LayerDev& d, int mode, int npred, int top, hipStream_t s);
 hipError_t launch_cache_fill(const LayerDev& d, int mode, int max_copies, hipStream_t s);
 hipError_t launch_cache_reset(const LayerDev& d, hipStream_t s);
 // CRC-32 (zlib's) of n byte ranges base + r * stride + off, len bytes each

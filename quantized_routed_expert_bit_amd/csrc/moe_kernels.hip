@@ -2662,8 +2662,9 @@ constexpr uint32_t kStampMask = (1u << 30) - 1;
 struct CacheArgs {
   int E, S, mode;                 // mode 0: demand (offs), 1: prefetch (pred)
   const int* offs;                // [E + 1] bucketing offsets (demand)
-  const int* pred;                // [npred] predicted expert ids (prefetch)
+  const int* pred;                // [npred] predicted expert ids (prefetch), [token][rank]
   int npred;
+  int pk, pp;                     // predictions per token; the first pp of each are prefetched
   uint64_t rec_bytes;             // bytes copied per record
   int* slot_of;                   // [E]
   int* owner;                     // [S]
@@ -2690,7 +2691,7 @@ __global__ __launch_bounds__(kCacheThreads) void cache_plan_kernel(CacheArgs c) 
   if (!demand)
     for (int i = tid; i < c.npred; i += kCacheThreads) {
       const int e = c.pred[i];
-      if (e >= 0 && e < c.E) s_sel[e] = 1;
+      if (i % c.pk < c.pp && e >= 0 && e < c.E) s_sel[e] = 1;
     }
   __syncthreads();
   const uint32_t now = (c.clock[0] + (demand ? 1u : 0u)) & kStampMask;
@@ -2801,7 +2802,7 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(const uint8_t* __restri
     *reinterpret_cast<uint4*>(d + i) = ld16_nt(s + i);
 }
 
-hipError_t launch_cache_plan(const LayerDev& d, int mode, int npred, hipStream_t s) {
+hipError_t launch_cache_plan(const LayerDev& d, int mode, int npred, int top, hipStream_t s) {
   CacheArgs c{};
   c.E = d.E;
   c.S = d.cache_slots;
@@ -2809,6 +2810,8 @@ hipError_t launch_cache_plan(const LayerDev& d, int mode, int npred, hipStream_t
   c.offs = reinterpret_cast<const int*>(d.ws + d.L.offs);
   c.pred = reinterpret_cast<const int*>(d.ws + d.L.pred);
   c.npred = npred;
+  c.pk = d.k;
+  c.pp = top > 0 && top < d.k ? top : d.k;
   c.rec_bytes = d.rec_bytes;
   uint8_t* cs = d.ws + d.L.cache;
   c.slot_of = reinterpret_cast<int*>(cs + kCacheSlotOf);

@@ -136,15 +136,20 @@ class MoELayer:
         return ({k: v for k, v in zip(L.PROFILE_SLOTS, list(arr)) if not k.startswith("reserved")},
                 calls.value)
 
-    def set_cache(self, n_slots, prefetch=False, slots=None):
+    def set_cache(self, n_slots, prefetch=False, slots=None, prefetch_top=None):
         """Give the layer an expert cache of n_slots records in HBM (a new
-        device tensor unless `slots` is given); 0 removes it."""
+        device tensor unless `slots` is given); 0 removes it.  prefetch: the
+        previous layer's lookahead prefetches into it (prefetch_top: only the
+        that many highest-ranked predictions of each token; None: all k)."""
         if n_slots and slots is None:
             slots = torch.empty(n_slots * self._stride, dtype=torch.uint8, device=self.device)
         self._slots = slots
+        flags = L.MOE_CACHE_PREFETCH if prefetch else 0
+        if prefetch_top is not None:
+            flags |= L.cache_prefetch_top(prefetch_top)
         self._check(self.lib.moe_set_cache(self.ctx, _ptr(slots) if n_slots else None,
-                                           0 if slots is None else slots.numel(), n_slots,
-                                           L.MOE_CACHE_PREFETCH if prefetch else 0, _stream()),
+                                           0 if slots is None else slots.numel(), n_slots, flags,
+                                           _stream()),
                     "moe_set_cache")
         return self
 

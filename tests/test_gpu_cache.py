@@ -57,13 +57,16 @@ def _model(w):
     return lambda n_slots: oracle.OracleExpertCache(SH.n_experts, n_slots, lay["end"])
 
 
-def test_cached_stack_matches_resident_bitwise_with_lfu_counts(torch_dev):
+@pytest.mark.parametrize("top", [None, 6])
+def test_cached_stack_matches_resident_bitwise_with_lfu_counts(torch_dev, top):
+    """top: the prefetch takes each token's `top` highest-ranked predictions
+    (None: all k)."""
     import torch
     from oracle import select_topk
     pairs = [_pair(torch_dev, l, 1) for l in range(N_LAYERS)]
     n_slots = 16
     for l, (_, cac) in enumerate(pairs):
-        cac.set_cache(n_slots, prefetch=l > 0)
+        cac.set_cache(n_slots, prefetch=l > 0, prefetch_top=top if l > 0 else None)
     models = [_model(None)(n_slots) for _ in range(N_LAYERS)]
     n_tok = 24
     for t in range(n_tok):
@@ -75,7 +78,7 @@ def test_cached_stack_matches_resident_bitwise_with_lfu_counts(torch_dev):
             nxt_c = pairs[l + 1][1] if l + 1 < N_LAYERS else None
             if nxt_r is not None:   # the prediction the lookahead will make for layer l + 1
                 lg = nxt_r.router_logits(ra).cpu().numpy().astype(np.float64)
-                pred = select_topk(lg, SH.top_k)[0].reshape(-1)
+                pred = select_topk(lg, SH.top_k)[0][:, :top or SH.top_k].reshape(-1)
             _, ia, pa = res.forward(ra, return_selection=True, y=ra, residual=ra, lookahead=nxt_r)
             _, ib, pb = cac.forward(rb, return_selection=True, y=rb, residual=rb, lookahead=nxt_c)
             torch.cuda.synchronize()
@@ -130,6 +133,11 @@ def test_cache_refusals(torch_dev):
         with pytest.raises(MoEError) as ei:
             cac.set_cache(n)
         assert ei.value.code == -3
+    for kw in (dict(prefetch=True, prefetch_top=9),    # deeper than k = 8
+               dict(prefetch=False, prefetch_top=6)):  # a depth without the prefetch
+        with pytest.raises(MoEError) as ei:
+            cac.set_cache(32, **kw)
+        assert ei.value.code == -1
     cac.set_cache(32)
     x = P.bf16_tensor(synth.make_hidden(0, 1, 4, SH.hidden, tag=900), torch_dev)
     with pytest.raises(MoEError) as ei:
