@@ -74,11 +74,12 @@ def large_layer(torch_dev):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("T", [1, 8, 64])
+@pytest.mark.parametrize("T", [1, 8, 24, 64])
 def test_large_decode_layer_every_token(torch_dev, large_layer, T):
-    """Every token of each batch; at 8 and 64 tokens the routed experts with
-    3 to 31 rows run as 32-row matrix-core tiles over a 112-group K chain, the
-    ones with 1 or 2 rows on the streaming path."""
+    """Every token of each batch; from 8 tokens the routed experts with 3 to
+    31 rows run as 32-row matrix-core tiles over a 112-group K chain (split by
+    K at 8 tokens, by columns from 24; at 24 the shared expert's 24 rows take
+    those tiles too), the ones with 1 or 2 rows on the streaming path."""
     m, ol = large_layer
     H = synth.WORKLOADS[3].shape.hidden
     P.log(f"large decode T={T}: all tokens")
