@@ -1427,8 +1427,9 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // workgroup = one 128-row tile x 128 gate+up columns (or 256 down columns);
 // wave w owns 32 (64) of the columns for all 128 rows (4 x 2 accumulators of
 // 32x32).  Per 64-wide K group, the token rows (A, fp16) and each wave's
-// weight codes and scales (B) are copied into a 3-stage LDS ring by LDS DMA
-// two groups ahead, so the only wait in the loop is one barrier per group.
+// weight codes and scales (B) are copied into an NST-stage LDS ring by LDS
+// DMA NST - 1 groups ahead (gate/up 2 stages, down 3), so the only wait in
+// the loop is one barrier per group.
 // A is stored unpadded (128 B rows) with the 16-byte segments of row r
 // XOR-swizzled by (r >> 1) & 7: the 64 LDS banks span two rows, and the MFMA
 // operand reads (16 consecutive rows per 16 lanes) are then bank-conflict
@@ -1612,9 +1613,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
   }
   // fp32 slot rows through LDS as well, 64 rows at a time: per wave 64 rows x
   // 64 columns (rows padded to 72 floats, so rows r and r + 4 use different
-  // banks), then 16-byte stores of the 256-byte row segments.
+  // banks), then 16-byte stores of the 256-byte row segments (the down
+  // launch's 3-stage ring holds them; the gate/up instantiation never gets
+  // here)
   constexpr int RD = 72;
-  static_assert(kWideWaves * 64 * RD * 4 <= NST * STAGE * 2, "staging fits the ring");
+  static_assert(UP || kWideWaves * 64 * RD * 4 <= NST * STAGE * 2, "staging fits the ring");
   float* stf = reinterpret_cast<float*>(ring) + wave * (64 * RD);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -2604,8 +2607,11 @@ hipError_t launch_mfma_up(const LayerDev& d, int T, hipStream_t s) {
   // one workgroup per unit (an upper bound: the shared expert's tiles take
   // its column blocks, every other tile the routed ones).  4 waves (128
   // columns): measured faster than 8 waves (256 columns), which halve the
-  // token-row reads but leave one workgroup per CU.
-  hipLaunchKernelGGL((mfma_wide_kernel<true, kWideWaves>), dim3(wide_grid<true>(d, T, nt)),
+  // token-row reads but leave one workgroup per CU.  A 2-stage ring (52 KB
+  // of LDS): two of these workgroups then fit a CU beside a streaming one
+  // (the 256-token stack at hidden 7168: 7.46 against 7.75 ms per step;
+  // prefill unchanged).
+  hipLaunchKernelGGL((mfma_wide_kernel<true, kWideWaves, 2>), dim3(wide_grid<true>(d, T, nt)),
                      dim3(64 * kWideWaves), 0, s, m);
   return hipGetLastError();
 }
