@@ -392,10 +392,9 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
   // prediction orders that layer's work and, with a cache there, prefetches
   // its experts on that context's copy stream while this layer computes.
   // It reads x before the combine writes y, so y may alias x.  Without a
-  // prefetch to start it runs after this layer's streaming launches, where
-  // the main stream waits for the matrix-core stream anyway, instead of
-  // ahead of the experts (the stack: about 40 us per layer off the critical
-  // path).
+  // prefetch to start it runs after this layer's streaming launches, beside
+  // the longer wide matrix-core path, instead of ahead of the experts (the
+  // stack: about 40 us per layer off the critical path).
   const bool la_early = next && next->d.slot_of && (next->cache_flags & MOE_CACHE_PREFETCH);
   if (la_early) {
     e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
@@ -412,43 +411,45 @@ static int forward_impl(moe_ctx* ctx, const LayerDev& d, const void* x, int32_t 
       next->pf_pending = true;
     }
   }
-  // Wide matrix-core work (experts with many rows) runs on the context's side
-  // stream, concurrently with the streaming launches, which also carry the
-  // narrow matrix-core tiles; the two touch disjoint slots.  Decode-sized
-  // batches need no wide work and so no fork or join.
+  // Wide matrix-core work (experts with many rows) runs concurrently with
+  // the streaming launches, which also carry the narrow matrix-core tiles;
+  // the two touch disjoint slots.  The wide launches stay on the caller's
+  // stream and the streaming ones move to the context's side stream behind
+  // a fork: the wide gate/up launch, the longer path, then reaches the CUs
+  // first (the 256-token stack at hidden 7168: 7.40 against 7.49 ms per
+  // step).  Decode-sized batches need no wide work and so no fork or join.
   const bool mf = mfma_needed(d, n_tokens);
-  hipStream_t ms = s;
+  hipStream_t gs = s;   // the streaming launches' stream
   if (mf) {
-    ms = ctx->side;
+    gs = ctx->side;
     if ((e = hipEventRecord(ctx->fork, s)) != hipSuccess ||
-        (e = hipStreamWaitEvent(ms, ctx->fork, 0)) != hipSuccess)
-      return hip_fail(ctx, e, "forking the matrix-core stream");
-    mark(3, 0, ms);
-    e = launch_mfma_up(d, n_tokens, ms);
+        (e = hipStreamWaitEvent(gs, ctx->fork, 0)) != hipSuccess)
+      return hip_fail(ctx, e, "forking the streaming stream");
+    mark(3, 0, s);
+    e = launch_mfma_up(d, n_tokens, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core gate/up launch");
-    mark(3, 1, ms);
-    mark(4, 0, ms);
-    e = launch_mfma_down(d, n_tokens, ms);
+    mark(3, 1, s);
+    mark(4, 0, s);
+    e = launch_mfma_down(d, n_tokens, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "matrix-core down launch");
-    mark(4, 1, ms);
-    if ((e = hipEventRecord(ctx->join, ms)) != hipSuccess)
-      return hip_fail(ctx, e, "joining the matrix-core stream");
+    mark(4, 1, s);
   }
-  mark(1, 0, s);
-  e = launch_gemv_up(d, n_tokens, s);
+  mark(1, 0, gs);
+  e = launch_gemv_up(d, n_tokens, gs);
   if (e != hipSuccess) return hip_fail(ctx, e, "streaming gate/up launch");
-  mark(1, 1, s);
-  mark(2, 0, s);
-  e = launch_gemv_down(d, n_tokens, s);
+  mark(1, 1, gs);
+  mark(2, 0, gs);
+  e = launch_gemv_down(d, n_tokens, gs);
   if (e != hipSuccess) return hip_fail(ctx, e, "streaming down launch");
-  mark(2, 1, s);
+  mark(2, 1, gs);
   if (next && !la_early) {
-    e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, s);
+    e = launch_router(next->d, xin, f32, n_tokens, 2, nullptr, nullptr, nullptr, gs);
     if (e != hipSuccess) return hip_fail(ctx, e, "lookahead router launch");
   }
   if (mf) {
-    if ((e = hipStreamWaitEvent(s, ctx->join, 0)) != hipSuccess)
-      return hip_fail(ctx, e, "joining the matrix-core stream");
+    if ((e = hipEventRecord(ctx->join, gs)) != hipSuccess ||
+        (e = hipStreamWaitEvent(s, ctx->join, 0)) != hipSuccess)
+      return hip_fail(ctx, e, "joining the streaming stream");
   }
   mark(5, 0, s);
   e = launch_combine(d, n_tokens, reinterpret_cast<const float*>(d.ws + d.L.p), residual, y, s);
