@@ -1428,8 +1428,8 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // wave w owns 32 (64) of the columns for all 128 rows (4 x 2 accumulators of
 // 32x32).  Per 64-wide K group, the token rows (A, fp16) and each wave's
 // weight codes and scales (B) are copied into an NST-stage LDS ring by LDS
-// DMA NST - 1 groups ahead (gate/up 2 stages, down 3), so the only wait in
-// the loop is one barrier per group.
+// DMA NST - 1 groups ahead (2 stages, 52 KB: two workgroups fit a CU beside
+// a streaming one), so the only wait in the loop is one barrier per group.
 // A is stored unpadded (128 B rows) with the 16-byte segments of row r
 // XOR-swizzled by (r >> 1) & 7: the 64 LDS banks span two rows, and the MFMA
 // operand reads (16 consecutive rows per 16 lanes) are then bank-conflict
@@ -1611,34 +1611,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void mfma_wide_kernel(MfmaArgs a) 
     }
     return;
   }
-  // fp32 slot rows through LDS as well, 64 rows at a time: per wave 64 rows x
-  // 64 columns (rows padded to 72 floats, so rows r and r + 4 use different
-  // banks), then 16-byte stores of the 256-byte row segments (the down
-  // launch's 3-stage ring holds them; the gate/up instantiation never gets
-  // here)
+  // fp32 slot rows through LDS as well, CH rows at a time (64, or 32 when
+  // the ring cannot hold 64): per wave CH rows x 64 columns (rows padded to
+  // 72 floats, so rows r and r + 4 use different banks), then 16-byte stores
+  // of the 256-byte row segments
   constexpr int RD = 72;
-  static_assert(UP || kWideWaves * 64 * RD * 4 <= NST * STAGE * 2, "staging fits the ring");
-  float* stf = reinterpret_cast<float*>(ring) + wave * (64 * RD);
+  constexpr int CH = kWideWaves * 64 * RD * 4 <= NST * STAGE * 2 ? 64 : 32;
+  constexpr int MBC = CH / 32;   // 32-row blocks per chunk
+  static_assert(UP || kWideWaves * CH * RD * 4 <= NST * STAGE * 2, "staging fits the ring");
+  float* stf = reinterpret_cast<float*>(ring) + wave * (CH * RD);
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (half * 2 < nmb) {
-      __syncthreads();    // the ring (or the previous half) is no longer read
+  for (int ch = 0; ch < kMfmaBM / CH; ++ch) {
+    if (ch * MBC < nmb) {
+      __syncthreads();    // the ring (or the previous chunk) is no longer read
       if (won) {
 #pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
-          if (half * 2 + m2 < nmb) {
+        for (int m2 = 0; m2 < MBC; ++m2) {
+          if (ch * MBC + m2 < nmb) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
               const int row = m2 * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
 #pragma unroll
-              for (int nb = 0; nb < 2; ++nb) stf[row * RD + nb * 32 + l32] = acc[half * 2 + m2][nb][j];
+              for (int nb = 0; nb < 2; ++nb) stf[row * RD + nb * 32 + l32] = acc[ch * MBC + m2][nb][j];
             }
           }
         }
       }
       __syncthreads();
       if (won) {
-        const int r0 = half * 64, nr = min(64, mrows - r0);
+        const int r0 = ch * CH, nr = min(CH, mrows - r0);
         for (int i = lane; i < nr * 16; i += 64) {
           const int row = i >> 4, q = i & 15;
           const float4 v = *reinterpret_cast<const float4*>(stf + row * RD + q * 4);
@@ -2610,7 +2611,7 @@ hipError_t launch_mfma_up(const LayerDev& d, int T, hipStream_t s) {
   // token-row reads but leave one workgroup per CU.  A 2-stage ring (52 KB
   // of LDS): two of these workgroups then fit a CU beside a streaming one
   // (the 256-token stack at hidden 7168: 7.46 against 7.75 ms per step;
-  // prefill unchanged).
+  // prefill unchanged; the down launch likewise, 7.38 against 7.46 ms).
   hipLaunchKernelGGL((mfma_wide_kernel<true, kWideWaves, 2>), dim3(wide_grid<true>(d, T, nt)),
                      dim3(64 * kWideWaves), 0, s, m);
   return hipGetLastError();
@@ -2620,7 +2621,7 @@ hipError_t launch_mfma_down(const LayerDev& d, int T, hipStream_t s) {
   const int nt = mfma_tiles_max(d, T);
   if (nt == 0) return hipSuccess;
   const MfmaArgs m = mfma_args(d, T);
-  hipLaunchKernelGGL((mfma_wide_kernel<false, kWideWaves>), dim3(wide_grid<false>(d, T, nt)),
+  hipLaunchKernelGGL((mfma_wide_kernel<false, kWideWaves, 2>), dim3(wide_grid<false>(d, T, nt)),
                      dim3(64 * kWideWaves), 0, s, m);
   return hipGetLastError();
 }
