@@ -303,6 +303,10 @@ def run_stack(args, dev):
     # milliseconds of GPU work, so launching eagerly costs nothing measurable
     kdom, _, el = profiled(layers, step, args.steps, timed=True, slots=(dom,))
     us_step = el * 1e6 / args.steps
+    # the same steps captured in one HIP graph and replayed: no launch gaps
+    # and no event pairs (the library records no timing events inside a
+    # capture), so this is reported beside the headline, not as it
+    g_el, _ = timed_graph(step, args.steps)
     rmin, rwide = layers[0].mfma_min_rows, layers[0].wide_min_rows
     work = [kernel_work(c, sh, T, rmin, rwide) for c in counts]
     distinct = [int((c > 0).sum()) for c in counts]
@@ -323,6 +327,10 @@ def run_stack(args, dev):
         kernel_us_per_step={k: round(share[k] * 1e3, 2) for k in KERNELS},
         kernel_timing=f"{n_prof} untimed eager steps with event pairs around every kernel; "
                       f"the roofline kernel ({dom}) from its event pairs in the timed steps",
+        graph={"tokens_s": round(T * args.steps / g_el, 1),
+               "us_per_step": round(g_el * 1e6 / args.steps, 1),
+               "what": f"the same {args.steps} steps captured in one HIP graph, replayed once "
+                       "untimed and once timed (HIP events, no kernel event pairs)"},
         distinct_experts_per_layer=distinct,
         rows_top_expert_per_layer=[int(c.max()) for c in counts],
         wide_experts_per_layer=[int((c >= rwide).sum()) for c in counts])
