@@ -961,10 +961,11 @@ __device__ void topk_select(const RouterArgs& a, float* s_lg, int* s_ids, int nt
   }
 }
 
-// Router GEMV on the matrix cores, for large batches.  Workgroup = (64-expert
-// row block, k-split of kRouterGPW groups, 64-token tile); wave w owns tokens
-// 32 (w & 1) .. +31 (one 32-row MFMA block) against experts 32 (w >> 1) ..
-// +31.  Per 64-wide group the token rows are converted to fp16 (the 8-bit
+// Router GEMV on the matrix cores, for large batches.  Workgroup = (block of
+// kRmExperts experts, k-split of kRouterGPW groups, 64-token tile); wave w
+// owns tokens 32 (w & 1) .. +31 (one 32-row MFMA block) against experts
+// 32 (w >> 1) .. +31 of the block.  128 experts per workgroup (8 waves): the
+// token rows are read once per 128 experts instead of once per 64.  Per 64-wide group the token rows are converted to fp16 (the 8-bit
 // pair order) into an LDS double buffer, the next groups' rows and codes being
 // loaded meanwhile; B is the centred codes (q - 128, exact in fp16), and the
 // group's products are folded into the logits as s * P + (b + 128 s) * sum(x)
@@ -973,8 +974,11 @@ __device__ void topk_select(const RouterArgs& a, float* s_lg, int* s_ids, int nt
 // fp16 exactly.  Writes the same k-split partials; the eb == 0 workgroups also
 // publish x16 (the hi half) and the streaming path's group sums over it.
 constexpr int kRmTok = 64;   // tokens per matrix-core router tile
+constexpr int kRmWaves = 8;  // waves per workgroup: 16 x kRmWaves experts
+constexpr int kRmThreads = 64 * kRmWaves;
+constexpr int kRmExperts = 16 * kRmWaves;
 template <bool F32>
-__global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
+__global__ __launch_bounds__(kRmThreads) void router_mfma_kernel(RouterArgs a) {
   constexpr int NP = F32 ? 2 : 1;                          // fp16 planes: hi [, lo]
   __shared__ __align__(16) uint16_t xa[2][NP][kRmTok * 64];   // fp16 x, 8-bit pair order, swizzled
   __shared__ __align__(16) float xsum[2][kRmTok];             // per-token group sums (hi + lo)
@@ -984,12 +988,12 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
   const int t0 = tb * kRmTok, nt = min(kRmTok, a.T - t0);
   const int g0 = ks * kRouterGPW, ng = min(kRouterGPW, a.G - g0);
   const bool wx = a.write_x && eb == 0;
-  // x chunks of this thread: chunk c = tid + 256 j (j < 2) is token c / 8,
+  // x chunks of this thread: chunk c = tid + kRmThreads j (j < NCH) is token c / 8,
   // columns 8 (c % 8) .. +7 of the group; the 8 chunks of a token are 8
   // consecutive lanes.  Rows past the batch repeat its last token (their
   // logits are not written).  The group loop is unrolled, so each group's
   // chunks have registers of their own; they are loaded LA groups ahead.
-  constexpr int NCH = kRmTok * 8 / 256;
+  constexpr int NCH = kRmTok * 8 / kRmThreads;
   constexpr int NV = F32 ? 2 : 1;        // 16-byte loads per chunk
   constexpr int LA = F32 ? 3 : 4;        // groups loaded ahead
   typedef uint32_t u4v __attribute__((ext_vector_type(4)));
@@ -997,7 +1001,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
   auto load_x = [&](int gl) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = tid + 256 * j, t = min(c >> 3, nt - 1), r = c & 7;
+      const int c = tid + kRmThreads * j, t = min(c >> 3, nt - 1), r = c & 7;
       const size_t off = (size_t)(t0 + t) * a.H + (size_t)(g0 + gl) * 64 + r * 8;
       if (F32) {
         const u4v* src = reinterpret_cast<const u4v*>(static_cast<const float*>(a.x) + off);
@@ -1015,7 +1019,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
   auto stage_x = [&](int gl, int buf) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = tid + 256 * j, t = c >> 3, r = c & 7, c8 = r * 8;
+      const int c = tid + kRmThreads * j, t = c >> 3, r = c & 7, c8 = r * 8;
       float v[8];
       if (F32) {
         const u4v p0 = raw[gl][j][0], p1 = raw[gl][j][NV - 1];
@@ -1067,10 +1071,14 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
       }
     }
   };
-  // B: this lane's expert (row 32 (w >> 1) + l32 of the tile row block) and
-  // 8-byte half hi of each 16-column chunk
+  // B: this lane's expert (row 32 (w >> 1) + l32 of the workgroup's
+  // kRmExperts, in 64-row tile block 2 eb + (brow >> 6)) and 8-byte half hi
+  // of each 16-column chunk; a wave whose experts lie past Epad (an odd count
+  // of 64-row blocks) loads block 0's rows and writes nothing
   const int brow = 32 * (wave >> 1) + l32;
-  const uint8_t* btile = a.router + ((size_t)eb * a.G + g0) * kQ8TileBytes;
+  const int bblk = eb * (kRmExperts / 64) + (brow >> 6);
+  const bool bon = bblk * 64 < a.Epad;
+  const uint8_t* btile = a.router + ((size_t)(bon ? bblk : 0) * a.G + g0) * kQ8TileBytes;
   const int m = 32 * (wave & 1) + l32;   // this lane's token row in the A operand
   const Lift L;
   f32x16 lg;
@@ -1082,11 +1090,11 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
     const uint8_t* tile = btile + (size_t)gl * kQ8TileBytes;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint2 v = *reinterpret_cast<const uint2*>(tile + kk * 1024 + brow * 16 + hi * 8);
+      const uint2 v = *reinterpret_cast<const uint2*>(tile + kk * 1024 + (brow & 63) * 16 + hi * 8);
       cd[gl][kk][0] = v.x;
       cd[gl][kk][1] = v.y;
     }
-    sbq[gl] = ld4(tile + kQ8CodeBytes + brow * 4);
+    sbq[gl] = ld4(tile + kQ8CodeBytes + (brow & 63) * 4);
   };
 #pragma unroll
   for (int gl = 0; gl < LA - 1; ++gl)
@@ -1139,7 +1147,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(RouterArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int mo = 32 * (wave & 1) + 8 * (j >> 2) + 4 * hi + (j & 3);
-    if (mo < nt) a.part[((size_t)ks * a.T + t0 + mo) * a.Epad + eb * 64 + brow] = lg[j];
+    if (bon && mo < nt) a.part[((size_t)ks * a.T + t0 + mo) * a.Epad + eb * kRmExperts + brow] = lg[j];
   }
 }
 
@@ -2360,11 +2368,11 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   a.cap_up = d.L.cap_up;
   a.cap_dn = d.L.cap_dn;
   if (T >= kRmTok) {   // large batches: the GEMV on the matrix cores
-    const dim3 grid(a.n_rb, a.KS, (T + kRmTok - 1) / kRmTok);
+    const dim3 grid((d.Epad + kRmExperts - 1) / kRmExperts, a.KS, (T + kRmTok - 1) / kRmTok);
     if (x_f32)
-      hipLaunchKernelGGL(router_mfma_kernel<true>, grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(router_mfma_kernel<true>, grid, dim3(kRmThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(router_mfma_kernel<false>, grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(router_mfma_kernel<false>, grid, dim3(kRmThreads), 0, s, a);
   } else
     hipLaunchKernelGGL(router_gemv_kernel, dim3(a.n_rb, a.KS, a.n_tb), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
