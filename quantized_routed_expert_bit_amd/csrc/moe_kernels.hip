@@ -891,9 +891,9 @@ __device__ __forceinline__ uint32_t pick(uint32_t m, uint32_t a, uint32_t b) {
 // (ties go to the lowest index), and shifts the winning lane's list by one.
 // The softmax over the selected logits is summed in selection order; the
 // token's LDS row is reused for the exponentials.
-template <int LPT, int NV>
+template <int LPT, int NV, int NT>
 __device__ void topk_select(const RouterArgs& a, float* s_lg, int* s_ids, int nt, int t0) {
-  constexpr int NG = 256 / LPT;             // token groups per workgroup
+  constexpr int NG = NT / LPT;              // token groups per workgroup
   constexpr uint32_t kNone = 0xFFFFFFFFu;   // index of an exhausted list entry
   const int tid = threadIdx.x, l = tid % LPT;
   for (int t = tid / LPT; t < nt; t += NG) {
@@ -1151,66 +1151,77 @@ __global__ __launch_bounds__(kRmThreads) void router_mfma_kernel(RouterArgs a) {
   }
 }
 
-// Top-k: workgroup = tpw tokens (tpw * Epad <= 4096).  Sums the k-split
-// partials in fixed (split-ascending) order, adds the logit bias, then selects
-// k experts per token by (logit desc, index asc) and takes the softmax over
-// them.  A batch that one workgroup covers (decode) is bucketed in the same
-// launch.  LPT/NV: lanes per token and logits per lane (LPT * NV >= Epad).
-template <int LPT, int NV>
-__global__ __launch_bounds__(256) void router_topk_kernel(RouterArgs a, int tpw) {
+// Top-k: workgroup = tpw tokens (tpw * Epad <= 4096) on NT threads.  Sums the
+// k-split partials in fixed (split-ascending) order, adds the logit bias, then
+// selects k experts per token by (logit desc, index asc) and takes the softmax
+// over them.  A batch that one workgroup covers (decode) is bucketed in the
+// same launch; there 512 or 1024 threads give each of up to 16 tokens its own
+// wave and load all partials in one round.  LPT/NV: lanes per token and logits
+// per lane (LPT * NV >= Epad).
+template <int LPT, int NV, int NT>
+__global__ __launch_bounds__(NT) void router_topk_kernel(RouterArgs a, int tpw) {
   __shared__ float s_lg[4096];
   __shared__ int s_ids[kRouterTokMax * kMaxTopK];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * tpw;
   const int nt = min(tpw, a.T - t0);
   const int npair = nt * a.Epad;
-  // every load unconditional (indices clamped into the buffer), so a batch of
-  // 8 pairs x 8 splits is in flight at once (one batch for 16 tokens x 128
-  // experts)
-  constexpr int NP = 8;
-  for (int p0 = 0; p0 < npair; p0 += 256 * NP) {
-    float acc[NP];
-    int pt[NP], pe[NP];
+  // every load unconditional (indices clamped into the buffer), so NP pairs x
+  // KC splits are in flight at once: 8 x 8, or 4 x 16 where a thread has at
+  // most 4 pairs and 16 splits cover K (one round instead of two for 512
+  // experts at hidden 7168)
+  auto sum_parts = [&](auto np_c, auto kc_c) {
+    constexpr int NP = decltype(np_c)::value, KC = decltype(kc_c)::value;
+    for (int p0 = 0; p0 < npair; p0 += NT * NP) {
+      float acc[NP];
+      int pt[NP], pe[NP];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      acc[j] = 0.f;
-      const int i = min(p0 + tid + 256 * j, npair - 1);
-      pt[j] = i / a.Epad;
-      pe[j] = i - pt[j] * a.Epad;
-    }
-    for (int k0 = 0; k0 < a.KS; k0 += 8) {
-      float pv[NP][8];
+      for (int j = 0; j < NP; ++j) {
+        acc[j] = 0.f;
+        const int i = min(p0 + tid + NT * j, npair - 1);
+        pt[j] = i / a.Epad;
+        pe[j] = i - pt[j] * a.Epad;
+      }
+      for (int k0 = 0; k0 < a.KS; k0 += KC) {
+        float pv[NP][KC];
 #pragma unroll
-      for (int j = 0; j < NP; ++j)
+        for (int j = 0; j < NP; ++j)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int ks = min(k0 + q, a.KS - 1);
-          pv[j][q] = a.part[((size_t)ks * a.T + t0 + pt[j]) * a.Epad + pe[j]];
+          for (int q = 0; q < KC; ++q) {
+            const int ks = min(k0 + q, a.KS - 1);
+            pv[j][q] = a.part[((size_t)ks * a.T + t0 + pt[j]) * a.Epad + pe[j]];
+          }
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+#pragma unroll
+          for (int q = 0; q < KC; ++q) acc[j] += k0 + q < a.KS ? pv[j][q] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int i = p0 + tid + NT * j;
+        if (i < npair) {
+          const int t = pt[j], e = pe[j];
+          float v = -INFINITY;
+          if (e < a.E) {
+            const float sum = a.bias ? acc[j] + a.bias[e] : acc[j];
+            if (a.mode == 1) a.logits_out[(size_t)(t0 + t) * a.E + e] = sum;
+            // a NaN logit (out of contract) ranks last; -0 ranks as +0
+            v = sum == sum ? sum + 0.f : -INFINITY;
+          }
+          s_lg[i] = v;
         }
-#pragma unroll
-      for (int j = 0; j < NP; ++j)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[j] += k0 + q < a.KS ? pv[j][q] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int i = p0 + tid + 256 * j;
-      if (i < npair) {
-        const int t = pt[j], e = pe[j];
-        float v = -INFINITY;
-        if (e < a.E) {
-          const float sum = a.bias ? acc[j] + a.bias[e] : acc[j];
-          if (a.mode == 1) a.logits_out[(size_t)(t0 + t) * a.E + e] = sum;
-          // a NaN logit (out of contract) ranks last; -0 ranks as +0
-          v = sum == sum ? sum + 0.f : -INFINITY;
-        }
-        s_lg[i] = v;
       }
     }
-  }
+  };
+  // (either shape is correct for any batch; 1024 threads keep to the first,
+  // which fits their 128 registers)
+  if (NT == 1024 || (npair <= 4 * NT && a.KS <= 16))
+    sum_parts(std::integral_constant<int, 4>{}, std::integral_constant<int, 16>{});
+  else if constexpr (NT != 1024)
+    sum_parts(std::integral_constant<int, 8>{}, std::integral_constant<int, 8>{});
   if (a.mode == 1) return;
   __syncthreads();
-  topk_select<LPT, NV>(a, s_lg, s_ids, nt, t0);
+  topk_select<LPT, NV, NT>(a, s_lg, s_ids, nt, t0);
   if (a.mode == 2 && blockIdx.x == 0 && tid == 0) a.misc[kPredValid] = a.T * a.k;
   if (a.mode == 0 && gridDim.x == 1) {   // at most kRouterTokMax * kMaxTopK = 512 slots
     __shared__ __align__(16) uint8_t smem[kBucketWaveSmem];
@@ -2386,13 +2397,19 @@ hipError_t launch_router(const LayerDev& d, const void* x, int x_f32, int T, int
   if (T >= kRmTok && tpw > T / 128) tpw = T / 128 > 1 ? T / 128 : 1;
   const int n_wg = (T + tpw - 1) / tpw;
   // a 16-lane group per token where the logits fit 8 per lane and the k
-  // winners fit the group's lanes; else the whole wave
+  // winners fit the group's lanes; else the whole wave.  One workgroup with
+  // more tokens than waves (512 experts at 5 to 8 tokens): a wave per token,
+  // and 1024 threads where that loads every partial in one round (8 tokens
+  // at hidden 7168: two selection rounds and four load rounds become one each)
+  const int nt1 = T < tpw ? T : tpw;
   if (d.Epad <= 128 && d.k <= 16)
-    hipLaunchKernelGGL((router_topk_kernel<16, 8>), dim3(n_wg), dim3(256), 0, s, a, tpw);
+    hipLaunchKernelGGL((router_topk_kernel<16, 8, 256>), dim3(n_wg), dim3(256), 0, s, a, tpw);
+  else if (d.Epad <= 512 && n_wg == 1 && nt1 > 4)
+    hipLaunchKernelGGL((router_topk_kernel<64, 8, 1024>), dim3(n_wg), dim3(1024), 0, s, a, tpw);
   else if (d.Epad <= 512)
-    hipLaunchKernelGGL((router_topk_kernel<64, 8>), dim3(n_wg), dim3(256), 0, s, a, tpw);
+    hipLaunchKernelGGL((router_topk_kernel<64, 8, 256>), dim3(n_wg), dim3(256), 0, s, a, tpw);
   else
-    hipLaunchKernelGGL((router_topk_kernel<64, 16>), dim3(n_wg), dim3(256), 0, s, a, tpw);
+    hipLaunchKernelGGL((router_topk_kernel<64, 16, 256>), dim3(n_wg), dim3(256), 0, s, a, tpw);
   e = hipGetLastError();
   if (e != hipSuccess || mode != 0 || n_wg == 1) return e;   // one workgroup buckets itself
   hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kBucketThreads), 0, s, a);

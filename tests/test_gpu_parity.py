@@ -131,6 +131,7 @@ def test_streaming_unit_layouts(torch_dev):
     dict(H=192, E=8, k=1, I=192, Is=64, T=33),       # k = 1, many tokens per expert
     dict(H=64, E=1, k=1, I=64, Is=0, T=3),           # single expert
     dict(H=128, E=16, k=3, I=128, Is=64, T=201),     # bucketing pass, 603 slots (not a multiple of 4)
+    dict(H=640, E=200, k=6, I=128, Is=64, T=13),     # top-k: one 1024-thread workgroup, a wave per token
 ])
 def test_layer_parity_edge_shapes(torch_dev, shape):
     H, E, k, I, Is, T = (shape[n] for n in ("H", "E", "k", "I", "Is", "T"))

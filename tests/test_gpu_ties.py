@@ -4,8 +4,9 @@ wins.  A zero router (every code 128 with bias -128 * scale, so every weight
 is exactly 0) makes every logit equal to the router bias, exactly, on both
 sides; the GPU's ids must then equal the oracle's element by element, in
 order, and p the softmax of the selected biases.  Covers each top-k variant
-(16-lane groups for up to 128 experts, the whole wave up to 512, 16 logits
-per lane beyond) and the multi-workgroup bucketing pass."""
+(16-lane groups for up to 128 experts, the whole wave up to 512 (one
+workgroup of 1024 threads for 5 to 16 tokens), 16 logits per lane beyond)
+and the multi-workgroup bucketing pass."""
 import numpy as np
 import pytest
 
@@ -41,6 +42,7 @@ SHAPES = [
     dict(H=2816, E=128, k=8, I=704, Is=2112, T=16),    # the decode layer's shape
     dict(H=256, E=128, k=8, I=128, Is=128, T=300),     # several top-k workgroups + bucketing pass
     dict(H=256, E=512, k=16, I=128, Is=128, T=8),      # whole-wave groups
+    dict(H=256, E=256, k=8, I=128, Is=128, T=16),      # a wave per token, 16 waves
     dict(H=128, E=1000, k=32, I=64, Is=0, T=5),        # 16 logits per lane
 ]
 
