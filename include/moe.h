@@ -77,7 +77,7 @@
  * written or freed.  All device work of a call is ordered on the caller's
  * hipStream_t (passed as void*, NULL = the null stream): it starts after work
  * already enqueued there and finishes before work enqueued later.  Inside a
- * forward, the 128-row matrix-core kernels (batches with experts of 32+ rows)
+ * forward, the 128-row matrix-core kernels (batches with experts of 24+ rows)
  * run on a stream the context owns, forked
  * from and joined back into the caller's stream with events (so a forward can
  * be captured into a HIP graph).  moe_forward performs no host synchronisation
@@ -238,8 +238,8 @@ int moe_router_logits(moe_ctx *ctx, const void *x, int32_t x_dtype, int32_t n_to
  * tokens routed to it in one forward (T for the shared expert).  Rows below
  * mfma_min_rows take the streaming dot-product path; rows in
  * [mfma_min_rows, wide_min_rows) take the matrix-core path in 32-row tiles;
- * rows >= wide_min_rows take it in 128-row tiles.  Defaults: 4 and 32, or 3
- * and 32 when hidden >= 4096.
+ * rows >= wide_min_rows take it in 128-row tiles.  Defaults: 4 and 24, or 3
+ * and 24 when hidden >= 4096.
  * mfma_min_rows = 1 sends every expert to the matrix cores; values above
  * max_tokens keep them all on the streaming path.  Never changes the selected
  * experts.  Errors: MOE_EINVAL unless 1 <= mfma_min_rows <= wide_min_rows. */

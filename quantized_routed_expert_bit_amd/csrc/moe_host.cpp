@@ -195,7 +195,11 @@ int moe_open(const moe_config* cfg, moe_ctx** out) {
   // tiles for 2-row experts: 64 tokens 2003 against 2165 us per forward
   // (3 or more rows on the tiles), the 256-token stack 7.79 against 7.97 ms.
   d.mfma_min_rows = cfg->hidden >= 4096 ? 3 : 4;
-  d.wide_min_rows = 32;
+  // 128-row tiles from 24 rows: the 256-token stack 7.03 against 7.08 ms per
+  // step (eager; 20, 28 and 32 rows all slower), 16 x 128 prefill chunks
+  // 2.25-2.27 against 2.29 ms, the 64-token layer and the 2048-token grouped
+  // prefill within noise.
+  d.wide_min_rows = 24;
   d.L = ws_layout(*cfg);
   if (hipSetDevice(cfg->device) != hipSuccess ||
       hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||

@@ -40,7 +40,7 @@ class MoELayer:
             raise MoEError(rc, f"moe_open: {self.lib.moe_strerror(rc).decode()}")
         self.workspace_bytes = int(self.lib.moe_workspace_bytes(ctypes.byref(self.cfg)))
         # the library's defaults
-        self.mfma_min_rows, self.wide_min_rows = (3 if hidden >= 4096 else 4), 32
+        self.mfma_min_rows, self.wide_min_rows = (3 if hidden >= 4096 else 4), 24
         self._keep = ()
 
     def _check(self, rc, what):

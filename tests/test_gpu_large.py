@@ -74,12 +74,14 @@ def large_layer(torch_dev):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("T", [1, 8, 24, 64])
+@pytest.mark.parametrize("T", [1, 8, 20, 24, 64])
 def test_large_decode_layer_every_token(torch_dev, large_layer, T):
     """Every token of each batch; from 8 tokens the routed experts with 3 to
-    31 rows run as 32-row matrix-core tiles over a 112-group K chain (split by
-    K at 8 tokens, by columns from 24; at 24 the shared expert's 24 rows take
-    those tiles too), the ones with 1 or 2 rows on the streaming path."""
+    23 rows run as 32-row matrix-core tiles over a 112-group K chain (split by
+    K at 8 tokens, by columns at 20, 24 and 64), the ones with 1 or 2 rows on
+    the streaming path.  At 20 tokens the shared expert's 20 rows take those
+    tiles too; from 24 it runs as a 128-row tile on the wide kernels, beside
+    the streaming launches, as does every routed expert with 24 or more rows."""
     m, ol = large_layer
     H = synth.WORKLOADS[3].shape.hidden
     P.log(f"large decode T={T}: all tokens")
@@ -88,7 +90,8 @@ def test_large_decode_layer_every_token(torch_dev, large_layer, T):
     ids_np = ids.cpu().numpy()
     cnt = np.bincount(ids_np.reshape(-1), minlength=512)
     P.log(f"  {int((cnt > 0).sum())} experts, rows per expert max {cnt.max()}, "
-          f"{int(((cnt >= 3) & (cnt < 32)).sum())} with 3-31 rows")
+          f"{int(((cnt >= m.mfma_min_rows) & (cnt < m.wide_min_rows)).sum())} on 32-row tiles, "
+          f"{int((cnt >= m.wide_min_rows).sum())} on 128-row tiles")
     with P.oracle_pool() as pool:
         P.check_forward(ol, oracle.bf16_bits_to_f64(xb), y.cpu().numpy(), ids_np,
                         p.cpu().numpy(), f"large T={T}", pool=pool)
@@ -159,7 +162,7 @@ def test_stack_full_layer_on_gpu_residual(torch_dev, stack, layer):
     ids_np = ids.cpu().numpy()
     cnt = np.bincount(ids_np.reshape(-1), minlength=512)
     P.log(f"stack layer {layer}: {int((cnt > 0).sum())} experts, top expert {cnt.max()} rows, "
-          f"{int((cnt >= 32).sum())} with >= 32 rows")
+          f"{int((cnt >= m.wide_min_rows).sum())} on 128-row tiles")
     xin = oracle.rms_normalize(r.cpu().numpy().astype(np.float64))
     lg = m.router_logits(r).cpu().numpy()
     dl = np.abs(lg - ol.logits(xin))
