@@ -142,16 +142,20 @@ def source_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(name):
+def measured_traffic(name, path_rows):
     """HBM bytes per launch of a kernel on a workload, from the committed
     rocprofv3 FETCH_SIZE + WRITE_SIZE passes (calibrated against a plain copy);
     None once the kernel sources differ from the ones the counters were taken
-    on."""
+    on, or the layers' path thresholds (mfma_min_rows, wide_min_rows: which
+    experts the launch carries) differ from the ones they ran with."""
     path = os.path.join(ROOT, "profiles", name)
     try:
         fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
-                      if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+                      if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ",
+                                          "path_rows: ")))
         if source_sha256() != fields["source_sha256"].strip():
+            return None
+        if [int(v) for v in fields["path_rows"].split()] != [int(v) for v in path_rows]:
             return None
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -315,7 +319,7 @@ def run_stack(args, dev):
     b = float(np.mean([w[dom][0] for w in work]))
     f = float(np.mean([w[dom][1] for w in work]))
     rl = roofline(dom, b, f, kdom[dom] * 1e3)
-    rl["traffic"] = measured_traffic(f"{dom}_stack_hbm_traffic.md")
+    rl["traffic"] = measured_traffic(f"{dom}_stack_hbm_traffic.md", (rmin, rwide))
     res = dict(
         tokens_s=T * args.steps / el, us_per_step=us_step, roofline=rl,
         stack_hbm={"alg_bytes_per_step": int(alg), "GB_s": round(alg / (el / args.steps) / 1e9, 1),
@@ -325,6 +329,7 @@ def run_stack(args, dev):
                     "frac": round(flops / (el / args.steps) / 1e12 / MFMA_F16_PEAK_TFS, 4)},
         kernel_us_per_launch={k: round(v * 1e3, 3) for k, v in kern.items()},
         kernel_us_per_step={k: round(share[k] * 1e3, 2) for k in KERNELS},
+        path_rows=[rmin, rwide],
         kernel_timing=f"{n_prof} untimed eager steps with event pairs around every kernel; "
                       f"the roofline kernel ({dom}) from its event pairs in the timed steps",
         graph={"tokens_s": round(T * args.steps / g_el, 1),
@@ -615,10 +620,12 @@ def run_decode(args, dev, batches=(1, 4, 16), copies=6, keep=False):
                         "layer_frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                         "gemv_up_roofline": roofline("gemv_up", up_b, up_f, kern["gemv_up"] * 1e3),
                         "gemv_down_roofline": roofline("gemv_down", dn_b, dn_f, kern["gemv_down"] * 1e3),
-                        "kernel_us": {k: round(v * 1e3, 3) for k, v in kern.items()}}
+                        "kernel_us": {k: round(v * 1e3, 3) for k, v in kern.items()},
+                        "path_rows": [m0.mfma_min_rows, m0.wide_min_rows]}
         if T == 16:
-            out["T16"]["gemv_up_roofline"]["traffic"] = measured_traffic("gemv_up_decode_T16_hbm_traffic.md")
-            out["T16"]["gemv_down_roofline"]["traffic"] = measured_traffic("gemv_down_decode_T16_hbm_traffic.md")
+            rows = (m0.mfma_min_rows, m0.wide_min_rows)
+            out["T16"]["gemv_up_roofline"]["traffic"] = measured_traffic("gemv_up_decode_T16_hbm_traffic.md", rows)
+            out["T16"]["gemv_down_roofline"]["traffic"] = measured_traffic("gemv_down_decode_T16_hbm_traffic.md", rows)
         log(f"decode T={T}: {out[f'T{T}']}")
     if keep:
         return out, layers
