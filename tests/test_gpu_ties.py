@@ -81,3 +81,30 @@ def test_exact_ties_lowest_index_wins(torch_dev, shape, bias):
     ref = ol.forward(x64, pool=None)
     P.compare_y(y.cpu().numpy(), ref["y"], f"ties {bias}")
     m.close()
+
+
+def test_path_boundaries_exact_rows(torch_dev):
+    """The zero router sends every token to experts 0..k-1, so each of them,
+    and the shared expert, has exactly T rows: T runs across each path
+    boundary at the layer's own thresholds (streaming below mfma_min_rows,
+    32-row tiles below wide_min_rows, then 128-row tiles, one full tile and a
+    second one of a single row), every token against the oracle."""
+    import torch
+    from quantized_routed_expert_bit_amd import MoELayer
+    H, E, k, I, Is = 256, 64, 4, 128, 128
+    li = synth.LayerInputs(21, 87, 0, synth.LayerShape(H, E, k, I, Is), None)
+    router = zero_router(H, E)
+    w = P.upload_layer(li, torch_dev)
+    m = MoELayer(H, E, k, I, Is, 129)
+    m.set_weights(torch.from_numpy(router).to(torch_dev), w["bank"], w["stride"], w["shared"], None)
+    R, W = m.mfma_min_rows, m.wide_min_rows
+    ol = oracle.OracleLayer(H, E, k, I, Is, router, None, li.record, li.shared_record())
+    for T in (R - 1, R, W - 1, W, W + 1, 128, 129):
+        P.log(f"path boundaries: T={T} (R={R}, W={W})")
+        xb = synth.make_hidden(21, 87, T, H)
+        y, ids, p = m.forward(P.bf16_tensor(xb, torch_dev), return_selection=True)
+        assert np.array_equal(ids.cpu().numpy(), np.tile(np.arange(k), (T, 1)))
+        assert np.all(np.abs(p.cpu().numpy() - 1.0 / k) <= 1e-7)
+        ref = ol.forward(oracle.bf16_bits_to_f64(xb), pool=None)
+        P.compare_y(y.cpu().numpy(), ref["y"], f"boundary T={T}")
+    m.close()
