@@ -83,7 +83,8 @@ def test_exact_ties_lowest_index_wins(torch_dev, shape, bias):
     m.close()
 
 
-def test_path_boundaries_exact_rows(torch_dev):
+@pytest.mark.parametrize("H", [256, 4096])   # mfma_min_rows 4, and 3 from hidden 4096
+def test_path_boundaries_exact_rows(torch_dev, H):
     """The zero router sends every token to experts 0..k-1, so each of them,
     and the shared expert, has exactly T rows: T runs across each path
     boundary at the layer's own thresholds (streaming below mfma_min_rows,
@@ -91,7 +92,7 @@ def test_path_boundaries_exact_rows(torch_dev):
     second one of a single row), every token against the oracle."""
     import torch
     from quantized_routed_expert_bit_amd import MoELayer
-    H, E, k, I, Is = 256, 64, 4, 128, 128
+    E, k, I, Is = 64, 4, 128, 128
     li = synth.LayerInputs(21, 87, 0, synth.LayerShape(H, E, k, I, Is), None)
     router = zero_router(H, E)
     w = P.upload_layer(li, torch_dev)
