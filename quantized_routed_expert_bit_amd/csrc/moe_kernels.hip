@@ -452,12 +452,11 @@ __device__ void bucket_tokens(const RouterArgs& a, const int* ids, uint8_t* smem
       }
       ++n_mfma;
     } else {
-      if (tid == 0) {
-        a.items[2 * n_gemv] = make_int4(E, a.T, Tk, 0);
-        a.items[2 * n_gemv + 1] = make_int4(Tk, Tk + min(1, a.T - 1), Tk + min(2, a.T - 1),
-                                            Tk + min(3, a.T - 1));
+      if (tid == 0) {   // at the fixed index E, after every routed item
+        a.items[2 * E] = make_int4(E, a.T, Tk, 0);
+        a.items[2 * E + 1] = make_int4(Tk, Tk + min(1, a.T - 1), Tk + min(2, a.T - 1),
+                                       Tk + min(3, a.T - 1));
       }
-      ++n_gemv;
     }
   }
   __syncthreads();
@@ -644,11 +643,10 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
       ++n_mfma;
       if (wide) n_tiles += nt; else n_narrow += nt;
     } else {
-      if (lane == 0) {
-        a.items[2 * n_gemv] = make_int4(E, T, Tk, 0);
-        a.items[2 * n_gemv + 1] = make_int4(Tk, Tk + min(1, T - 1), Tk + min(2, T - 1), Tk + min(3, T - 1));
+      if (lane == 0) {   // at the fixed index E, after every routed item
+        a.items[2 * E] = make_int4(E, T, Tk, 0);
+        a.items[2 * E + 1] = make_int4(Tk, Tk + min(1, T - 1), Tk + min(2, T - 1), Tk + min(3, T - 1));
       }
-      ++n_gemv;
     }
   }
   if (lane < 8) put_unit_counts(a, n_tiles, nts, lane);
@@ -1852,6 +1850,7 @@ struct NarrowGrid {
 // workgroups past this forward's work all sit at the end of the grid.
 __device__ __forceinline__ bool narrow_work(const int* misc, const NarrowGrid& ng, int& b,
                                             int& tile, int& cblk) {
+  if (ng.nsht == 0 && ng.ncbr == 0) return false;   // no 32-row tiles in this launch
   const int nreal = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNNarrow];
   const int nsht = ng.nsht, ncbs = ng.ncbs, ncbr = ng.ncbr;
   const int nrt = max(nreal - nsht, 0);
@@ -1871,22 +1870,18 @@ __device__ __forceinline__ bool narrow_work(const int* misc, const NarrowGrid& n
   return false;
 }
 
-// Which (work item, row block) a streaming workgroup owns.  The grid is flat:
-// the first nsh workgroups are the row blocks of the shared expert (the last
-// streaming item when it streams), started first because it is the largest;
-// then nrb row blocks per routed item.  Returns false for a workgroup past
-// the routed items of this forward.
-__device__ __forceinline__ bool gemv_work(const int* misc, int b, int nsh, int nrb, int& item_i,
-                                          int& rb) {
-  const int n_items = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNGemv];
-  if (b < nsh) {
-    item_i = n_items - 1;
-    rb = b;
-    return item_i >= 0;
-  }
-  item_i = (b - nsh) / nrb;
-  rb = (b - nsh) - item_i * nrb;
-  return item_i < n_items - (nsh > 0 ? 1 : 0);
+// Which (work item, row block) a streaming workgroup owns, from its index
+// alone.  The grid is flat: the first nsh workgroups are the row blocks of the
+// shared expert (item E of the list when it streams), started first because
+// it is the largest; then nrb row blocks per routed item (items 0 .. E - 1).
+// The index needs no memory read, so a workgroup issues its item's load and
+// the read of the live routed-item count together and waits once; it then
+// leaves if it lies past the routed items of this forward.
+__device__ __forceinline__ void gemv_unit(int b, int nsh, int nrb, int E, int& item_i, int& rb) {
+  const bool shb = b < nsh;
+  const int q = shb ? 0 : (b - nsh) / nrb;
+  item_i = shb ? E : min(q, E);
+  rb = shb ? b : (b - nsh) - q * nrb;
 }
 
 // Four wave-uniform values (one per token row of a streaming pass) selected
@@ -1981,9 +1976,14 @@ void gemv_up_kernel(
   float (*red)[kGemvWaves][kGemvTokV2][64] =
       reinterpret_cast<float (*)[kGemvWaves][kGemvTokV2][64]>(dyn);
   int item_i, u;
-  if (!gemv_work(misc, b, nsh, nunits, item_i, u)) return;
+  gemv_unit(b, nsh, nunits, E, item_i, u);
+  // item and live count read together (gemv_unit); the empty statement takes
+  // both, so the compiler cannot wait for the count before issuing the item
   const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + 2 * item_i));
   const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
+  const int n_items = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNGemv];
+  asm volatile("" ::"s"(e), "s"(m), "s"(loff), "s"(n_items));
+  if (b >= nsh && item_i >= n_items) return;
   const bool sh = e == E;
   const int inter = sh ? Is : I;
   const int rb = HALF ? u >> 1 : u, rh = HALF ? u & 1 : 0, nrb_i = inter >> 6;
@@ -2129,9 +2129,14 @@ void gemv_down_kernel(
   const int nrb = H >> 6;
   const int nunits = (nrb + rpu - 1) / rpu;
   int item_i, u;
-  if (!gemv_work(misc, b, nsh, nunits, item_i, u)) return;
+  gemv_unit(b, nsh, nunits, E, item_i, u);
+  // item and live count read together (gemv_unit); the empty statement takes
+  // both, so the compiler cannot wait for the count before issuing the item
   const cu32p itp = as_const(reinterpret_cast<const uint32_t*>(items + 2 * item_i));
   const int e = (int)itp[0], m = (int)itp[1], loff = (int)itp[2];
+  const int n_items = (int)as_const(reinterpret_cast<const uint32_t*>(misc))[kNGemv];
+  asm volatile("" ::"s"(e), "s"(m), "s"(loff), "s"(n_items));
+  if (b >= nsh && item_i >= n_items) return;
   const bool sh = e == E;
   const int inter = sh ? Is : I;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2494,6 +2499,7 @@ static NarrowGrid narrow_grid(const LayerDev& d, int T, int ncols, int ncols_s, 
   g.cs = nn_c >= d.narrow_cs_min_wgs ? 1 : 0;
   g.ncbs = g.cs ? ncs_c : ncols_s / cw;
   g.ncbr = g.cs ? ncr_c : ncols / cw;
+  if (ntm == 0) g.ncbs = g.ncbr = 0;   // the batch cannot have any
   *nn = g.nsht * g.ncbs + (ntm - g.nsht) * g.ncbr;
   return g;
 }
