@@ -628,7 +628,7 @@ __device__ void bucket_wave(const RouterArgs& a, const int* ids, uint8_t* smem) 
   }
   int n_gemv = (tg & 0xffff) + (tg >> 16), n_mfma = (tm & 0xffff) + (tm >> 16);
   int n_tiles = tt & 0xffff, n_narrow = tt >> 16;
-  if (a.has_shared) {   // the shared expert: last item of its path, its tiles last
+  if (a.has_shared) {   // the shared expert: the last matrix-core item (its tiles last) or streaming item E
     const int T = a.T;
     if (T >= R) {
       const bool wide = T >= W;
@@ -2464,7 +2464,7 @@ static ExpertPtrs expert_ptrs(const LayerDev& d, int T) {
 }
 
 // The shared expert streams when the batch is below the matrix-core threshold
-// (the bucketing pass then appends it as the last streaming item).
+// (the bucketing pass then lists it at the fixed index E of the streaming items).
 static bool shared_streams(const LayerDev& d, int T) { return d.has_shared && T < d.mfma_min_rows; }
 static int routed_stream_items(const LayerDev& d, int T) {
   const int Tk = T * d.k;
